@@ -1,0 +1,170 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) recurrent KDA decode library (libkda.so).
+ *
+ * Recurrent KDA (Kimi Delta Attention) decode advances, for every live request
+ * and value head, a K x V fp32 state S by one token at a time:
+ *
+ *   S <- diag(exp g_t) S                 per-key-channel decay
+ *   v' = beta_t (v_t - S^T k_t)          delta-rule correction (decayed S)
+ *   S <- S + k_t v'^T                    rank-1 update
+ *   o_t = scale S^T q_t                  readout (updated S)
+ *   y_t = gated_rmsnorm(o_t, z_t, w)     optional epilogue, else y_t = o_t
+ *
+ * Sources.  vLLM PR 57585 (recurrent KDA launch tuning on SM90), "Purpose and
+ * source" and "Retained baseline trace attribution": the operation is a fused
+ * recurrent KDA forward over N requests x HV value heads, launched 34 times
+ * per decode graph, with bf16 inputs and fp32 state at K = V = 128
+ * ("Microbenchmark and earlier serving limits").  FlashInfer PR 4562 (H12
+ * packed decode across the SM100 family), inline review of the binding: q, k
+ * and v arrive as row-strided views of one fused projection, gate and beta
+ * per token, an indexed state pool with per-request slot indices, a
+ * caller-owned output, the readout scale 1/sqrt(128) and per-token row
+ * strides; its description adds caller-stream execution, row-strided beta,
+ * padding rows that are skipped and graph replay.  b12x PR 249 (direct
+ * single-token KDA decode), walkthrough: the decode kernel is followed by a
+ * normalisation kernel that gates the decoded output; its review asks that
+ * the written buffers (output, state) be checked against every input for
+ * overlap before launch; its purpose section keeps the one-token case an
+ * internal route of the general call.  The pages never print the recurrence
+ * itself; the one above is the gated delta rule of Kimi Delta Attention.
+ *
+ * Conventions for every entry point.
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library allocates nothing, never synchronises and never copies to or
+ *     from the host.  Each call enqueues one kernel on `stream` (a
+ *     hipStream_t; NULL = the default stream) and returns; it can be
+ *     captured into a HIP graph.
+ *   - Arguments are validated on the host in O(1) before anything is
+ *     launched.  On any error status nothing was launched and no buffer was
+ *     touched.  KDA_ERR_LAUNCH reports a failed launch.
+ *   - Strides are counted in elements of the tensor's own type.
+ *   - bf16 tensors hold raw bf16 bit patterns (uint16_t storage).
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,         /* a required pointer is NULL                          */
+    KDA_ERR_SHAPE = 2,        /* a size is out of range, or K, V are not 128         */
+    KDA_ERR_ALIGN = 3,        /* a pointer or stride breaks the alignment rules      */
+    KDA_ERR_ALIAS = 4,        /* out or state overlaps another buffer of the call    */
+    KDA_ERR_UNSUPPORTED = 5,  /* unknown flag bits                                   */
+    KDA_ERR_DEVICE = 6,       /* the current device is not gfx950, or a HIP query failed */
+    KDA_ERR_LAUNCH = 7        /* the kernel launch failed                            */
+} kda_status;
+
+/* flags: bits 8..9 force the value-tile width of one workgroup
+ * (1 = 32 columns, 2 = 64, 3 = 128; 0 = the library's choice).  Results are
+ * bit-identical for every width; the knob exists for tests and tuning. */
+#define KDA_FLAG_VTILE_SHIFT 8u
+#define KDA_FLAG_VTILE_MASK (3u << KDA_FLAG_VTILE_SHIFT)
+#define KDA_FLAG_VTILE(code) (((uint32_t)(code) & 3u) << KDA_FLAG_VTILE_SHIFT)
+
+/*
+ * One decode call.  Token t of the call is row t of every per-token tensor.
+ *
+ *   N          requests in the call (N = 0: nothing to do, returns KDA_OK)
+ *   H          q/k heads;  HV value heads, a multiple of H; value head hv
+ *              reads q/k head hv / (HV / H)
+ *   K, V       key and value head size; the GPU kernels take K = V = 128
+ *   scale      readout scale (1/sqrt(K) in the serving models)
+ *   q, k       bf16, element (t, h, i) at t*q_stride + h*K + i.
+ *              16-byte aligned; q_stride, k_stride multiples of 8, >= H*K
+ *   v          bf16, element (t, hv, j) at t*v_stride + hv*V + j.
+ *              8-byte aligned; v_stride a multiple of 4, >= HV*V
+ *   g          fp32 log-decay (already activated, <= 0 in practice, -inf
+ *              allowed: it clears that key row), (t, hv, i) at
+ *              t*g_stride + hv*K + i.  16-byte aligned; g_stride a multiple
+ *              of 4, >= HV*K
+ *   beta       fp32, (t, hv) at t*beta_stride + hv; beta_stride >= HV
+ *   state      fp32 pool, (slot, hv, i, j) at slot*slot_stride + (hv*K + i)*V + j
+ *              (V contiguous), num_slots slots.  Read and written IN PLACE.
+ *              16-byte aligned; slot_stride a multiple of 4, >= HV*K*V
+ *   slot_idx   int32 [N]: the pool slot of each request.  A value outside
+ *              [0, num_slots) (-1 marks a padding row) skips the request:
+ *              no state is read or written and its output rows are left
+ *              untouched.  Two live requests must not share a slot in one
+ *              call (their updates would race).
+ *   out        bf16 result, (t, hv, j) at t*out_stride + hv*V + j, written
+ *              for live requests only.  8-byte aligned; out_stride a
+ *              multiple of 4, >= HV*V
+ *   gate       NULL: out = o (no epilogue).  Otherwise bf16 z, (t, hv, j) at
+ *              t*gate_stride + hv*V + j (8-byte aligned, gate_stride a
+ *              multiple of 4, >= HV*V), and
+ *   norm_weight bf16 [V] (8-byte aligned), norm_eps > 0 or 0:
+ *              out = o / sqrt(mean_j o^2 + eps) * w * silu(z).
+ *
+ * Aliasing: out and state may not overlap each other, or any input
+ * (q, k, v, g, beta, slot_idx, cu_seqlens, gate, norm_weight); inputs may
+ * overlap each other (q, k, v are often views of one projection).  Ranges are
+ * the bounding byte ranges of each strided tensor.
+ */
+typedef struct kda_decode_args {
+    int32_t N, H, HV, K, V;
+    float scale;
+    const void *q;      int64_t q_stride;
+    const void *k;      int64_t k_stride;
+    const void *v;      int64_t v_stride;
+    const float *g;     int64_t g_stride;
+    const float *beta;  int64_t beta_stride;
+    float *state;       int64_t num_slots;   int64_t slot_stride;
+    const int32_t *slot_idx;
+    void *out;          int64_t out_stride;
+    const void *gate;   int64_t gate_stride;
+    const void *norm_weight;
+    float norm_eps;
+} kda_decode_args;
+
+/*
+ * Every request decodes exactly T >= 1 tokens, request-major: request n owns
+ * token rows n*T .. n*T+T-1.  The tokens of one request are recurred in
+ * order within the call with the state held on chip; the state is written
+ * back once, after the last token.  One-token decode (T = 1) is the common
+ * serving case and takes the same kernel.  Equivalent to kda_decode_packed
+ * with cu_seqlens[n] = n*T.
+ */
+kda_status kda_decode_step(const kda_decode_args *args, int32_t T, uint32_t flags, void *stream);
+
+/*
+ * Packed variable-length decode: request n owns token rows
+ * cu_seqlens[n] .. cu_seqlens[n+1]-1 (cu_seqlens: device int32 [N+1],
+ * non-decreasing, cu_seqlens[N] <= total_tokens; a request with no tokens
+ * leaves its slot untouched).  total_tokens is the number of token rows the
+ * per-token tensors hold; it bounds the overlap checks only.  The device
+ * metadata (slot_idx, cu_seqlens) is trusted as the serving scheduler wrote
+ * it; slots outside the pool are skipped, never dereferenced.
+ */
+kda_status kda_decode_packed(const kda_decode_args *args, const int32_t *cu_seqlens,
+                             int64_t total_tokens, uint32_t flags, void *stream);
+
+/*
+ * Standalone gated RMSNorm over rows of V values (b12x PR 249, walkthrough:
+ * the normalisation kernel that gates the decoded output):
+ *   y[r][j] = x[r][j] / sqrt(mean_j x[r][j]^2 + eps) * w[j] * silu(z[r][j])
+ * x, gate, y: bf16 [rows][V] contiguous; weight bf16 [V]; V even, 2 <= V <= 8192;
+ * all four 4-byte aligned; eps >= 0.  y may equal x exactly (in place); any
+ * other overlap of y with x, gate or weight is KDA_ERR_ALIAS.
+ */
+kda_status kda_gated_rmsnorm(const void *x, const void *gate, const void *weight, void *y,
+                             int64_t rows, int32_t V, float eps, void *stream);
+
+/* The value-tile width (32, 64 or 128 columns per workgroup) the library
+ * picks for `units` = N*HV (request, value head) pairs, T tokens and with or
+ * without the norm epilogue.  Host-only, no device access. */
+int32_t kda_decode_plan(int64_t units, int32_t T, int32_t has_norm);
+
+/* Static description of a status code. */
+const char *kda_status_string(kda_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,217 @@
+"""Recurrent KDA decode on MI355X (gfx950): Python binding of libkda.so.
+
+This module only marshals arguments: it turns torch tensors into the plain
+pointers, sizes and strides of the C ABI in ``include/kda.h`` and raises on
+an error status.  Every step of the decode runs in the HIP kernels of
+``csrc/kda_decode.hip``.  There is no fallback: without the built library
+every call raises.
+
+torch supplies device memory and the current stream.  It is imported before
+the library is loaded so that libkda.so binds to the HIP runtime torch
+already loaded.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "KdaError", "KdaDecodeArgs", "library", "library_path",
+    "kda_decode_step", "kda_decode_packed", "kda_gated_rmsnorm",
+    "kda_decode_plan", "kda_status_string", "decode_args",
+    "KDA_FLAG_VTILE",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libkda.so")
+
+KDA_STATUS = {
+    0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_ALIGN",
+    4: "KDA_ERR_ALIAS", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_DEVICE", 7: "KDA_ERR_LAUNCH",
+}
+KDA_FLAG_VTILE_SHIFT = 8
+
+
+def KDA_FLAG_VTILE(width: int) -> int:
+    """Flag bits forcing a value-tile width of 32, 64 or 128 columns."""
+    code = {32: 1, 64: 2, 128: 3}[width]
+    return code << KDA_FLAG_VTILE_SHIFT
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        self.name = KDA_STATUS.get(status, str(status))
+        super().__init__(f"{what}: {self.name} ({kda_status_string(status)})")
+
+
+class KdaDecodeArgs(ctypes.Structure):
+    """Mirror of ``kda_decode_args`` in include/kda.h."""
+    _fields_ = [
+        ("N", ctypes.c_int32), ("H", ctypes.c_int32), ("HV", ctypes.c_int32),
+        ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("q_stride", ctypes.c_int64),
+        ("k", ctypes.c_void_p), ("k_stride", ctypes.c_int64),
+        ("v", ctypes.c_void_p), ("v_stride", ctypes.c_int64),
+        ("g", ctypes.c_void_p), ("g_stride", ctypes.c_int64),
+        ("beta", ctypes.c_void_p), ("beta_stride", ctypes.c_int64),
+        ("state", ctypes.c_void_p), ("num_slots", ctypes.c_int64), ("slot_stride", ctypes.c_int64),
+        ("slot_idx", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("out_stride", ctypes.c_int64),
+        ("gate", ctypes.c_void_p), ("gate_stride", ctypes.c_int64),
+        ("norm_weight", ctypes.c_void_p),
+        ("norm_eps", ctypes.c_float),
+    ]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libkda.so (built in place by ``build.py``); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise RuntimeError(f"{library_path} is not built: run linear_attention_recurrent_decode_amd.build.build()")
+    lib = ctypes.CDLL(library_path)
+    P = ctypes.POINTER(KdaDecodeArgs)
+    lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_decode_step.argtypes = [P, ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p]
+    lib.kda_decode_packed.restype = ctypes.c_int
+    lib.kda_decode_packed.argtypes = [P, ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p]
+    lib.kda_gated_rmsnorm.restype = ctypes.c_int
+    lib.kda_gated_rmsnorm.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p]
+    lib.kda_decode_plan.restype = ctypes.c_int32
+    lib.kda_decode_plan.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def kda_status_string(status: int) -> str:
+    return library().kda_status_string(int(status)).decode()
+
+
+def kda_decode_plan(units: int, T: int = 1, has_norm: bool = False) -> int:
+    return int(library().kda_decode_plan(int(units), int(T), int(bool(has_norm))))
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    # inner dimensions dense; the leading (token / slot) dimension may be strided
+    expect = 1
+    for d in range(ndim - 1, 0, -1):
+        if t.shape[d] > 1 and t.stride(d) != expect:
+            raise ValueError(f"{name}: inner dimensions must be contiguous")
+        expect *= t.shape[d]
+
+
+def _lead_stride(t: torch.Tensor) -> int:
+    inner = 1
+    for d in t.shape[1:]:
+        inner *= d
+    return t.stride(0) if t.shape[0] > 1 else inner
+
+
+def decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate=None, norm_weight=None,
+                eps: float = 1e-6) -> KdaDecodeArgs:
+    """Marshal tensors into a ``kda_decode_args`` struct (no validation of
+    values; the library validates sizes, alignment and overlap)."""
+    _check(q, "q", torch.bfloat16, 3)
+    _check(k, "k", torch.bfloat16, 3)
+    _check(v, "v", torch.bfloat16, 3)
+    _check(g, "g", torch.float32, 3)
+    _check(beta, "beta", torch.float32, 2)
+    _check(state, "state", torch.float32, 4)
+    _check(slot_idx, "slot_idx", torch.int32, 1)
+    _check(out, "out", torch.bfloat16, 3)
+    tokens, H, K = q.shape
+    HV, V = v.shape[1], v.shape[2]
+    if k.shape != q.shape or v.shape[0] != tokens or g.shape != (tokens, HV, K) or \
+            beta.shape != (tokens, HV) or out.shape != (tokens, HV, V) or state.shape[1:] != (HV, K, V):
+        raise ValueError("inconsistent shapes")
+    a = KdaDecodeArgs()
+    a.N, a.H, a.HV, a.K, a.V = slot_idx.shape[0], H, HV, K, V
+    a.scale = float(scale)
+    a.q, a.q_stride = q.data_ptr(), _lead_stride(q)
+    a.k, a.k_stride = k.data_ptr(), _lead_stride(k)
+    a.v, a.v_stride = v.data_ptr(), _lead_stride(v)
+    a.g, a.g_stride = g.data_ptr(), _lead_stride(g)
+    a.beta, a.beta_stride = beta.data_ptr(), _lead_stride(beta)
+    a.state, a.num_slots, a.slot_stride = state.data_ptr(), state.shape[0], _lead_stride(state)
+    a.slot_idx = slot_idx.data_ptr()
+    a.out, a.out_stride = out.data_ptr(), _lead_stride(out)
+    if (gate is None) != (norm_weight is None):
+        raise ValueError("gate and norm_weight go together")
+    if gate is not None:
+        _check(gate, "gate", torch.bfloat16, 3)
+        _check(norm_weight, "norm_weight", torch.bfloat16, 1)
+        if gate.shape != out.shape or norm_weight.shape != (V,):
+            raise ValueError("inconsistent gate / norm_weight shapes")
+        a.gate, a.gate_stride = gate.data_ptr(), _lead_stride(gate)
+        a.norm_weight = norm_weight.data_ptr()
+    a.norm_eps = float(eps)
+    return a
+
+
+def kda_decode_step(q, k, v, g, beta, state, slot_idx, out, *, T: int, scale: float,
+                    gate=None, norm_weight=None, eps: float = 1e-6, flags: int = 0, stream=None):
+    """Decode T tokens for each of N requests (tokens request-major, N*T rows);
+    updates ``state`` in place and writes ``out`` for live requests."""
+    a = decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate, norm_weight, eps)
+    if q.shape[0] != a.N * int(T):
+        raise ValueError("step call needs N*T token rows")
+    st = library().kda_decode_step(ctypes.byref(a), int(T), int(flags), _stream(stream))
+    if st != 0:
+        raise KdaError(st, "kda_decode_step")
+    return out
+
+
+def kda_decode_packed(q, k, v, g, beta, state, slot_idx, cu_seqlens, out, *, scale: float,
+                      gate=None, norm_weight=None, eps: float = 1e-6, flags: int = 0, stream=None):
+    """Packed variable-length decode: request n owns token rows
+    cu_seqlens[n] .. cu_seqlens[n+1]-1."""
+    a = decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate, norm_weight, eps)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    if cu_seqlens.shape[0] != a.N + 1:
+        raise ValueError("cu_seqlens must hold N+1 entries")
+    st = library().kda_decode_packed(ctypes.byref(a), cu_seqlens.data_ptr(), q.shape[0], int(flags), _stream(stream))
+    if st != 0:
+        raise KdaError(st, "kda_decode_packed")
+    return out
+
+
+def kda_gated_rmsnorm(x, gate, weight, y, eps: float = 1e-6, stream=None):
+    """y = x / sqrt(mean(x^2) + eps) * weight * silu(gate) over the last dim."""
+    for t, n in ((x, "x"), (gate, "gate"), (y, "y")):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous bf16 tensor")
+    if weight.dtype != torch.bfloat16 or weight.dim() != 1 or not weight.is_contiguous():
+        raise ValueError("weight must be a contiguous bf16 vector")
+    V = x.shape[-1]
+    if gate.shape != x.shape or y.shape != x.shape or weight.shape[0] != V:
+        raise ValueError("shape mismatch")
+    rows = x.numel() // V if V else 0
+    st = library().kda_gated_rmsnorm(x.data_ptr(), gate.data_ptr(), weight.data_ptr(), y.data_ptr(),
+                                     rows, V, float(eps), _stream(stream))
+    if st != 0:
+        raise KdaError(st, "kda_gated_rmsnorm")
+    return y

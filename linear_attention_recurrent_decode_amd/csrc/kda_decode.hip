@@ -1,0 +1,561 @@
+// kda_decode.hip -- gfx950 kernels and the C ABI of libkda.so (declared in kda.h).
+//
+// Recurrent KDA decode is a bandwidth-bound stream over the state pool: per
+// (request, value head) and call, a 64 KiB fp32 state tile is read once and
+// written once, while the arithmetic per token is a few fused multiply-adds
+// per state element.  Nothing here is a dense contraction, so nothing runs on
+// the matrix cores; the design goals are every byte of the tile in flight at
+// once, 16-byte coalesced accesses, and a short dependency chain per token.
+//
+// Work decomposition.  One wave64 owns 32 value columns x all 128 key rows of
+// one (request, value head) tile: 4096 floats, 64 per lane, held in VGPRs for
+// every token of the call.  Lane l holds columns 4*(l%8) .. +3 (one 16-byte
+// vector per row) of the 16 key rows 16*(l/8) .. +15.  Each of the 16 loads of
+// a wave covers 8 rows x 128 contiguous bytes.  A workgroup is 1, 2 or 4 waves
+// (a value tile of 32, 64 or 128 columns); the grid is one workgroup per
+// (request, value head, value tile).  Columns never interact in the
+// recurrence, so the tiling cannot change a single result bit: every wave runs
+// the same per-column arithmetic in the same order whatever the tile width.
+//
+// Per token (vLLM PR 57585 names the op; the gated delta rule of Kimi Delta
+// Attention is the recurrence):
+//   a_i = exp(g_i)
+//   u_j = sum_i S_ij (a_i k_i)      -- the correction against the decayed state
+//   w_j = sum_i S_ij (a_i q_i)
+//   kq  = sum_i k_i q_i
+//   v'_j = beta (v_j - u_j)
+//   o_j = scale (w_j + v'_j kq)     -- equals scale * sum_i S'_ij q_i
+//   S'_ij = a_i S_ij + k_i v'_j
+// so both key-axis reductions come from one pass over the old state, and the
+// only cross-lane step per token is one 3-level butterfly over the 8 lanes
+// that share a column group.  The gated RMSNorm epilogue (b12x PR 249,
+// walkthrough: normalise and gate the decoded output) needs the sum of o^2
+// over all 128 columns, which forces the 4-wave tile and adds one LDS
+// exchange per token.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <stdint.h>
+#include <string.h>
+
+#include "kda.h"
+
+namespace {
+
+constexpr int KD = 128;           // key head size handled by the kernels
+constexpr int VD = 128;           // value head size handled by the kernels
+constexpr int ROWS_PER_LANE = 16;  // 128 key rows over 8 row groups
+constexpr int MAX_DEVICES = 64;
+
+struct DecodeParams {
+    const uint16_t *q;
+    const uint16_t *k;
+    const uint16_t *v;
+    const float *g;
+    const float *beta;
+    float *state;
+    const int32_t *slot_idx;
+    const int32_t *cu_seqlens;   // NULL: fixed T tokens per request
+    uint16_t *out;
+    const uint16_t *gate;
+    const uint16_t *norm_weight;
+    int64_t q_stride, k_stride, v_stride, g_stride, beta_stride, out_stride, gate_stride;
+    int64_t num_slots, slot_stride;
+    int32_t HV, heads_per_qk, T;
+    float scale, eps;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest even; NaN becomes a quiet NaN.
+__device__ __forceinline__ uint32_t to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return 0x7FC0u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return to_bf16(lo) | (to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float silu(float z)
+{
+    return z / (1.0f + __expf(-z));
+}
+
+// Sum over the 8 lanes of a column group (lane bits 3..5).  Every lane ends
+// with the same bits: each level adds the same two operands on both sides.
+__device__ __forceinline__ float sum_row_groups(float x)
+{
+    x += __shfl_xor(x, 8);
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+// Sum over the 8 column groups of a wave (lane bits 0..2).
+__device__ __forceinline__ float sum_col_groups(float x)
+{
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    return x;
+}
+
+template <int NW, bool NORM>
+__global__ __launch_bounds__(64 * NW) void kda_decode_kernel(DecodeParams p)
+{
+    static_assert(NW == 1 || NW == 2 || NW == 4, "a workgroup is 1, 2 or 4 waves");
+    static_assert(!NORM || NW == 4, "the norm epilogue needs all 128 columns in one workgroup");
+    constexpr int NVT = 4 / NW;   // value tiles per head
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t block = blockIdx.x;
+    const int vt = (int)(block % NVT);
+    const int64_t unit = block / NVT;
+    const int64_t req = unit / p.HV;
+    const int hv = (int)(unit - req * p.HV);
+
+    // slot gather: padding rows and slots outside the pool are skipped
+    const int64_t slot = p.slot_idx[req];
+    if (slot < 0 || slot >= p.num_slots)
+        return;
+    int64_t bos, eos;
+    if (p.cu_seqlens) {
+        bos = p.cu_seqlens[req];
+        eos = p.cu_seqlens[req + 1];
+    } else {
+        bos = req * p.T;
+        eos = bos + p.T;
+    }
+    if (eos <= bos)
+        return;
+    const int h = hv / p.heads_per_qk;
+
+    const int cg = lane & 7;              // column group: 4 columns
+    const int rg = lane >> 3;             // row group: 16 key rows
+    const int col = (vt * NW + wave) * 32 + cg * 4;
+    const int row0 = rg * ROWS_PER_LANE;
+
+    float *tile = p.state + slot * p.slot_stride + (int64_t)hv * (KD * VD) + (int64_t)row0 * VD + col;
+    float4 s[ROWS_PER_LANE];
+#pragma unroll
+    for (int i = 0; i < ROWS_PER_LANE; ++i)
+        s[i] = *reinterpret_cast<const float4 *>(tile + i * VD);
+
+    __shared__ float norm_partial[2][4];
+
+    for (int64_t t = bos; t < eos; ++t) {
+        const uint4 *kp = reinterpret_cast<const uint4 *>(p.k + t * p.k_stride + h * KD + row0);
+        const uint4 *qp = reinterpret_cast<const uint4 *>(p.q + t * p.q_stride + h * KD + row0);
+        const float4 *gp = reinterpret_cast<const float4 *>(p.g + t * p.g_stride + (int64_t)hv * KD + row0);
+        const uint4 k0 = kp[0], k1 = kp[1];
+        const uint4 q0 = qp[0], q1 = qp[1];
+        const uint2 vv = *reinterpret_cast<const uint2 *>(p.v + t * p.v_stride + (int64_t)hv * VD + col);
+        const float b = p.beta[t * p.beta_stride + hv];
+
+        float kk[ROWS_PER_LANE], qq[ROWS_PER_LANE], a[ROWS_PER_LANE];
+        const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+        const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            kk[2 * i] = bf16_lo(kw[i]);
+            kk[2 * i + 1] = bf16_hi(kw[i]);
+            qq[2 * i] = bf16_lo(qw[i]);
+            qq[2 * i + 1] = bf16_hi(qw[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 gg = gp[i];
+            a[4 * i + 0] = __expf(gg.x);
+            a[4 * i + 1] = __expf(gg.y);
+            a[4 * i + 2] = __expf(gg.z);
+            a[4 * i + 3] = __expf(gg.w);
+        }
+
+        // one pass over the old state: both key-axis partial sums
+        float u0 = 0.f, u1 = 0.f, u2 = 0.f, u3 = 0.f;
+        float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f;
+        float kq = 0.f;
+#pragma unroll
+        for (int i = 0; i < ROWS_PER_LANE; ++i) {
+            const float ak = a[i] * kk[i];
+            const float aq = a[i] * qq[i];
+            u0 = fmaf(s[i].x, ak, u0);
+            u1 = fmaf(s[i].y, ak, u1);
+            u2 = fmaf(s[i].z, ak, u2);
+            u3 = fmaf(s[i].w, ak, u3);
+            w0 = fmaf(s[i].x, aq, w0);
+            w1 = fmaf(s[i].y, aq, w1);
+            w2 = fmaf(s[i].z, aq, w2);
+            w3 = fmaf(s[i].w, aq, w3);
+            kq = fmaf(kk[i], qq[i], kq);
+        }
+        u0 = sum_row_groups(u0);
+        u1 = sum_row_groups(u1);
+        u2 = sum_row_groups(u2);
+        u3 = sum_row_groups(u3);
+        w0 = sum_row_groups(w0);
+        w1 = sum_row_groups(w1);
+        w2 = sum_row_groups(w2);
+        w3 = sum_row_groups(w3);
+        kq = sum_row_groups(kq);
+
+        // delta correction, readout, rank-1 update
+        const float vp0 = b * (bf16_lo(vv.x) - u0);
+        const float vp1 = b * (bf16_hi(vv.x) - u1);
+        const float vp2 = b * (bf16_lo(vv.y) - u2);
+        const float vp3 = b * (bf16_hi(vv.y) - u3);
+        float o0 = p.scale * fmaf(vp0, kq, w0);
+        float o1 = p.scale * fmaf(vp1, kq, w1);
+        float o2 = p.scale * fmaf(vp2, kq, w2);
+        float o3 = p.scale * fmaf(vp3, kq, w3);
+#pragma unroll
+        for (int i = 0; i < ROWS_PER_LANE; ++i) {
+            s[i].x = fmaf(kk[i], vp0, a[i] * s[i].x);
+            s[i].y = fmaf(kk[i], vp1, a[i] * s[i].y);
+            s[i].z = fmaf(kk[i], vp2, a[i] * s[i].z);
+            s[i].w = fmaf(kk[i], vp3, a[i] * s[i].w);
+        }
+
+        if constexpr (NORM) {
+            float ss = o0 * o0 + o1 * o1 + o2 * o2 + o3 * o3;
+            ss = sum_col_groups(ss);
+            float *slot_sum = norm_partial[t & 1];
+            if (lane == 0)
+                slot_sum[wave] = ss;
+            __syncthreads();
+            const float total = (slot_sum[0] + slot_sum[1]) + (slot_sum[2] + slot_sum[3]);
+            const float r = rsqrtf(total * (1.0f / VD) + p.eps);
+            const uint2 zz = *reinterpret_cast<const uint2 *>(p.gate + t * p.gate_stride + (int64_t)hv * VD + col);
+            const uint2 ww = *reinterpret_cast<const uint2 *>(p.norm_weight + col);
+            o0 = o0 * r * bf16_lo(ww.x) * silu(bf16_lo(zz.x));
+            o1 = o1 * r * bf16_hi(ww.x) * silu(bf16_hi(zz.x));
+            o2 = o2 * r * bf16_lo(ww.y) * silu(bf16_lo(zz.y));
+            o3 = o3 * r * bf16_hi(ww.y) * silu(bf16_hi(zz.y));
+        }
+        if (rg == 0) {
+            uint2 packed;
+            packed.x = pack_bf16x2(o0, o1);
+            packed.y = pack_bf16x2(o2, o3);
+            *reinterpret_cast<uint2 *>(p.out + t * p.out_stride + (int64_t)hv * VD + col) = packed;
+        }
+    }
+
+    // slot scatter: the tile goes back where it came from
+#pragma unroll
+    for (int i = 0; i < ROWS_PER_LANE; ++i)
+        *reinterpret_cast<float4 *>(tile + i * VD) = s[i];
+}
+
+// Standalone gated RMSNorm: one wave per row, 4 rows per workgroup.
+__global__ __launch_bounds__(256) void kda_gated_rmsnorm_kernel(const uint16_t *x, const uint16_t *z,
+                                                                const uint16_t *w, uint16_t *y,
+                                                                int64_t rows, int V, float eps)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows)
+        return;
+    const int pairs = V / 2;
+    const uint32_t *xr = reinterpret_cast<const uint32_t *>(x + row * V);
+    const uint32_t *zr = reinterpret_cast<const uint32_t *>(z + row * V);
+    const uint32_t *wr = reinterpret_cast<const uint32_t *>(w);
+    uint32_t *yr = reinterpret_cast<uint32_t *>(y + row * V);
+
+    float ss = 0.f;
+    for (int j = lane; j < pairs; j += 64) {
+        const uint32_t xw = xr[j];
+        const float x0 = bf16_lo(xw), x1 = bf16_hi(xw);
+        ss = fmaf(x0, x0, ss);
+        ss = fmaf(x1, x1, ss);
+    }
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    ss += __shfl_xor(ss, 4);
+    ss += __shfl_xor(ss, 8);
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const float r = rsqrtf(ss / (float)V + eps);
+    for (int j = lane; j < pairs; j += 64) {
+        const uint32_t xw = xr[j], zw = zr[j], ww = wr[j];
+        const float y0 = bf16_lo(xw) * r * bf16_lo(ww) * silu(bf16_lo(zw));
+        const float y1 = bf16_hi(xw) * r * bf16_hi(ww) * silu(bf16_hi(zw));
+        yr[j] = pack_bf16x2(y0, y1);
+    }
+}
+
+// ------------------------------------------------------------------ host
+
+std::atomic<int> g_device_kind[MAX_DEVICES];   // 0 unknown, 1 gfx950, 2 other
+
+kda_status check_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES)
+        return KDA_ERR_DEVICE;
+    int kind = g_device_kind[dev].load(std::memory_order_relaxed);
+    if (kind == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return KDA_ERR_DEVICE;
+        kind = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_device_kind[dev].store(kind, std::memory_order_relaxed);
+    }
+    return kind == 1 ? KDA_OK : KDA_ERR_DEVICE;
+}
+
+struct ByteRange {
+    uintptr_t lo = 0, hi = 0;   // [lo, hi), empty when lo == hi
+};
+
+// Bounding byte range of a strided [rows][inner] tensor.
+ByteRange span(const void *ptr, int64_t rows, int64_t stride, int64_t inner, int64_t elem)
+{
+    ByteRange r;
+    if (!ptr || rows <= 0 || inner <= 0)
+        return r;
+    r.lo = reinterpret_cast<uintptr_t>(ptr);
+    r.hi = r.lo + (uintptr_t)(((rows - 1) * stride + inner) * elem);
+    return r;
+}
+
+bool overlaps(ByteRange a, ByteRange b)
+{
+    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void *p, uintptr_t bytes)
+{
+    return (reinterpret_cast<uintptr_t>(p) & (bytes - 1)) == 0;
+}
+
+int vtile_from_flags(uint32_t flags)
+{
+    switch ((flags & KDA_FLAG_VTILE_MASK) >> KDA_FLAG_VTILE_SHIFT) {
+    case 1: return 32;
+    case 2: return 64;
+    case 3: return 128;
+    default: return 0;
+    }
+}
+
+kda_status validate(const kda_decode_args *a, int64_t tokens, const int32_t *cu_seqlens, uint32_t flags)
+{
+    if (flags & ~KDA_FLAG_VTILE_MASK)
+        return KDA_ERR_UNSUPPORTED;
+    if (a->N < 0 || a->H < 1 || a->HV < 1 || a->HV % a->H != 0 || tokens < 0)
+        return KDA_ERR_SHAPE;
+    if (a->K != KD || a->V != VD)
+        return KDA_ERR_SHAPE;
+    if (a->N == 0)
+        return KDA_OK;
+    // per-token tensors may be NULL only when the call holds no token rows
+    if (tokens > 0 && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->out))
+        return KDA_ERR_NULL;
+    if (!a->state || !a->slot_idx)
+        return KDA_ERR_NULL;
+    if (!a->norm_weight && a->gate)
+        return KDA_ERR_NULL;
+    const int64_t hk = (int64_t)a->H * a->K, hvk = (int64_t)a->HV * a->K, hvv = (int64_t)a->HV * a->V;
+    if (a->num_slots < 0 || a->slot_stride < hvk * a->V)
+        return KDA_ERR_SHAPE;
+    if (a->q_stride < hk || a->k_stride < hk || a->v_stride < hvv || a->g_stride < hvk ||
+        a->beta_stride < a->HV || a->out_stride < hvv || (a->gate && a->gate_stride < hvv))
+        return KDA_ERR_SHAPE;
+    if (!(a->norm_eps >= 0.0f))
+        return KDA_ERR_SHAPE;
+    if (!aligned(a->q, 16) || !aligned(a->k, 16) || a->q_stride % 8 || a->k_stride % 8 ||
+        !aligned(a->v, 8) || a->v_stride % 4 || !aligned(a->g, 16) || a->g_stride % 4 ||
+        !aligned(a->beta, 4) || !aligned(a->state, 16) || a->slot_stride % 4 ||
+        !aligned(a->out, 8) || a->out_stride % 4 || !aligned(a->slot_idx, 4) ||
+        (cu_seqlens && !aligned(cu_seqlens, 4)) ||
+        (a->gate && (!aligned(a->gate, 8) || a->gate_stride % 4 || !aligned(a->norm_weight, 8))))
+        return KDA_ERR_ALIGN;
+
+    const ByteRange out = span(a->out, tokens, a->out_stride, hvv, 2);
+    const ByteRange state = span(a->state, a->num_slots, a->slot_stride, hvk * a->V, 4);
+    const ByteRange inputs[] = {
+        span(a->q, tokens, a->q_stride, hk, 2),
+        span(a->k, tokens, a->k_stride, hk, 2),
+        span(a->v, tokens, a->v_stride, hvv, 2),
+        span(a->g, tokens, a->g_stride, hvk, 4),
+        span(a->beta, tokens, a->beta_stride, a->HV, 4),
+        span(a->slot_idx, 1, 0, a->N, 4),
+        span(cu_seqlens, 1, 0, (int64_t)a->N + 1, 4),
+        span(a->gate, tokens, a->gate_stride, hvv, 2),
+        span(a->norm_weight, 1, 0, a->V, 2),
+    };
+    if (overlaps(out, state))
+        return KDA_ERR_ALIAS;
+    for (const ByteRange &in : inputs)
+        if (overlaps(out, in) || overlaps(state, in))
+            return KDA_ERR_ALIAS;
+    return KDA_OK;
+}
+
+int32_t plan_vtile(int64_t units, int32_t T, bool norm)
+{
+    (void)T;
+    if (norm)
+        return 128;
+    if (units >= 256)
+        return 128;
+    if (units >= 128)
+        return 64;
+    return 32;
+}
+
+template <int NW, bool NORM>
+kda_status launch_decode(const DecodeParams &p, int64_t units, hipStream_t stream)
+{
+    const int64_t blocks = units * (4 / NW);
+    if (blocks > 0x7FFFFFFF)
+        return KDA_ERR_SHAPE;
+    void *args[] = {const_cast<DecodeParams *>(&p)};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM>),
+                                         dim3((uint32_t)blocks), dim3(64 * NW), args, 0, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status run_decode(const kda_decode_args *a, int32_t T, const int32_t *cu_seqlens, int64_t tokens,
+                      uint32_t flags, void *stream)
+{
+    if (!a)
+        return KDA_ERR_NULL;
+    kda_status st = validate(a, tokens, cu_seqlens, flags);
+    if (st != KDA_OK)
+        return st;
+    if (a->N == 0)
+        return KDA_OK;
+    const bool norm = a->gate != nullptr;
+    const int64_t units = (int64_t)a->N * a->HV;
+    int vtile = vtile_from_flags(flags);
+    if (vtile == 0)
+        vtile = plan_vtile(units, T, norm);
+    if (norm && vtile != 128)
+        return KDA_ERR_UNSUPPORTED;
+    st = check_device();
+    if (st != KDA_OK)
+        return st;
+
+    DecodeParams p;
+    p.q = static_cast<const uint16_t *>(a->q);
+    p.k = static_cast<const uint16_t *>(a->k);
+    p.v = static_cast<const uint16_t *>(a->v);
+    p.g = a->g;
+    p.beta = a->beta;
+    p.state = a->state;
+    p.slot_idx = a->slot_idx;
+    p.cu_seqlens = cu_seqlens;
+    p.out = static_cast<uint16_t *>(a->out);
+    p.gate = static_cast<const uint16_t *>(a->gate);
+    p.norm_weight = static_cast<const uint16_t *>(a->norm_weight);
+    p.q_stride = a->q_stride;
+    p.k_stride = a->k_stride;
+    p.v_stride = a->v_stride;
+    p.g_stride = a->g_stride;
+    p.beta_stride = a->beta_stride;
+    p.out_stride = a->out_stride;
+    p.gate_stride = a->gate_stride;
+    p.num_slots = a->num_slots;
+    p.slot_stride = a->slot_stride;
+    p.HV = a->HV;
+    p.heads_per_qk = a->HV / a->H;
+    p.T = T;
+    p.scale = a->scale;
+    p.eps = a->norm_eps;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (norm)
+        return launch_decode<4, true>(p, units, s);
+    switch (vtile) {
+    case 32: return launch_decode<1, false>(p, units, s);
+    case 64: return launch_decode<2, false>(p, units, s);
+    default: return launch_decode<4, false>(p, units, s);
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_decode_step(const kda_decode_args *args, int32_t T, uint32_t flags, void *stream)
+{
+    if (!args)
+        return KDA_ERR_NULL;
+    if (T < 1)
+        return KDA_ERR_SHAPE;
+    return run_decode(args, T, nullptr, (int64_t)args->N * T, flags, stream);
+}
+
+kda_status kda_decode_packed(const kda_decode_args *args, const int32_t *cu_seqlens, int64_t total_tokens,
+                             uint32_t flags, void *stream)
+{
+    if (!args || !cu_seqlens)
+        return KDA_ERR_NULL;
+    return run_decode(args, 0, cu_seqlens, total_tokens, flags, stream);
+}
+
+kda_status kda_gated_rmsnorm(const void *x, const void *gate, const void *weight, void *y, int64_t rows,
+                             int32_t V, float eps, void *stream)
+{
+    if (!x || !gate || !weight || !y)
+        return KDA_ERR_NULL;
+    if (rows < 0 || V < 2 || V > 8192 || V % 2 || !(eps >= 0.0f))
+        return KDA_ERR_SHAPE;
+    if (!aligned(x, 4) || !aligned(gate, 4) || !aligned(weight, 4) || !aligned(y, 4))
+        return KDA_ERR_ALIGN;
+    const ByteRange yr = span(y, rows, V, V, 2);
+    if (y != x && overlaps(yr, span(x, rows, V, V, 2)))
+        return KDA_ERR_ALIAS;
+    if (overlaps(yr, span(gate, rows, V, V, 2)) || overlaps(yr, span(weight, 1, 0, V, 2)))
+        return KDA_ERR_ALIAS;
+    if (rows == 0)
+        return KDA_OK;
+    kda_status st = check_device();
+    if (st != KDA_OK)
+        return st;
+    const int64_t blocks = (rows + 3) / 4;
+    if (blocks > 0x7FFFFFFF)
+        return KDA_ERR_SHAPE;
+    const uint16_t *xp = static_cast<const uint16_t *>(x);
+    const uint16_t *zp = static_cast<const uint16_t *>(gate);
+    const uint16_t *wp = static_cast<const uint16_t *>(weight);
+    uint16_t *yp = static_cast<uint16_t *>(y);
+    int Vi = V;
+    void *args[] = {&xp, &zp, &wp, &yp, &rows, &Vi, &eps};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&kda_gated_rmsnorm_kernel),
+                                         dim3((uint32_t)blocks), dim3(256), args, 0,
+                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+int32_t kda_decode_plan(int64_t units, int32_t T, int32_t has_norm)
+{
+    return plan_vtile(units, T, has_norm != 0);
+}
+
+const char *kda_status_string(kda_status status)
+{
+    switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "a size is out of range or unsupported";
+    case KDA_ERR_ALIGN: return "a pointer or stride breaks the alignment rules";
+    case KDA_ERR_ALIAS: return "a written buffer overlaps another buffer of the call";
+    case KDA_ERR_UNSUPPORTED: return "unsupported flag or mode";
+    case KDA_ERR_DEVICE: return "the current device is not gfx950, or a HIP query failed";
+    case KDA_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

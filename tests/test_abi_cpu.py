@@ -1,0 +1,193 @@
+"""Host-side checks of the C ABI: the library loads, exports what kda.h
+declares, the ctypes struct matches the C layout, and every validation path
+returns its status before any device work.  The pointers used here are fake
+addresses: each call below is rejected by host validation, so nothing is
+dereferenced and no kernel is launched.  On a machine with a GPU the whole
+module is skipped, so that a call that wrongly passed validation could never
+reach a kernel with fake pointers."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import torch
+
+import linear_attention_recurrent_decode_amd as kda
+
+pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                reason="fake device pointers are only used where no GPU exists")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)) - {"kda_decode_args"})
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert names == ["kda_decode_packed", "kda_decode_plan", "kda_decode_step",
+                     "kda_gated_rmsnorm", "kda_status_string"]
+    lib = kda.library()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", kda.library_path], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (kda_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_struct_layout_matches_c(tmp_path):
+    fields = [f[0] for f in kda.KdaDecodeArgs._fields_]
+    src = tmp_path / "layout.c"
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "kda.h"', 'int main(void) {',
+             '  printf("size %zu\\n", sizeof(kda_decode_args));']
+    for f in fields:
+        lines.append(f'  printf("{f} %zu\\n", offsetof(kda_decode_args, {f}));')
+    lines.append("  return 0; }")
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.dirname(HEADER), "-o", str(exe), str(src)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True).stdout.splitlines())
+    assert int(got["size"]) == ctypes.sizeof(kda.KdaDecodeArgs)
+    for f in fields:
+        assert int(got[f]) == getattr(kda.KdaDecodeArgs, f).offset, f
+
+
+def test_status_strings_and_plan():
+    for code in range(8):
+        assert kda.kda_status_string(code)
+    assert kda.kda_status_string(99) == "unknown status"
+    for units in (1, 8, 64, 127, 128, 255, 256, 3072, 1 << 20):
+        for T in (1, 2, 4):
+            assert kda.kda_decode_plan(units, T, False) in (32, 64, 128)
+            assert kda.kda_decode_plan(units, T, True) == 128
+
+
+BASE = 0x7F0000000000
+
+
+def _valid_args(N=4, H=2, HV=4, T=1):
+    """Fake, well-formed device addresses: disjoint 64 MiB regions."""
+    a = kda.KdaDecodeArgs()
+    a.N, a.H, a.HV, a.K, a.V, a.scale = N, H, HV, 128, 128, 0.088
+    region = iter(range(BASE, BASE + 64 * (1 << 26), 1 << 26))
+    a.q, a.q_stride = next(region), H * 128
+    a.k, a.k_stride = next(region), H * 128
+    a.v, a.v_stride = next(region), HV * 128
+    a.g, a.g_stride = next(region), HV * 128
+    a.beta, a.beta_stride = next(region), HV
+    a.state, a.num_slots, a.slot_stride = next(region), 8, HV * 128 * 128
+    a.slot_idx = next(region)
+    a.out, a.out_stride = next(region), HV * 128
+    a.gate, a.gate_stride, a.norm_weight, a.norm_eps = 0, 0, 0, 1e-6
+    return a, next(region)
+
+
+def _step(a, T=1, flags=0):
+    return kda.library().kda_decode_step(ctypes.byref(a), T, flags, None)
+
+
+def _packed(a, cu, tokens, flags=0):
+    return kda.library().kda_decode_packed(ctypes.byref(a), cu, tokens, flags, None)
+
+
+NULL, SHAPE, ALIGN, ALIAS, UNSUP, DEVICE = 1, 2, 3, 4, 5, 6
+
+
+def test_null_pointers():
+    assert kda.library().kda_decode_step(None, 1, 0, None) == NULL
+    for f in ("q", "k", "v", "g", "beta", "state", "slot_idx", "out"):
+        a, _ = _valid_args()
+        setattr(a, f, 0)
+        assert _step(a) == NULL, f
+    a, cu = _valid_args()
+    assert _packed(a, None, 4) == NULL
+    a, _ = _valid_args()
+    a.gate, a.gate_stride = BASE + 40 * (1 << 26), 4 * 128
+    assert _step(a) == NULL                      # gate without weight
+
+
+def test_shapes():
+    for field, value in (("K", 64), ("V", 256), ("H", 3), ("HV", 0), ("N", -1), ("num_slots", -1),
+                         ("slot_stride", 4 * 128 * 128 - 4), ("q_stride", 128), ("out_stride", 4),
+                         ("beta_stride", 3), ("norm_eps", -1.0), ("norm_eps", float("nan"))):
+        a, _ = _valid_args()
+        setattr(a, field, value)
+        assert _step(a) == SHAPE, field
+    a, _ = _valid_args()
+    assert _step(a, T=0) == SHAPE
+
+
+def test_alignment():
+    for field, value in (("q", BASE + 8), ("k", BASE + (1 << 26) + 2), ("v", BASE + 2 * (1 << 26) + 4),
+                         ("g", BASE + 3 * (1 << 26) + 8), ("state", BASE + 5 * (1 << 26) + 4),
+                         ("out", BASE + 7 * (1 << 26) + 2)):
+        a, _ = _valid_args()
+        setattr(a, field, value)
+        assert _step(a) == ALIGN, field
+    for field, value in (("q_stride", 2 * 128 + 4), ("v_stride", 4 * 128 + 2), ("g_stride", 4 * 128 + 2),
+                         ("slot_stride", 4 * 128 * 128 + 2), ("out_stride", 4 * 128 + 2)):
+        a, _ = _valid_args()
+        setattr(a, field, value)
+        assert _step(a) == ALIGN, field
+
+
+def test_aliasing():
+    a, _ = _valid_args()
+    a.out = a.q + 256                              # out inside q
+    assert _step(a) == ALIAS
+    a, _ = _valid_args()
+    a.state = a.g                                  # state on g
+    assert _step(a) == ALIAS
+    a, _ = _valid_args()
+    a.out = a.state + 8 * 4 * 128 * 128 * 4 - 64   # out starts in the last pool slot
+    a.out -= a.out % 8
+    assert _step(a) == ALIAS
+    a, _ = _valid_args()
+    a.slot_idx = a.state + 64                      # metadata inside the pool
+    assert _step(a) == ALIAS
+    a, cu = _valid_args()
+    a.out = cu                                     # out over cu_seqlens
+    assert _packed(a, cu, 4) == ALIAS
+    # inputs may overlap each other: q and k as views of one projection
+    a, _ = _valid_args()
+    a.k = a.q + 2 * 128 * 2
+    a.q_stride = a.k_stride = 4 * 128
+    assert _step(a) == DEVICE                      # passes validation, stops at the device check
+
+
+def test_unknown_flags():
+    a, _ = _valid_args()
+    assert _step(a, flags=1) == UNSUP
+    a, _ = _valid_args()
+    a.gate, a.gate_stride, a.norm_weight = BASE + 40 * (1 << 26), 4 * 128, BASE + 41 * (1 << 26)
+    assert _step(a, flags=kda.KDA_FLAG_VTILE(32)) == UNSUP      # the norm needs 128 columns
+
+
+def test_zero_requests_is_a_no_op():
+    a, _ = _valid_args(N=0)
+    a.q = a.k = a.v = a.g = a.beta = a.out = 0
+    assert _step(a) == 0
+
+
+def test_gated_rmsnorm_validation():
+    f = kda.library().kda_gated_rmsnorm
+    x, z, w, y = BASE, BASE + (1 << 26), BASE + 2 * (1 << 26), BASE + 3 * (1 << 26)
+    assert f(None, z, w, y, 4, 128, 1e-6, None) == NULL
+    assert f(x, z, w, y, 4, 127, 1e-6, None) == SHAPE
+    assert f(x, z, w, y, 4, 0, 1e-6, None) == SHAPE
+    assert f(x, z, w, y, 4, 128, -1.0, None) == SHAPE
+    assert f(x + 2, z, w, y, 4, 128, 1e-6, None) == ALIGN
+    assert f(x, z, w, x + 256, 4, 128, 1e-6, None) == ALIAS     # partial overlap
+    assert f(x, z, w, z, 4, 128, 1e-6, None) == ALIAS
+    assert f(x, z, w, x, 0, 128, 1e-6, None) == 0                # in place, no rows
+
+
+def test_valid_call_without_gpu_reports_device():
+    a, _ = _valid_args()
+    assert _step(a) == DEVICE

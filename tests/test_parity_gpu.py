@@ -1,0 +1,267 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, on the
+serving workloads at full size and on small cases that span several tiles
+with ragged tails, plus the bit-exact properties of the path."""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs as ki
+import linear_attention_recurrent_decode_amd as kda
+from kda_harness import (DEV, bf16_tensor, compare, f32_tensor, parity, run_gpu, run_oracle, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(name, rep):
+    print(f"[parity] {name}: {rep}", flush=True)
+
+
+# ------------------------------------------------------- full-size workloads
+@pytest.mark.parametrize("name", list(ki.WORKLOADS))
+def test_workload_full_size(name):
+    print(f"[parity] start {name}", flush=True)
+    p = ki.workload(name)
+    _log(name, parity(p))
+
+
+@pytest.mark.parametrize("width", [32, 64, 128])
+def test_dominant_shape_every_tile_width(width):
+    p = ki.workload("n32_t1_h8")
+    _log(f"n32_t1_h8 vtile={width}", parity(p, flags=kda.KDA_FLAG_VTILE(width)))
+
+
+def test_packed_workload_as_step_when_uniform():
+    p = ki.workload("n16_t4_h8")
+    _log("n16_t4_h8 packed", parity(p, packed=True))
+
+
+# ------------------------------------------------------- small / ragged cases
+SMALL = [
+    # (N, H, HV, T, num_slots, n_pad, norm)
+    (1, 1, 1, 1, 1, 0, False),
+    (3, 2, 6, 1, 9, 0, False),      # HV = 3H: three value heads per q/k head
+    (5, 3, 3, 3, 11, 1, False),
+    (7, 2, 4, None, 19, 2, False),  # packed, ragged lengths, padding rows
+    (9, 4, 4, 2, 12, 0, True),
+    (6, 1, 2, None, 8, 1, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL)
+def test_small_cases(case):
+    N, H, HV, T, slots, n_pad, norm = case
+    p = ki.make_problem("small", 77 + N, N=N, H=H, HV=HV, K=128, V=128, num_slots=slots, T=T,
+                        n_pad=n_pad, norm=norm)
+    _log(f"small {case}", parity(p))
+
+
+# ------------------------------------------------------- edge cases
+def test_all_requests_padding():
+    p = ki.make_problem("allpad", 5, N=4, H=2, HV=2, K=128, V=128, num_slots=6, T=None, n_pad=4)
+    parity(p)
+
+
+def test_out_of_range_slots_are_skipped():
+    p = ki.make_problem("oor", 6, N=5, H=2, HV=2, K=128, V=128, num_slots=8, T=2)
+    p.slot_idx[1] = 8
+    p.slot_idx[3] = -7
+    parity(p)
+
+
+def test_zero_length_requests_leave_state_alone():
+    p = ki.make_problem("zlen", 7, N=5, H=1, HV=2, K=128, V=128, num_slots=8, T=None)
+    lens = np.array([2, 0, 1, 0, 3])
+    p.cu_seqlens = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    tokens = int(p.cu_seqlens[-1])
+    for f in ("q", "k", "v", "g", "beta"):
+        setattr(p, f, getattr(p, f)[:tokens].copy())
+    free = [s for s in range(p.num_slots) if s not in set(p.slot_idx[[0, 2, 4]].tolist())]
+    p.slot_idx[[1, 3]] = free[:2]      # live, distinct slots, but no tokens: nothing may change
+    d = upload(p)
+    before = d.state.clone()
+    run_gpu(d, packed=True)
+    torch.cuda.synchronize()
+    for s in free[:2]:
+        assert torch.equal(d.state[s], before[s])
+    ref_out, ref_state = run_oracle(p)
+    compare(d, ref_out, ref_state)
+
+
+def test_zero_requests():
+    p = ki.make_problem("z", 8, N=1, H=1, HV=1, K=128, V=128, num_slots=1, T=1)
+    d = upload(p)
+    before = d.state.clone()
+    kda.kda_decode_step(d.q[:0], d.k[:0], d.v[:0], d.g[:0], d.beta[:0], d.state, d.slot_idx[:0], d.out[:0],
+                        T=1, scale=p.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(before, d.state)
+
+
+def test_reset_and_identity_on_gpu():
+    p = ki.make_problem("special", 9, N=4, H=2, HV=2, K=128, V=128, num_slots=4, T=1)
+    p.g[0] = -np.inf                         # request 0: full reset
+    p.g[1, :, ::3] = -np.inf                 # request 1: a third of the rows reset
+    p.g[2] = 0.0                             # request 2: identity (g = 0, beta = 0)
+    p.beta[2] = 0.0
+    d = upload(p)
+    before = d.state.clone()
+    run_gpu(d)
+    torch.cuda.synchronize()
+    s2 = int(p.slot_idx[2])
+    assert torch.equal(d.state[s2], before[s2])          # bitwise unchanged
+    ref_out, ref_state = run_oracle(p)
+    compare(d, ref_out, ref_state)
+
+
+def test_large_slot_offsets():
+    """Slots whose element offset exceeds 2^31 (pool > 8 GiB at HV = 8)."""
+    HV, slots = 8, 16400
+    p = ki.make_problem("big", 10, N=4, H=8, HV=HV, K=128, V=128, num_slots=slots, T=2)
+    p.slot_idx[:] = [16399, 16384, 3, 16390]
+    d = upload(p)
+    run_gpu(d)
+    torch.cuda.synchronize()
+    ref_out, ref_state = run_oracle(p)
+    _log("large offsets", compare(d, ref_out, ref_state))
+    del d
+    torch.cuda.empty_cache()
+
+
+def test_strided_views_of_fused_projection():
+    p = ki.make_problem("fused", 11, N=6, H=2, HV=4, K=128, V=128, num_slots=9, T=2)
+    d = upload(p)
+    T, HK, HVV = p.tokens, p.H * p.K, p.HV * p.V
+    fused = torch.zeros((T, 2 * HK + HVV + 64), dtype=torch.bfloat16, device=DEV)
+    fused[:, :HK] = d.q.reshape(T, HK)
+    fused[:, HK:2 * HK] = d.k.reshape(T, HK)
+    fused[:, 2 * HK:2 * HK + HVV] = d.v.reshape(T, HVV)
+    beta_wide = torch.zeros((T, p.HV + 3), dtype=torch.float32, device=DEV)
+    beta_wide[:, :p.HV] = d.beta
+    d.q = fused[:, :HK].view(T, p.H, p.K)
+    d.k = fused[:, HK:2 * HK].view(T, p.H, p.K)
+    d.v = fused[:, 2 * HK:2 * HK + HVV].view(T, p.HV, p.V)
+    d.beta = beta_wide[:, :p.HV]
+    run_gpu(d)
+    torch.cuda.synchronize()
+    ref_out, ref_state = run_oracle(p)
+    compare(d, ref_out, ref_state)
+
+
+# ------------------------------------------------------- bit-exact properties
+def _fresh(p, seed=1234):
+    d = upload(p, background_seed=seed)
+    return d
+
+
+def test_tile_widths_bit_identical():
+    for name in ("n32_t1_h8", "n8_t4_h8", "packed_n256_h12"):
+        p = ki.workload(name)
+        results = []
+        for width in (32, 64, 128):
+            d = _fresh(p)
+            run_gpu(d, flags=kda.KDA_FLAG_VTILE(width))
+            torch.cuda.synchronize()
+            results.append((d.out.view(torch.int16).clone(), d.state.clone()))
+        for o, s in results[1:]:
+            assert torch.equal(o, results[0][0]) and torch.equal(s, results[0][1]), name
+
+
+def test_chained_single_tokens_bit_identical():
+    p = ki.workload("n32_t4_h8")
+    d_multi = _fresh(p)
+    run_gpu(d_multi)
+    d = _fresh(p)
+    N = p.N
+    for t in range(4):
+        rows = torch.arange(N, device=DEV) * 4 + t
+        out_t = torch.empty((N, p.HV, p.V), dtype=torch.bfloat16, device=DEV)
+        kda.kda_decode_step(d.q[rows], d.k[rows], d.v[rows], d.g[rows], d.beta[rows], d.state, d.slot_idx,
+                            out_t, T=1, scale=p.scale)
+        d.out[rows] = out_t
+    torch.cuda.synchronize()
+    assert torch.equal(d.state, d_multi.state)
+    assert torch.equal(d.out.view(torch.int16), d_multi.out.view(torch.int16))
+
+
+def test_request_permutation_bit_identical():
+    p = ki.workload("packed_n256_h12")
+    d = _fresh(p)
+    run_gpu(d)
+    perm = np.random.default_rng(3).permutation(p.N)
+    cu = p.cu_seqlens
+    rows = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in perm])
+    lens = np.diff(cu)[perm]
+    cu2 = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    d2 = _fresh(p)
+    r = torch.from_numpy(rows).to(DEV)
+    out2 = torch.empty_like(d2.out)
+    kda.kda_decode_packed(d2.q[r], d2.k[r], d2.v[r], d2.g[r], d2.beta[r], d2.state,
+                          torch.from_numpy(p.slot_idx[perm].astype(np.int32)).to(DEV),
+                          torch.from_numpy(cu2).to(DEV), out2, scale=p.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(d2.state, d.state)
+    live_rows = torch.from_numpy(np.isin(rows, np.concatenate(
+        [np.arange(cu[n], cu[n + 1]) for n in p.live_requests()]))).to(DEV)
+    assert torch.equal(out2.view(torch.int16)[live_rows], d.out.view(torch.int16)[r][live_rows])
+
+
+def test_deterministic_and_non_default_stream():
+    p = ki.workload("n32_t1_h16_norm")
+    d1 = _fresh(p)
+    run_gpu(d1)
+    d2 = _fresh(p)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        run_gpu(d2)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(d1.state, d2.state)
+    assert torch.equal(d1.out.view(torch.int16), d2.out.view(torch.int16))
+
+
+def test_graph_replay_matches_eager():
+    p = ki.workload("n32_t1_h8")
+    eager = _fresh(p)
+    run_gpu(eager)
+    torch.cuda.synchronize()
+    d = _fresh(p)
+    init = d.state.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            run_gpu(d)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        d.state.copy_(init)                  # eager work between replays
+        d.out.view(torch.int16).fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d.state, eager.state)
+        assert torch.equal(d.out.view(torch.int16), eager.out.view(torch.int16))
+
+
+# ------------------------------------------------------- standalone norm
+@pytest.mark.parametrize("rows,V", [(512, 128), (5, 128), (3, 2), (7, 130), (33, 1024), (2, 8192)])
+def test_gated_rmsnorm(rows, V):
+    import oracle
+    x = ki.to_bf16_bits(ki.normal(31, 1, rows * V).reshape(rows, V) * 0.05)
+    z = ki.to_bf16_bits(ki.normal(31, 2, rows * V).reshape(rows, V))
+    w = ki.to_bf16_bits(1.0 + 0.02 * ki.normal(31, 3, V))
+    ref = oracle.gated_rmsnorm(x, z, w, 1e-6)
+    xt, zt, wt = bf16_tensor(x), bf16_tensor(z), bf16_tensor(w)
+    y = torch.empty_like(xt)
+    kda.kda_gated_rmsnorm(xt, zt, wt, y, 1e-6)
+    torch.cuda.synchronize()
+    from kda_harness import bf16_to_f64, bf16_ulp
+    got = bf16_to_f64(y)
+    err = np.abs(got - ref)
+    assert np.all(err <= 2e-3 + 2.0 ** -8 * np.abs(ref))
+    assert np.all(err <= bf16_ulp(ref) + 1e-6 * np.abs(ref).max())
+    # in place
+    kda.kda_gated_rmsnorm(xt, zt, wt, xt, 1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(xt.view(torch.int16), y.view(torch.int16))
