@@ -22,6 +22,9 @@ HIPCC_FLAGS = [
     "-fPIC",
     "-shared",
     "-Wall",
+    # every fused multiply-add in the kernels is an explicit fmaf: no implicit
+    # contraction, so inlined copies of the same code round the same way
+    "-ffp-contract=off",
     # no packed-fp32 instructions: scalar fp32 code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

@@ -10,8 +10,9 @@
 // Work decomposition.  One wave64 owns 32 value columns x all 128 key rows of
 // one (request, value head) tile: 4096 floats, 64 per lane, held in VGPRs for
 // every token of the call.  Lane l holds columns 4*(l%8) .. +3 (one 16-byte
-// vector per row) of the 16 key rows 16*(l/8) .. +15.  Each of the 16 loads of
-// a wave covers 8 rows x 128 contiguous bytes.  A workgroup is 1, 2 or 4 waves
+// vector per row) of the 16 key rows 16*(l/8) .. +15, so eight consecutive
+// lanes read one row's 128 contiguous bytes.  Each of the 16 loads of a wave
+// covers 8 rows x 128 bytes.  A workgroup is 1, 2 or 4 waves
 // (a value tile of 32, 64 or 128 columns); the grid is one workgroup per
 // (request, value head, value tile).  Columns never interact in the
 // recurrence, so the tiling cannot change a single result bit: every wave runs
@@ -27,8 +28,8 @@
 //   o_j = scale (w_j + v'_j kq)     -- equals scale * sum_i S'_ij q_i
 //   S'_ij = a_i S_ij + k_i v'_j
 // so both key-axis reductions come from one pass over the old state, and the
-// only cross-lane step per token is one 3-level butterfly over the 8 lanes
-// that share a column group.  The gated RMSNorm epilogue (b12x PR 249,
+// only cross-lane step per token is one 3-level reduction (DPP and permlane
+// swaps, no LDS) over the 8 lanes that share a column group.  The gated RMSNorm epilogue (b12x PR 249,
 // walkthrough: normalise and gate the decoded output) needs the sum of o^2
 // over all 128 columns, which forces the 4-wave tile and adds one LDS
 // exchange per token.
@@ -66,6 +67,8 @@ struct DecodeParams {
     float scale, eps;
 };
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -89,26 +92,197 @@ __device__ __forceinline__ float silu(float z)
     return z / (1.0f + __expf(-z));
 }
 
-// Sum over the 8 lanes of a column group (lane bits 3..5).  Every lane ends
-// with the same bits: each level adds the same two operands on both sides.
+// DPP lane moves (gfx9 DPP controls).
+#define KDA_DPP(x, ctrl)                                                                                   \
+    __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (x)), (ctrl), 0xF, 0xF, \
+                                                          false))
+constexpr int DPP_ROW_ROR8 = 0x128;          // lane l <- l^8 within its 16-lane row
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;   // lane l <- 7 - l within its 8-lane half row
+constexpr int DPP_QUAD_XOR1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;          // quad_perm [2,3,0,1]
+
+// gfx950 v_permlane16_swap / v_permlane32_swap exchange the odd 16-lane rows
+// (upper 32 lanes) of `a` with the even rows (lower 32 lanes) of `b`; with
+// a = b = x, a + b then pairs every lane with lane l^16 (l^32).  Both
+// registers are read and written, so they are in-out operands; the s_nop
+// pads give the two wait states a VALU result needs before these read it
+// (and before a DPP reads theirs).
+__device__ __forceinline__ float add_permlane16_swap(float x)
+{
+    uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+
+__device__ __forceinline__ float add_permlane32_swap(float x)
+{
+    uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+
+// Sum over the 8 lanes that share a column group (lane bits 3..5: lanes l,
+// l+8, .., l+56), all on the VALU.  Each level adds the same two operands on
+// both lanes of a pair, so every lane of the group ends with the same bits,
+// and the order of additions is the same for every tile width.
 __device__ __forceinline__ float sum_row_groups(float x)
 {
-    x += __shfl_xor(x, 8);
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
+    x += KDA_DPP(x, DPP_ROW_ROR8);
+    x = add_permlane16_swap(x);
+    return add_permlane32_swap(x);
 }
 
-// Sum over the 8 column groups of a wave (lane bits 0..2).
+// Sum over the 8 column groups of a wave (lane bits 0..2): pairs l <-> 7-l,
+// then l <-> l^1, then l <-> l^2, all symmetric, all on the VALU.
 __device__ __forceinline__ float sum_col_groups(float x)
 {
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
+    x += KDA_DPP(x, DPP_ROW_HALF_MIRROR);
+    x += KDA_DPP(x, DPP_QUAD_XOR1);
+    x += KDA_DPP(x, DPP_QUAD_XOR2);
     return x;
 }
 
-template <int NW, bool NORM>
+// One token's inputs as a lane needs them: q, k, g over its 16 key rows, v
+// over its 4 value columns, beta of the head.
+struct TokenIn {
+    uint4 k0, k1, q0, q1;
+    float4 g0, g1, g2, g3;
+    uint2 v;
+    float beta;
+};
+
+__device__ __forceinline__ void load_token(TokenIn &in, const DecodeParams &p, int64_t t, int h, int hv, int row0,
+                                           int col)
+{
+    const uint4 *kp = reinterpret_cast<const uint4 *>(p.k + t * p.k_stride + h * KD + row0);
+    const uint4 *qp = reinterpret_cast<const uint4 *>(p.q + t * p.q_stride + h * KD + row0);
+    const float4 *gp = reinterpret_cast<const float4 *>(p.g + t * p.g_stride + (int64_t)hv * KD + row0);
+    in.k0 = kp[0];
+    in.k1 = kp[1];
+    in.q0 = qp[0];
+    in.q1 = qp[1];
+    in.g0 = gp[0];
+    in.g1 = gp[1];
+    in.g2 = gp[2];
+    in.g3 = gp[3];
+    in.v = *reinterpret_cast<const uint2 *>(p.v + t * p.v_stride + (int64_t)hv * VD + col);
+    in.beta = p.beta[t * p.beta_stride + hv];
+}
+
+// Advance the lane's part of the state by one token and write its output.
+// Every floating-point operation is spelled out (explicit fmaf, no implicit
+// contraction), so each inlined copy of this function rounds identically.
+// With PREFETCH the next token's inputs are loaded into `in` as soon as this
+// token's are unpacked, so they are in flight while this token computes.
+template <bool NORM, bool PREFETCH>
+__device__ __forceinline__ void advance_token(f32x4 (&s)[ROWS_PER_LANE], TokenIn &in, const DecodeParams &p,
+                                              int64_t t, int64_t eos, int h, int hv, int lane, int wave, int rg,
+                                              int row0, int col, float (&norm_partial)[2][4])
+{
+    // unpack; the decay factors a_i = exp(g_i)
+    float kk[ROWS_PER_LANE], qq[ROWS_PER_LANE], a[ROWS_PER_LANE];
+    const uint32_t kw[8] = {in.k0.x, in.k0.y, in.k0.z, in.k0.w, in.k1.x, in.k1.y, in.k1.z, in.k1.w};
+    const uint32_t qw[8] = {in.q0.x, in.q0.y, in.q0.z, in.q0.w, in.q1.x, in.q1.y, in.q1.z, in.q1.w};
+    const float gg[16] = {in.g0.x, in.g0.y, in.g0.z, in.g0.w, in.g1.x, in.g1.y, in.g1.z, in.g1.w,
+                          in.g2.x, in.g2.y, in.g2.z, in.g2.w, in.g3.x, in.g3.y, in.g3.z, in.g3.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        kk[2 * i] = bf16_lo(kw[i]);
+        kk[2 * i + 1] = bf16_hi(kw[i]);
+        qq[2 * i] = bf16_lo(qw[i]);
+        qq[2 * i + 1] = bf16_hi(qw[i]);
+    }
+    float kq = 0.f;
+#pragma unroll
+    for (int i = 0; i < ROWS_PER_LANE; ++i) {
+        a[i] = __expf(gg[i]);
+        kq = fmaf(kk[i], qq[i], kq);
+    }
+    const float v0 = bf16_lo(in.v.x), v1 = bf16_hi(in.v.x), v2 = bf16_lo(in.v.y), v3 = bf16_hi(in.v.y);
+    const float b = in.beta;
+    if constexpr (PREFETCH) {
+        if (t + 1 < eos)
+            load_token(in, p, t + 1, h, hv, row0, col);
+    }
+
+    // one pass over the old state: both key-axis partial sums
+    float u0 = 0.f, u1 = 0.f, u2 = 0.f, u3 = 0.f;
+    float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f;
+#pragma unroll
+    for (int i = 0; i < ROWS_PER_LANE; ++i) {
+        const float ak = a[i] * kk[i], aq = a[i] * qq[i];
+        u0 = fmaf(s[i].x, ak, u0);
+        u1 = fmaf(s[i].y, ak, u1);
+        u2 = fmaf(s[i].z, ak, u2);
+        u3 = fmaf(s[i].w, ak, u3);
+        w0 = fmaf(s[i].x, aq, w0);
+        w1 = fmaf(s[i].y, aq, w1);
+        w2 = fmaf(s[i].z, aq, w2);
+        w3 = fmaf(s[i].w, aq, w3);
+    }
+    u0 = sum_row_groups(u0);
+    u1 = sum_row_groups(u1);
+    u2 = sum_row_groups(u2);
+    u3 = sum_row_groups(u3);
+    w0 = sum_row_groups(w0);
+    w1 = sum_row_groups(w1);
+    w2 = sum_row_groups(w2);
+    w3 = sum_row_groups(w3);
+    kq = sum_row_groups(kq);
+
+    // delta correction, readout, rank-1 update
+    const float vp0 = b * (v0 - u0);
+    const float vp1 = b * (v1 - u1);
+    const float vp2 = b * (v2 - u2);
+    const float vp3 = b * (v3 - u3);
+    float o0 = p.scale * fmaf(vp0, kq, w0);
+    float o1 = p.scale * fmaf(vp1, kq, w1);
+    float o2 = p.scale * fmaf(vp2, kq, w2);
+    float o3 = p.scale * fmaf(vp3, kq, w3);
+#pragma unroll
+    for (int i = 0; i < ROWS_PER_LANE; ++i) {
+        s[i].x = fmaf(kk[i], vp0, a[i] * s[i].x);
+        s[i].y = fmaf(kk[i], vp1, a[i] * s[i].y);
+        s[i].z = fmaf(kk[i], vp2, a[i] * s[i].z);
+        s[i].w = fmaf(kk[i], vp3, a[i] * s[i].w);
+    }
+
+    if constexpr (NORM) {
+        // gated RMSNorm over the head's 128 columns: the four waves of the
+        // workgroup hold 32 columns each and meet in LDS.  The gate and
+        // weight are loaded here, off the state tile's critical path.
+        const uint2 zz = *reinterpret_cast<const uint2 *>(p.gate + t * p.gate_stride + (int64_t)hv * VD + col);
+        const uint2 nw = *reinterpret_cast<const uint2 *>(p.norm_weight + col);
+        float ss = fmaf(o3, o3, fmaf(o2, o2, fmaf(o1, o1, o0 * o0)));
+        ss = sum_col_groups(ss);
+        float *slot_sum = norm_partial[t & 1];
+        if (lane == 0)
+            slot_sum[wave] = ss;
+        __syncthreads();
+        const float total = (slot_sum[0] + slot_sum[1]) + (slot_sum[2] + slot_sum[3]);
+        const float r = rsqrtf(fmaf(total, 1.0f / VD, p.eps));
+        o0 = o0 * r * bf16_lo(nw.x) * silu(bf16_lo(zz.x));
+        o1 = o1 * r * bf16_hi(nw.x) * silu(bf16_hi(zz.x));
+        o2 = o2 * r * bf16_lo(nw.y) * silu(bf16_lo(zz.y));
+        o3 = o3 * r * bf16_hi(nw.y) * silu(bf16_hi(zz.y));
+    }
+    if (rg == 0) {
+        uint2 packed;
+        packed.x = pack_bf16x2(o0, o1);
+        packed.y = pack_bf16x2(o2, o3);
+        *reinterpret_cast<uint2 *>(p.out + t * p.out_stride + (int64_t)hv * VD + col) = packed;
+    }
+}
+
+// Two bodies share advance_token and round identically:
+//   PEELED = false: the token loop prefetches token t+1 while token t
+//     computes; the first token's inputs go out just before the state tile.
+//     Fastest for one token per request and for packed batches.
+//   PEELED = true: the first token is peeled off the loop and the tile's
+//     loads are issued around the first token's input loads (4 rows, the
+//     inputs, 12 rows), pinned by scheduling fences; later tokens load at the
+//     top of their iteration.  Fastest for several tokens per request.
+template <int NW, bool NORM, bool PEELED>
 __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(DecodeParams p)
 {
     static_assert(NW == 1 || NW == 2 || NW == 4, "a workgroup is 1, 2 or 4 waves");
@@ -144,115 +318,46 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(DecodeParams p)
     const int col = (vt * NW + wave) * 32 + cg * 4;
     const int row0 = rg * ROWS_PER_LANE;
 
-    float *tile = p.state + slot * p.slot_stride + (int64_t)hv * (KD * VD) + (int64_t)row0 * VD + col;
-    float4 s[ROWS_PER_LANE];
-#pragma unroll
-    for (int i = 0; i < ROWS_PER_LANE; ++i)
-        s[i] = *reinterpret_cast<const float4 *>(tile + i * VD);
-
+    // The tile is streamed: read once, written once, no reuse in this call,
+    // so both directions use non-temporal accesses.
+    f32x4 *tile = reinterpret_cast<f32x4 *>(p.state + slot * p.slot_stride + (int64_t)hv * (KD * VD) +
+                                            (int64_t)row0 * VD + col);
+    f32x4 s[ROWS_PER_LANE];
+    TokenIn in;
     __shared__ float norm_partial[2][4];
 
-    for (int64_t t = bos; t < eos; ++t) {
-        const uint4 *kp = reinterpret_cast<const uint4 *>(p.k + t * p.k_stride + h * KD + row0);
-        const uint4 *qp = reinterpret_cast<const uint4 *>(p.q + t * p.q_stride + h * KD + row0);
-        const float4 *gp = reinterpret_cast<const float4 *>(p.g + t * p.g_stride + (int64_t)hv * KD + row0);
-        const uint4 k0 = kp[0], k1 = kp[1];
-        const uint4 q0 = qp[0], q1 = qp[1];
-        const uint2 vv = *reinterpret_cast<const uint2 *>(p.v + t * p.v_stride + (int64_t)hv * VD + col);
-        const float b = p.beta[t * p.beta_stride + hv];
-
-        float kk[ROWS_PER_LANE], qq[ROWS_PER_LANE], a[ROWS_PER_LANE];
-        const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-        const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    if constexpr (!PEELED) {
+        // first token's inputs, then the whole tile
+        load_token(in, p, bos, h, hv, row0, col);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            kk[2 * i] = bf16_lo(kw[i]);
-            kk[2 * i + 1] = bf16_hi(kw[i]);
-            qq[2 * i] = bf16_lo(qw[i]);
-            qq[2 * i + 1] = bf16_hi(qw[i]);
-        }
+        for (int i = 0; i < ROWS_PER_LANE; ++i)
+            s[i] = __builtin_nontemporal_load(tile + i * (VD / 4));
+        for (int64_t t = bos; t < eos; ++t)
+            advance_token<NORM, true>(s, in, p, t, eos, h, hv, lane, wave, rg, row0, col, norm_partial);
+    } else {
+        constexpr int FIRST_ROWS = 4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float4 gg = gp[i];
-            a[4 * i + 0] = __expf(gg.x);
-            a[4 * i + 1] = __expf(gg.y);
-            a[4 * i + 2] = __expf(gg.z);
-            a[4 * i + 3] = __expf(gg.w);
-        }
-
-        // one pass over the old state: both key-axis partial sums
-        float u0 = 0.f, u1 = 0.f, u2 = 0.f, u3 = 0.f;
-        float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f;
-        float kq = 0.f;
+        for (int i = 0; i < FIRST_ROWS; ++i)
+            s[i] = __builtin_nontemporal_load(tile + i * (VD / 4));
+        __builtin_amdgcn_sched_barrier(0);
+        load_token(in, p, bos, h, hv, row0, col);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < ROWS_PER_LANE; ++i) {
-            const float ak = a[i] * kk[i];
-            const float aq = a[i] * qq[i];
-            u0 = fmaf(s[i].x, ak, u0);
-            u1 = fmaf(s[i].y, ak, u1);
-            u2 = fmaf(s[i].z, ak, u2);
-            u3 = fmaf(s[i].w, ak, u3);
-            w0 = fmaf(s[i].x, aq, w0);
-            w1 = fmaf(s[i].y, aq, w1);
-            w2 = fmaf(s[i].z, aq, w2);
-            w3 = fmaf(s[i].w, aq, w3);
-            kq = fmaf(kk[i], qq[i], kq);
-        }
-        u0 = sum_row_groups(u0);
-        u1 = sum_row_groups(u1);
-        u2 = sum_row_groups(u2);
-        u3 = sum_row_groups(u3);
-        w0 = sum_row_groups(w0);
-        w1 = sum_row_groups(w1);
-        w2 = sum_row_groups(w2);
-        w3 = sum_row_groups(w3);
-        kq = sum_row_groups(kq);
-
-        // delta correction, readout, rank-1 update
-        const float vp0 = b * (bf16_lo(vv.x) - u0);
-        const float vp1 = b * (bf16_hi(vv.x) - u1);
-        const float vp2 = b * (bf16_lo(vv.y) - u2);
-        const float vp3 = b * (bf16_hi(vv.y) - u3);
-        float o0 = p.scale * fmaf(vp0, kq, w0);
-        float o1 = p.scale * fmaf(vp1, kq, w1);
-        float o2 = p.scale * fmaf(vp2, kq, w2);
-        float o3 = p.scale * fmaf(vp3, kq, w3);
-#pragma unroll
-        for (int i = 0; i < ROWS_PER_LANE; ++i) {
-            s[i].x = fmaf(kk[i], vp0, a[i] * s[i].x);
-            s[i].y = fmaf(kk[i], vp1, a[i] * s[i].y);
-            s[i].z = fmaf(kk[i], vp2, a[i] * s[i].z);
-            s[i].w = fmaf(kk[i], vp3, a[i] * s[i].w);
-        }
-
-        if constexpr (NORM) {
-            float ss = o0 * o0 + o1 * o1 + o2 * o2 + o3 * o3;
-            ss = sum_col_groups(ss);
-            float *slot_sum = norm_partial[t & 1];
-            if (lane == 0)
-                slot_sum[wave] = ss;
-            __syncthreads();
-            const float total = (slot_sum[0] + slot_sum[1]) + (slot_sum[2] + slot_sum[3]);
-            const float r = rsqrtf(total * (1.0f / VD) + p.eps);
-            const uint2 zz = *reinterpret_cast<const uint2 *>(p.gate + t * p.gate_stride + (int64_t)hv * VD + col);
-            const uint2 ww = *reinterpret_cast<const uint2 *>(p.norm_weight + col);
-            o0 = o0 * r * bf16_lo(ww.x) * silu(bf16_lo(zz.x));
-            o1 = o1 * r * bf16_hi(ww.x) * silu(bf16_hi(zz.x));
-            o2 = o2 * r * bf16_lo(ww.y) * silu(bf16_lo(zz.y));
-            o3 = o3 * r * bf16_hi(ww.y) * silu(bf16_hi(zz.y));
-        }
-        if (rg == 0) {
-            uint2 packed;
-            packed.x = pack_bf16x2(o0, o1);
-            packed.y = pack_bf16x2(o2, o3);
-            *reinterpret_cast<uint2 *>(p.out + t * p.out_stride + (int64_t)hv * VD + col) = packed;
+        for (int i = FIRST_ROWS; i < ROWS_PER_LANE; ++i)
+            s[i] = __builtin_nontemporal_load(tile + i * (VD / 4));
+        // all 16 loads of the tile are in flight before any math starts
+        __builtin_amdgcn_sched_barrier(0);
+        advance_token<NORM, false>(s, in, p, bos, eos, h, hv, lane, wave, rg, row0, col, norm_partial);
+        for (int64_t t = bos + 1; t < eos; ++t) {
+            load_token(in, p, t, h, hv, row0, col);
+            advance_token<NORM, false>(s, in, p, t, eos, h, hv, lane, wave, rg, row0, col, norm_partial);
         }
     }
 
     // slot scatter: the tile goes back where it came from
 #pragma unroll
     for (int i = 0; i < ROWS_PER_LANE; ++i)
-        *reinterpret_cast<float4 *>(tile + i * VD) = s[i];
+        __builtin_nontemporal_store(s[i], tile + i * (VD / 4));
 }
 
 // Standalone gated RMSNorm: one wave per row, 4 rows per workgroup.
@@ -414,14 +519,15 @@ int32_t plan_vtile(int64_t units, int32_t T, bool norm)
 }
 
 template <int NW, bool NORM>
-kda_status launch_decode(const DecodeParams &p, int64_t units, hipStream_t stream)
+kda_status launch_decode(const DecodeParams &p, int64_t units, bool peeled, hipStream_t stream)
 {
     const int64_t blocks = units * (4 / NW);
     if (blocks > 0x7FFFFFFF)
         return KDA_ERR_SHAPE;
     void *args[] = {const_cast<DecodeParams *>(&p)};
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM>),
-                                         dim3((uint32_t)blocks), dim3(64 * NW), args, 0, stream);
+    const void *fn = peeled ? reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, true>)
+                            : reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, false>);
+    const hipError_t e = hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(64 * NW), args, 0, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
@@ -474,12 +580,14 @@ kda_status run_decode(const kda_decode_args *a, int32_t T, const int32_t *cu_seq
     p.eps = a->norm_eps;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // several tokens per request in a step call: the peeled body
+    const bool peeled = cu_seqlens == nullptr && T > 1;
     if (norm)
-        return launch_decode<4, true>(p, units, s);
+        return launch_decode<4, true>(p, units, peeled, s);
     switch (vtile) {
-    case 32: return launch_decode<1, false>(p, units, s);
-    case 64: return launch_decode<2, false>(p, units, s);
-    default: return launch_decode<4, false>(p, units, s);
+    case 32: return launch_decode<1, false>(p, units, peeled, s);
+    case 64: return launch_decode<2, false>(p, units, peeled, s);
+    default: return launch_decode<4, false>(p, units, peeled, s);
     }
 }
 
