@@ -132,6 +132,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="also time cache-resident calls (same slots every call)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the timed region, run 5 plain device copies of this many MiB (untimed), "
+                         "a known-size reference for hardware byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -249,6 +252,15 @@ def main():
         torch.cuda.synchronize()
         warm = e0.elapsed_time(e1) * 1000.0 / args.steps
         log(f"[bench] cache-resident: {warm:.3f} us/call")
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 18            # floats
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     achieved = nbytes["total"] / (us_per_call * 1e-6) / 1e9
     state_gbps = nbytes["state"] / (us_per_call * 1e-6) / 1e9

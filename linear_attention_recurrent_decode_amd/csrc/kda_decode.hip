@@ -354,7 +354,11 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(DecodeParams p)
         }
     }
 
-    // slot scatter: the tile goes back where it came from
+    // slot scatter: the tile goes back where it came from.  The two waves of
+    // a 64-column tile store together, so each 512-byte state row gets its
+    // 256 bytes written at once (measured faster from 256 to 1023 tiles).
+    if constexpr (NW == 2)
+        __syncthreads();
 #pragma unroll
     for (int i = 0; i < ROWS_PER_LANE; ++i)
         __builtin_nontemporal_store(s[i], tile + i * (VD / 4));
@@ -506,16 +510,22 @@ kda_status validate(const kda_decode_args *a, int64_t tokens, const int32_t *cu_
     return KDA_OK;
 }
 
+// Value-tile width from the number of (request, value head) tiles, tuned on
+// MI355X with cold caches (256 compute units):
+//   fewer tiles than compute units: 32 columns, one wave per workgroup, the
+//     most workgroups in flight for a latency-bound call;
+//   one token per request, 256 .. 1023 tiles: 64 columns;
+//   several tokens per request, or 1024 tiles and up: 128 columns.
+// The norm epilogue needs all 128 columns in one workgroup.
 int32_t plan_vtile(int64_t units, int32_t T, bool norm)
 {
-    (void)T;
     if (norm)
         return 128;
-    if (units >= 256)
-        return 128;
-    if (units >= 128)
+    if (units < 256)
+        return 32;
+    if (T == 1 && units < 1024)
         return 64;
-    return 32;
+    return 128;
 }
 
 template <int NW, bool NORM>
@@ -545,7 +555,7 @@ kda_status run_decode(const kda_decode_args *a, int32_t T, const int32_t *cu_seq
     const int64_t units = (int64_t)a->N * a->HV;
     int vtile = vtile_from_flags(flags);
     if (vtile == 0)
-        vtile = plan_vtile(units, T, norm);
+        vtile = plan_vtile(units, cu_seqlens ? 1 : T, norm);
     if (norm && vtile != 128)
         return KDA_ERR_UNSUPPORTED;
     st = check_device();
@@ -580,8 +590,9 @@ kda_status run_decode(const kda_decode_args *a, int32_t T, const int32_t *cu_seq
     p.eps = a->norm_eps;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // several tokens per request in a step call: the peeled body
-    const bool peeled = cu_seqlens == nullptr && T > 1;
+    // several tokens per request in a step call, or a launch smaller than
+    // the chip: the peeled body
+    const bool peeled = cu_seqlens == nullptr && (T > 1 || units < 256);
     if (norm)
         return launch_decode<4, true>(p, units, peeled, s);
     switch (vtile) {
