@@ -274,15 +274,125 @@ __device__ __forceinline__ void advance_token(f32x4 (&s)[ROWS_PER_LANE], TokenIn
     }
 }
 
-// Two bodies share advance_token and round identically:
-//   PEELED = false: the token loop prefetches token t+1 while token t
-//     computes; the first token's inputs go out just before the state tile.
-//     Fastest for one token per request and for packed batches.
-//   PEELED = true: the first token is peeled off the loop and the tile's
-//     loads are issued around the first token's input loads (4 rows, the
-//     inputs, 12 rows), pinned by scheduling fences; later tokens load at the
-//     top of their iteration.  Fastest for several tokens per request.
-template <int NW, bool NORM, bool PEELED>
+// Token inputs of up to STAGE_TOKENS tokens of one (request, value head),
+// staged in LDS by the whole workgroup: q, k, g over all 128 key rows, v over
+// the workgroup's columns, beta.
+constexpr int STAGE_TOKENS = 4;
+
+template <int NW>
+struct TokenStage {
+    uint4 k[STAGE_TOKENS][KD / 8];
+    uint4 q[STAGE_TOKENS][KD / 8];
+    float4 g[STAGE_TOKENS][KD / 4];
+    uint2 v[STAGE_TOKENS][NW * 8];
+    float beta[STAGE_TOKENS];
+};
+
+// Cooperative global -> LDS copy of tokens t0 .. t0+nt-1 (nt <= STAGE_TOKENS),
+// in two halves so that the state tile's loads can be issued in between: the
+// loads into registers, then (after the tile's loads) the LDS writes.
+template <int NW>
+struct StagePieces {
+    static constexpr int THREADS = 64 * NW;
+    static constexpr int PIECES = KD / 8 + KD / 8 + KD / 4;   // 16-byte pieces of k, q, g per token
+    static constexpr int ITER = (STAGE_TOKENS * PIECES + THREADS - 1) / THREADS;
+    static constexpr int VITER = (STAGE_TOKENS * NW * 8 + THREADS - 1) / THREADS;
+    uint4 kqg[ITER];
+    uint2 v[VITER];
+    float beta;
+};
+
+template <int NW>
+__device__ __forceinline__ void stage_load(StagePieces<NW> &r, const DecodeParams &p, int64_t t0, int nt, int h,
+                                           int hv, int col0)
+{
+    using SP = StagePieces<NW>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < SP::ITER; ++it) {
+        const int idx = tid + it * SP::THREADS;
+        if (idx < nt * SP::PIECES) {
+            const int j = idx / SP::PIECES, e = idx - j * SP::PIECES;
+            const int64_t t = t0 + j;
+            const uint4 *src = e < KD / 8   ? reinterpret_cast<const uint4 *>(p.k + t * p.k_stride + h * KD) + e
+                               : e < KD / 4 ? reinterpret_cast<const uint4 *>(p.q + t * p.q_stride + h * KD) + (e - KD / 8)
+                                            : reinterpret_cast<const uint4 *>(p.g + t * p.g_stride + (int64_t)hv * KD) +
+                                                  (e - KD / 4);
+            r.kqg[it] = *src;
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < SP::VITER; ++it) {
+        const int idx = tid + it * SP::THREADS;
+        if (idx < nt * NW * 8) {
+            const int j = idx / (NW * 8), e = idx - j * (NW * 8);
+            r.v[it] = reinterpret_cast<const uint2 *>(p.v + (t0 + j) * p.v_stride + (int64_t)hv * VD + col0)[e];
+        }
+    }
+    if (tid < nt)
+        r.beta = p.beta[(t0 + tid) * p.beta_stride + hv];
+}
+
+template <int NW>
+__device__ __forceinline__ void stage_store(TokenStage<NW> &st, const StagePieces<NW> &r, int nt)
+{
+    using SP = StagePieces<NW>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < SP::ITER; ++it) {
+        const int idx = tid + it * SP::THREADS;
+        if (idx < nt * SP::PIECES) {
+            const int j = idx / SP::PIECES, e = idx - j * SP::PIECES;
+            if (e < KD / 8)
+                st.k[j][e] = r.kqg[it];
+            else if (e < KD / 4)
+                st.q[j][e - KD / 8] = r.kqg[it];
+            else
+                st.g[j][e - KD / 4] = __builtin_bit_cast(float4, r.kqg[it]);
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < SP::VITER; ++it) {
+        const int idx = tid + it * SP::THREADS;
+        if (idx < nt * NW * 8) {
+            const int j = idx / (NW * 8), e = idx - j * (NW * 8);
+            st.v[j][e] = r.v[it];
+        }
+    }
+    if (tid < nt)
+        st.beta[tid] = r.beta;
+}
+
+__device__ __forceinline__ void read_staged(TokenIn &in, const uint4 (&k)[KD / 8], const uint4 (&q)[KD / 8],
+                                            const float4 (&g)[KD / 4], uint2 v, float beta, int rg)
+{
+    in.k0 = k[2 * rg];
+    in.k1 = k[2 * rg + 1];
+    in.q0 = q[2 * rg];
+    in.q1 = q[2 * rg + 1];
+    in.g0 = g[4 * rg];
+    in.g1 = g[4 * rg + 1];
+    in.g2 = g[4 * rg + 2];
+    in.g3 = g[4 * rg + 3];
+    in.v = v;
+    in.beta = beta;
+}
+
+// Three bodies share advance_token and round identically:
+//   BODY_LOOP: the token loop prefetches token t+1 while token t computes;
+//     the first token's inputs go out just before the state tile.  Fastest
+//     for one token per request from one tile per compute unit up.
+//   BODY_PEELED: the first token is peeled off the loop and the tile's loads
+//     are issued around the first token's input loads (4 rows, the inputs,
+//     12 rows), pinned by scheduling fences; later tokens load at the top of
+//     their iteration.  Fastest for step calls with several tokens per
+//     request and for launches below one tile per compute unit.
+//   BODY_STAGED: the workgroup copies the inputs of up to STAGE_TOKENS tokens
+//     into LDS while the tile is in flight, so the token loop reads no global
+//     memory.  Fastest for packed batches of mixed lengths.
+constexpr int BODY_LOOP = 0, BODY_PEELED = 1, BODY_STAGED = 2;
+
+template <int NW, bool NORM, int BODY>
 __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(DecodeParams p)
 {
     static_assert(NW == 1 || NW == 2 || NW == 4, "a workgroup is 1, 2 or 4 waves");
@@ -326,7 +436,7 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(DecodeParams p)
     TokenIn in;
     __shared__ float norm_partial[2][4];
 
-    if constexpr (!PEELED) {
+    if constexpr (BODY == BODY_LOOP) {
         // first token's inputs, then the whole tile
         load_token(in, p, bos, h, hv, row0, col);
 #pragma unroll
@@ -334,7 +444,7 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(DecodeParams p)
             s[i] = __builtin_nontemporal_load(tile + i * (VD / 4));
         for (int64_t t = bos; t < eos; ++t)
             advance_token<NORM, true>(s, in, p, t, eos, h, hv, lane, wave, rg, row0, col, norm_partial);
-    } else {
+    } else if constexpr (BODY == BODY_PEELED) {
         constexpr int FIRST_ROWS = 4;
 #pragma unroll
         for (int i = 0; i < FIRST_ROWS; ++i)
@@ -351,6 +461,32 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(DecodeParams p)
         for (int64_t t = bos + 1; t < eos; ++t) {
             load_token(in, p, t, h, hv, row0, col);
             advance_token<NORM, false>(s, in, p, t, eos, h, hv, lane, wave, rg, row0, col, norm_partial);
+        }
+    } else {
+        __shared__ TokenStage<NW> st;
+        const int col0 = vt * NW * 32;     // first column of the workgroup's tile
+        int nt = (int)min<int64_t>(eos - bos, STAGE_TOKENS);
+        StagePieces<NW> pieces;
+        stage_load<NW>(pieces, p, bos, nt, h, hv, col0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < ROWS_PER_LANE; ++i)
+            s[i] = __builtin_nontemporal_load(tile + i * (VD / 4));
+        __builtin_amdgcn_sched_barrier(0);
+        stage_store<NW>(st, pieces, nt);   // waits for the inputs only, not the tile
+        for (int64_t t0 = bos; t0 < eos; t0 += STAGE_TOKENS) {
+            if (t0 != bos) {
+                __syncthreads();           // every wave is done with the previous chunk
+                nt = (int)min<int64_t>(eos - t0, STAGE_TOKENS);
+                stage_load<NW>(pieces, p, t0, nt, h, hv, col0);
+                stage_store<NW>(st, pieces, nt);
+            }
+            __syncthreads();
+            for (int j = 0; j < nt; ++j) {
+                read_staged(in, st.k[j], st.q[j], st.g[j], st.v[j][wave * 8 + cg], st.beta[j], rg);
+                advance_token<NORM, false>(s, in, p, t0 + j, eos, h, hv, lane, wave, rg, row0, col,
+                                           norm_partial);
+            }
         }
     }
 
@@ -529,14 +665,15 @@ int32_t plan_vtile(int64_t units, int32_t T, bool norm)
 }
 
 template <int NW, bool NORM>
-kda_status launch_decode(const DecodeParams &p, int64_t units, bool peeled, hipStream_t stream)
+kda_status launch_decode(const DecodeParams &p, int64_t units, int body, hipStream_t stream)
 {
     const int64_t blocks = units * (4 / NW);
     if (blocks > 0x7FFFFFFF)
         return KDA_ERR_SHAPE;
     void *args[] = {const_cast<DecodeParams *>(&p)};
-    const void *fn = peeled ? reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, true>)
-                            : reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, false>);
+    const void *fn = body == BODY_STAGED   ? reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_STAGED>)
+                     : body == BODY_PEELED ? reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_PEELED>)
+                                           : reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_LOOP>);
     const hipError_t e = hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(64 * NW), args, 0, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
@@ -590,15 +727,17 @@ kda_status run_decode(const kda_decode_args *a, int32_t T, const int32_t *cu_seq
     p.eps = a->norm_eps;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // several tokens per request in a step call, or a launch smaller than
-    // the chip: the peeled body
-    const bool peeled = cu_seqlens == nullptr && (T > 1 || units < 256);
+    // packed batches: the staged body; step calls with several tokens per
+    // request or fewer tiles than compute units: the peeled body; otherwise
+    // the prefetching loop (all measured on MI355X, cold caches)
+    const int body = cu_seqlens != nullptr ? BODY_STAGED
+                     : (T > 1 || units < 256) ? BODY_PEELED : BODY_LOOP;
     if (norm)
-        return launch_decode<4, true>(p, units, peeled, s);
+        return launch_decode<4, true>(p, units, body, s);
     switch (vtile) {
-    case 32: return launch_decode<1, false>(p, units, peeled, s);
-    case 64: return launch_decode<2, false>(p, units, peeled, s);
-    default: return launch_decode<4, false>(p, units, peeled, s);
+    case 32: return launch_decode<1, false>(p, units, body, s);
+    case 64: return launch_decode<2, false>(p, units, body, s);
+    default: return launch_decode<4, false>(p, units, body, s);
     }
 }
 

@@ -55,6 +55,34 @@ def test_small_cases(case):
     _log(f"small {case}", parity(p))
 
 
+@pytest.mark.parametrize("t_max", [6, 9])
+def test_packed_long_requests(t_max):
+    """Requests longer than one staging chunk of tokens (up to 9 tokens)."""
+    p = ki.make_problem("long", 40 + t_max, N=24, H=4, HV=8, K=128, V=128, num_slots=40, T=None,
+                        t_max=t_max, n_pad=3)
+    assert np.diff(p.cu_seqlens).max() > 4
+    _log(f"packed t_max={t_max}", parity(p))
+
+
+def test_step_six_tokens():
+    p = ki.make_problem("t6", 46, N=10, H=2, HV=4, K=128, V=128, num_slots=16, T=6)
+    _log("step T=6", parity(p))
+
+
+def test_packed_and_step_bodies_bit_identical():
+    """A uniform packed call and the step call over the same tokens give the
+    same bits (different kernel bodies, same arithmetic)."""
+    for name in ("n32_t4_h8", "n8_t4_h8"):
+        p = ki.workload(name)
+        a = _fresh(p)
+        run_gpu(a, packed=False)
+        b = _fresh(p)
+        run_gpu(b, packed=True)
+        torch.cuda.synchronize()
+        assert torch.equal(a.state, b.state), name
+        assert torch.equal(a.out.view(torch.int16), b.out.view(torch.int16)), name
+
+
 # ------------------------------------------------------- edge cases
 def test_all_requests_padding():
     p = ki.make_problem("allpad", 5, N=4, H=2, HV=2, K=128, V=128, num_slots=6, T=None, n_pad=4)
