@@ -47,7 +47,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(p) -> dict:
+def algorithmic_bytes(p, state_elem: int = 4) -> dict:
     """Bytes the call must move at least: each live (request, value head)
     reads and writes its K x V fp32 state once; each live token reads q, k
     (per q/k head), v, g, beta (per value head) and writes out (plus the gate
@@ -55,7 +55,7 @@ def algorithmic_bytes(p) -> dict:
     live = p.live_requests()
     lens = np.diff(p.cu_seqlens.astype(np.int64))
     live_tokens = int(lens[live].sum())
-    state = 2 * len(live) * p.HV * p.K * p.V * 4
+    state = 2 * len(live) * p.HV * p.K * p.V * state_elem
     per_token = 2 * p.H * p.K * 2 + p.HV * p.V * 2 + p.HV * p.K * 4 + p.HV * 4 + p.HV * p.V * 2
     if p.gate is not None:
         per_token += p.HV * p.V * 2
@@ -132,6 +132,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="also time cache-resident calls (same slots every call)")
+    ap.add_argument("--state", choices=("fp32", "bf16"), default="fp32", help="state pool element type")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed region, run 5 plain device copies of this many MiB (untimed), "
                          "a known-size reference for hardware byte counters")
@@ -155,11 +156,13 @@ def main():
     lib = kda.library()
 
     p = ki.workload(args.workload)
-    nbytes = algorithmic_bytes(p)
+    bf16_state = args.state == "bf16"
+    state_dtype = torch.bfloat16 if bf16_state else torch.float32
+    nbytes = algorithmic_bytes(p, 2 if bf16_state else 4)
     sets = slot_sets(p, ki)
     per_call_read = nbytes["state"] // 2
     R = max(1, math.ceil(COLD_BYTES / max(1, len(sets) * per_call_read)))
-    pool_bytes = p.num_slots * p.slot_elems * 4
+    pool_bytes = p.num_slots * p.slot_elems * (2 if bf16_state else 4)
     if R * pool_bytes > (96 << 30):
         R = max(1, (96 << 30) // pool_bytes)
     log(f"[bench] workload {p.name}: N={p.N} T={p.T} H={p.H} HV={p.HV} tokens={p.tokens} "
@@ -176,14 +179,17 @@ def main():
     cu = torch.from_numpy(p.cu_seqlens.astype(np.int32)).to(dev)
     out = torch.zeros((p.tokens, p.HV, p.V), dtype=torch.bfloat16, device=dev)
 
-    pools = [torch.empty((p.num_slots, p.HV, p.K, p.V), dtype=torch.float32, device=dev) for _ in range(R)]
+    pools = [torch.empty((p.num_slots, p.HV, p.K, p.V), dtype=state_dtype, device=dev) for _ in range(R)]
     chunk = max(1, (64 << 20) // (p.slot_elems * 4))
     for s0 in range(0, p.num_slots, chunk):
         sl = np.arange(s0, min(p.num_slots, s0 + chunk))
-        pools[0][s0:s0 + len(sl)] = torch.from_numpy(p.state_slots(sl)).to(dev)
+        vals = p.state_slots(sl)
+        if bf16_state:
+            vals = ki.bf16_bits_to_f32(ki.f32_to_bf16_bits(vals))
+        pools[0][s0:s0 + len(sl)] = torch.from_numpy(vals).to(dev).to(state_dtype)
     for r in range(1, R):
         pools[r].copy_(pools[0])
-    pool_live = pools[0][torch.from_numpy(p.slot_idx[p.live_requests()].astype(np.int64)).to(dev)].cpu().numpy()
+    pool_live = pools[0][torch.from_numpy(p.slot_idx[p.live_requests()].astype(np.int64)).to(dev)].float().cpu().numpy()
     set_t = [torch.from_numpy(s).to(dev) for s in sets]
 
     combos = []
@@ -193,14 +199,15 @@ def main():
             combos.append(a)
     T = p.T if p.T is not None else 0
     packed = p.T is None
+    call_flags = kda.KDA_FLAG_STATE_BF16 if bf16_state else 0
     cu_ptr = cu.data_ptr()
 
     def launch(i, stream_handle):
         a = combos[i % len(combos)]
         if packed:
-            st = lib.kda_decode_packed(ctypes.byref(a), cu_ptr, p.tokens, 0, stream_handle)
+            st = lib.kda_decode_packed(ctypes.byref(a), cu_ptr, p.tokens, call_flags, stream_handle)
         else:
-            st = lib.kda_decode_step(ctypes.byref(a), T, 0, stream_handle)
+            st = lib.kda_decode_step(ctypes.byref(a), T, call_flags, stream_handle)
         if st != 0:
             raise kda.KdaError(st, "decode")
 
@@ -280,7 +287,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": p.name, "N": p.N, "T": p.T if p.T is not None else "1..4 packed",
                    "H": p.H, "HV": p.HV, "K": p.K, "V": p.V, "num_slots": p.num_slots,
-                   "norm": p.gate is not None, "cold_slot_sets": len(sets), "cold_pool_copies": R,
+                   "norm": p.gate is not None, "state_dtype": args.state,
+                   "cold_slot_sets": len(sets), "cold_pool_copies": R,
                    "vtile": kda.kda_decode_plan(p.N * p.HV, T or 1, p.gate is not None)},
         "state_GBps": round(state_gbps, 1),
         "state_frac_of_peak": round(state_gbps / HBM_PEAK_GBPS, 4),

@@ -60,6 +60,12 @@ typedef enum kda_status {
     KDA_ERR_LAUNCH = 7        /* the kernel launch failed                            */
 } kda_status;
 
+/* flags: bit 0 selects a bf16 state pool (`state` then points to bf16 bit
+ * patterns; default fp32).  The state is widened exactly to fp32 on load, the
+ * call's tokens are recurred in fp32, and the state is rounded to nearest even
+ * once, when it is written back. */
+#define KDA_FLAG_STATE_BF16 (1u << 0)
+
 /* flags: bits 8..9 force the value-tile width of one workgroup
  * (1 = 32 columns, 2 = 64, 3 = 128; 0 = the library's choice).  Results are
  * bit-identical for every width; the knob exists for tests and tuning. */
@@ -84,9 +90,10 @@ typedef enum kda_status {
  *              t*g_stride + hv*K + i.  16-byte aligned; g_stride a multiple
  *              of 4, >= HV*K
  *   beta       fp32, (t, hv) at t*beta_stride + hv; beta_stride >= HV
- *   state      fp32 pool, (slot, hv, i, j) at slot*slot_stride + (hv*K + i)*V + j
- *              (V contiguous), num_slots slots.  Read and written IN PLACE.
- *              16-byte aligned; slot_stride a multiple of 4, >= HV*K*V
+ *   state      fp32 pool (bf16 with KDA_FLAG_STATE_BF16), (slot, hv, i, j) at
+ *              slot*slot_stride + (hv*K + i)*V + j (V contiguous), num_slots
+ *              slots.  Read and written IN PLACE.  16-byte aligned (8 for
+ *              bf16); slot_stride a multiple of 4, >= HV*K*V
  *   slot_idx   int32 [N]: the pool slot of each request.  A value outside
  *              [0, num_slots) (-1 marks a padding row) skips the request:
  *              no state is read or written and its output rows are left
@@ -114,7 +121,7 @@ typedef struct kda_decode_args {
     const void *v;      int64_t v_stride;
     const float *g;     int64_t g_stride;
     const float *beta;  int64_t beta_stride;
-    float *state;       int64_t num_slots;   int64_t slot_stride;
+    void *state;        int64_t num_slots;   int64_t slot_stride;
     const int32_t *slot_idx;
     void *out;          int64_t out_stride;
     const void *gate;   int64_t gate_stride;

@@ -22,7 +22,7 @@ __all__ = [
     "KdaError", "KdaDecodeArgs", "library", "library_path",
     "kda_decode_step", "kda_decode_packed", "kda_gated_rmsnorm",
     "kda_decode_plan", "kda_status_string", "decode_args",
-    "KDA_FLAG_VTILE",
+    "KDA_FLAG_VTILE", "KDA_FLAG_STATE_BF16",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -32,6 +32,7 @@ KDA_STATUS = {
     0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_ALIGN",
     4: "KDA_ERR_ALIAS", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_DEVICE", 7: "KDA_ERR_LAUNCH",
 }
+KDA_FLAG_STATE_BF16 = 1 << 0
 KDA_FLAG_VTILE_SHIFT = 8
 
 
@@ -131,6 +132,12 @@ def _lead_stride(t: torch.Tensor) -> int:
     return t.stride(0) if t.shape[0] > 1 else inner
 
 
+def _state_flag(state: torch.Tensor, flags: int) -> int:
+    """The state pool's dtype selects the bf16-state flag."""
+    flags = int(flags) & ~KDA_FLAG_STATE_BF16
+    return flags | (KDA_FLAG_STATE_BF16 if state.dtype == torch.bfloat16 else 0)
+
+
 def decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate=None, norm_weight=None,
                 eps: float = 1e-6) -> KdaDecodeArgs:
     """Marshal tensors into a ``kda_decode_args`` struct (no validation of
@@ -140,7 +147,7 @@ def decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate=None, norm_w
     _check(v, "v", torch.bfloat16, 3)
     _check(g, "g", torch.float32, 3)
     _check(beta, "beta", torch.float32, 2)
-    _check(state, "state", torch.float32, 4)
+    _check(state, "state", state.dtype if state.dtype in (torch.float32, torch.bfloat16) else torch.float32, 4)
     _check(slot_idx, "slot_idx", torch.int32, 1)
     _check(out, "out", torch.bfloat16, 3)
     tokens, H, K = q.shape
@@ -179,6 +186,7 @@ def kda_decode_step(q, k, v, g, beta, state, slot_idx, out, *, T: int, scale: fl
     a = decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate, norm_weight, eps)
     if q.shape[0] != a.N * int(T):
         raise ValueError("step call needs N*T token rows")
+    flags = _state_flag(state, flags)
     st = library().kda_decode_step(ctypes.byref(a), int(T), int(flags), _stream(stream))
     if st != 0:
         raise KdaError(st, "kda_decode_step")
@@ -193,6 +201,7 @@ def kda_decode_packed(q, k, v, g, beta, state, slot_idx, cu_seqlens, out, *, sca
     _check(cu_seqlens, "cu_seqlens", torch.int32, 1)
     if cu_seqlens.shape[0] != a.N + 1:
         raise ValueError("cu_seqlens must hold N+1 entries")
+    flags = _state_flag(state, flags)
     st = library().kda_decode_packed(ctypes.byref(a), cu_seqlens.data_ptr(), q.shape[0], int(flags), _stream(stream))
     if st != 0:
         raise KdaError(st, "kda_decode_packed")

@@ -39,6 +39,7 @@
 #include <atomic>
 #include <stdint.h>
 #include <string.h>
+#include <type_traits>
 
 #include "kda.h"
 
@@ -55,7 +56,7 @@ struct DecodeParams {
     const uint16_t *v;
     const float *g;
     const float *beta;
-    float *state;
+    void *state;                 // fp32 or bf16 pool (template parameter BF16S)
     const int32_t *slot_idx;
     const int32_t *cu_seqlens;   // NULL: fixed T tokens per request
     uint16_t *out;
@@ -68,6 +69,7 @@ struct DecodeParams {
 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -91,6 +93,40 @@ __device__ __forceinline__ float silu(float z)
 {
     return z / (1.0f + __expf(-z));
 }
+
+// The lane's 16 rows x 4 columns of a state tile in HBM.  fp32 state moves as
+// one 16-byte vector per row; bf16 state (BF16S) as one 8-byte vector per row,
+// widened exactly to fp32 on load and rounded to nearest even on store.  The
+// math in between is fp32 in both cases.  Both directions are non-temporal:
+// the tile is read once and written once per call.
+template <bool BF16S>
+struct TileIO {
+    using chunk = typename std::conditional<BF16S, u32x2, f32x4>::type;
+    chunk *ptr;
+
+    __device__ __forceinline__ TileIO(void *state, int64_t elem_offset)
+        : ptr(reinterpret_cast<chunk *>(static_cast<char *>(state) + elem_offset * (BF16S ? 2 : 4))) {}
+
+    __device__ __forceinline__ f32x4 load(int row) const
+    {
+        if constexpr (BF16S) {
+            const u32x2 r = __builtin_nontemporal_load(ptr + row * (VD / 4));
+            return f32x4{bf16_lo(r.x), bf16_hi(r.x), bf16_lo(r.y), bf16_hi(r.y)};
+        } else {
+            return __builtin_nontemporal_load(ptr + row * (VD / 4));
+        }
+    }
+
+    __device__ __forceinline__ void store(int row, f32x4 v) const
+    {
+        if constexpr (BF16S) {
+            const u32x2 r = {pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+            __builtin_nontemporal_store(r, ptr + row * (VD / 4));
+        } else {
+            __builtin_nontemporal_store(v, ptr + row * (VD / 4));
+        }
+    }
+};
 
 // DPP lane moves (gfx9 DPP controls).
 #define KDA_DPP(x, ctrl)                                                                                   \
@@ -392,7 +428,7 @@ __device__ __forceinline__ void read_staged(TokenIn &in, const uint4 (&k)[KD / 8
 //     memory.  Fastest for packed batches of mixed lengths.
 constexpr int BODY_LOOP = 0, BODY_PEELED = 1, BODY_STAGED = 2;
 
-template <int NW, bool NORM, int BODY>
+template <int NW, bool NORM, int BODY, bool BF16S>
 __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(DecodeParams p)
 {
     static_assert(NW == 1 || NW == 2 || NW == 4, "a workgroup is 1, 2 or 4 waves");
@@ -430,8 +466,7 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(DecodeParams p)
 
     // The tile is streamed: read once, written once, no reuse in this call,
     // so both directions use non-temporal accesses.
-    f32x4 *tile = reinterpret_cast<f32x4 *>(p.state + slot * p.slot_stride + (int64_t)hv * (KD * VD) +
-                                            (int64_t)row0 * VD + col);
+    const TileIO<BF16S> tile(p.state, slot * p.slot_stride + (int64_t)hv * (KD * VD) + (int64_t)row0 * VD + col);
     f32x4 s[ROWS_PER_LANE];
     TokenIn in;
     __shared__ float norm_partial[2][4];
@@ -441,20 +476,20 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(DecodeParams p)
         load_token(in, p, bos, h, hv, row0, col);
 #pragma unroll
         for (int i = 0; i < ROWS_PER_LANE; ++i)
-            s[i] = __builtin_nontemporal_load(tile + i * (VD / 4));
+            s[i] = tile.load(i);
         for (int64_t t = bos; t < eos; ++t)
             advance_token<NORM, true>(s, in, p, t, eos, h, hv, lane, wave, rg, row0, col, norm_partial);
     } else if constexpr (BODY == BODY_PEELED) {
         constexpr int FIRST_ROWS = 4;
 #pragma unroll
         for (int i = 0; i < FIRST_ROWS; ++i)
-            s[i] = __builtin_nontemporal_load(tile + i * (VD / 4));
+            s[i] = tile.load(i);
         __builtin_amdgcn_sched_barrier(0);
         load_token(in, p, bos, h, hv, row0, col);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = FIRST_ROWS; i < ROWS_PER_LANE; ++i)
-            s[i] = __builtin_nontemporal_load(tile + i * (VD / 4));
+            s[i] = tile.load(i);
         // all 16 loads of the tile are in flight before any math starts
         __builtin_amdgcn_sched_barrier(0);
         advance_token<NORM, false>(s, in, p, bos, eos, h, hv, lane, wave, rg, row0, col, norm_partial);
@@ -471,7 +506,7 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(DecodeParams p)
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < ROWS_PER_LANE; ++i)
-            s[i] = __builtin_nontemporal_load(tile + i * (VD / 4));
+            s[i] = tile.load(i);
         __builtin_amdgcn_sched_barrier(0);
         stage_store<NW>(st, pieces, nt);   // waits for the inputs only, not the tile
         for (int64_t t0 = bos; t0 < eos; t0 += STAGE_TOKENS) {
@@ -497,7 +532,7 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(DecodeParams p)
         __syncthreads();
 #pragma unroll
     for (int i = 0; i < ROWS_PER_LANE; ++i)
-        __builtin_nontemporal_store(s[i], tile + i * (VD / 4));
+        tile.store(i, s[i]);
 }
 
 // Standalone gated RMSNorm: one wave per row, 4 rows per workgroup.
@@ -594,8 +629,9 @@ int vtile_from_flags(uint32_t flags)
 
 kda_status validate(const kda_decode_args *a, int64_t tokens, const int32_t *cu_seqlens, uint32_t flags)
 {
-    if (flags & ~KDA_FLAG_VTILE_MASK)
+    if (flags & ~(KDA_FLAG_VTILE_MASK | KDA_FLAG_STATE_BF16))
         return KDA_ERR_UNSUPPORTED;
+    const int64_t state_elem = (flags & KDA_FLAG_STATE_BF16) ? 2 : 4;
     if (a->N < 0 || a->H < 1 || a->HV < 1 || a->HV % a->H != 0 || tokens < 0)
         return KDA_ERR_SHAPE;
     if (a->K != KD || a->V != VD)
@@ -619,14 +655,14 @@ kda_status validate(const kda_decode_args *a, int64_t tokens, const int32_t *cu_
         return KDA_ERR_SHAPE;
     if (!aligned(a->q, 16) || !aligned(a->k, 16) || a->q_stride % 8 || a->k_stride % 8 ||
         !aligned(a->v, 8) || a->v_stride % 4 || !aligned(a->g, 16) || a->g_stride % 4 ||
-        !aligned(a->beta, 4) || !aligned(a->state, 16) || a->slot_stride % 4 ||
+        !aligned(a->beta, 4) || !aligned(a->state, 4 * state_elem) || a->slot_stride % 4 ||
         !aligned(a->out, 8) || a->out_stride % 4 || !aligned(a->slot_idx, 4) ||
         (cu_seqlens && !aligned(cu_seqlens, 4)) ||
         (a->gate && (!aligned(a->gate, 8) || a->gate_stride % 4 || !aligned(a->norm_weight, 8))))
         return KDA_ERR_ALIGN;
 
     const ByteRange out = span(a->out, tokens, a->out_stride, hvv, 2);
-    const ByteRange state = span(a->state, a->num_slots, a->slot_stride, hvk * a->V, 4);
+    const ByteRange state = span(a->state, a->num_slots, a->slot_stride, hvk * a->V, state_elem);
     const ByteRange inputs[] = {
         span(a->q, tokens, a->q_stride, hk, 2),
         span(a->k, tokens, a->k_stride, hk, 2),
@@ -664,18 +700,31 @@ int32_t plan_vtile(int64_t units, int32_t T, bool norm)
     return 128;
 }
 
-template <int NW, bool NORM>
+template <int NW, bool NORM, bool BF16S>
 kda_status launch_decode(const DecodeParams &p, int64_t units, int body, hipStream_t stream)
 {
     const int64_t blocks = units * (4 / NW);
     if (blocks > 0x7FFFFFFF)
         return KDA_ERR_SHAPE;
     void *args[] = {const_cast<DecodeParams *>(&p)};
-    const void *fn = body == BODY_STAGED   ? reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_STAGED>)
-                     : body == BODY_PEELED ? reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_PEELED>)
-                                           : reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_LOOP>);
+    const void *fn =
+        body == BODY_STAGED   ? reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_STAGED, BF16S>)
+        : body == BODY_PEELED ? reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_PEELED, BF16S>)
+                              : reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_LOOP, BF16S>);
     const hipError_t e = hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(64 * NW), args, 0, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+template <bool BF16S>
+kda_status dispatch_width(const DecodeParams &p, int64_t units, int body, bool norm, int vtile, hipStream_t s)
+{
+    if (norm)
+        return launch_decode<4, true, BF16S>(p, units, body, s);
+    switch (vtile) {
+    case 32: return launch_decode<1, false, BF16S>(p, units, body, s);
+    case 64: return launch_decode<2, false, BF16S>(p, units, body, s);
+    default: return launch_decode<4, false, BF16S>(p, units, body, s);
+    }
 }
 
 kda_status run_decode(const kda_decode_args *a, int32_t T, const int32_t *cu_seqlens, int64_t tokens,
@@ -732,13 +781,9 @@ kda_status run_decode(const kda_decode_args *a, int32_t T, const int32_t *cu_seq
     // the prefetching loop (all measured on MI355X, cold caches)
     const int body = cu_seqlens != nullptr ? BODY_STAGED
                      : (T > 1 || units < 256) ? BODY_PEELED : BODY_LOOP;
-    if (norm)
-        return launch_decode<4, true>(p, units, body, s);
-    switch (vtile) {
-    case 32: return launch_decode<1, false>(p, units, body, s);
-    case 64: return launch_decode<2, false>(p, units, body, s);
-    default: return launch_decode<4, false>(p, units, body, s);
-    }
+    if (flags & KDA_FLAG_STATE_BF16)
+        return dispatch_width<true>(p, units, body, norm, vtile, s);
+    return dispatch_width<false>(p, units, body, norm, vtile, s);
 }
 
 }  // namespace

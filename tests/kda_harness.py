@@ -14,7 +14,11 @@ stated bar would let through, such as a 1% scale error on outputs near 0.05):
                 (relative 1e-4, with an absolute floor for entries that
                 cancel to ~0; the state's scale is ~0.05)
   state, strict |S_gpu - S_ref| <= 2e-6 max|S_ref| per (slot, head) tile
-where y_ref and S_ref are the oracle's double-precision values.
+With a bf16 state pool the stored state carries one bf16 rounding:
+  state, stated |S_gpu - S_ref| <= 2^-8 |S_ref| + 1e-6   (half a bf16 ulp)
+  state, strict |S_gpu - S_ref| <= ulp_bf16(S_ref) + 2e-6 max|S_ref| per tile
+where y_ref and S_ref are the oracle's double-precision values (the oracle
+starts from the bf16 state widened exactly).
 """
 from __future__ import annotations
 
@@ -61,17 +65,24 @@ class DeviceProblem:
     live_slots: np.ndarray        # the pool slots of live requests, in request order
 
 
-def upload(p: ki.Problem, background_seed: int = 1234) -> DeviceProblem:
+def upload(p: ki.Problem, background_seed: int = 1234, state_dtype=torch.float32) -> DeviceProblem:
     """Inputs to the GPU.  The pool is filled with a seeded N(0, 0.05)
     background generated on the device (these slots are only checked for
-    being left alone) and the live slots get the generator's values."""
+    being left alone) and the live slots get the generator's values (rounded
+    to bf16 for a bf16 pool)."""
     live = p.live_requests()
     live_slots = p.slot_idx[live].astype(np.int64)
     gen = torch.Generator(device=DEV)
     gen.manual_seed(background_seed)
-    state = torch.randn((p.num_slots, p.HV, p.K, p.V), generator=gen, device=DEV, dtype=torch.float32) * 0.05
+    state = (torch.randn((p.num_slots, p.HV, p.K, p.V), generator=gen, device=DEV, dtype=torch.float32) * 0.05
+             ).to(state_dtype)
     if len(live_slots):
-        state[torch.from_numpy(live_slots).to(DEV)] = f32_tensor(p.state_slots(live_slots))
+        vals = p.state_slots(live_slots)
+        if state_dtype == torch.bfloat16:
+            live_t = bf16_tensor(ki.f32_to_bf16_bits(vals))
+        else:
+            live_t = f32_tensor(vals)
+        state[torch.from_numpy(live_slots).to(DEV)] = live_t
     out = torch.empty((p.tokens, p.HV, p.V), device=DEV, dtype=torch.int16).fill_(
         np.int16(np.uint16(SENTINEL_BITS).view(np.int16))).view(torch.bfloat16)
     return DeviceProblem(
@@ -95,13 +106,16 @@ def run_gpu(d: DeviceProblem, packed: bool | None = None, flags: int = 0, stream
         kda.kda_decode_step(d.q, d.k, d.v, d.g, d.beta, d.state, d.slot_idx, d.out, T=p.T, **kw)
 
 
-def run_oracle(p: ki.Problem):
+def run_oracle(p: ki.Problem, state_bf16: bool = False):
     """Oracle over the live requests only, on a compact double pool holding
     just their slots.  Returns (out [tokens, HV, V] with NaN on skipped rows,
     final state [n_live, HV, K, V] in request order)."""
     live = p.live_requests()
     slots = p.slot_idx[live].astype(np.int64)
-    pool = p.state_slots(slots).astype(np.float64)
+    pool = p.state_slots(slots)
+    if state_bf16:
+        pool = ki.bf16_bits_to_f32(ki.f32_to_bf16_bits(pool))
+    pool = pool.astype(np.float64)
     remap = np.full(p.N, -1, dtype=np.int32)
     remap[live] = np.arange(len(live), dtype=np.int32)
     kw = {}
@@ -146,25 +160,35 @@ def compare(d: DeviceProblem, ref_out: np.ndarray, ref_state: np.ndarray, strict
         bad = err > bf16_ulp(r) + floor
         assert not bad.any(), f"output beyond 1 bf16 ulp: {err[bad][:5]} at ref {r[bad][:5]}"
 
-    S = d.state[torch.from_numpy(d.live_slots).to(DEV)].cpu().numpy().astype(np.float64) if len(d.live_slots) \
-        else np.zeros((0, p.HV, p.K, p.V))
+    bf16_state = d.state.dtype == torch.bfloat16
+    if len(d.live_slots):
+        S_t = d.state[torch.from_numpy(d.live_slots).to(DEV)]
+        S = bf16_to_f64(S_t) if bf16_state else S_t.cpu().numpy().astype(np.float64)
+    else:
+        S = np.zeros((0, p.HV, p.K, p.V))
     serr = np.abs(S - ref_state)
-    assert np.all(serr <= 1e-4 * np.abs(ref_state) + 1e-6), f"state outside the stated tolerance: max {serr.max()}"
     tile_max = np.abs(ref_state).max(axis=(2, 3), keepdims=True) if S.size else np.ones(1)
     rel_tile = (serr / tile_max).max() if S.size else 0.0
-    if strict:
-        assert rel_tile <= 2e-6, f"state error {rel_tile} of the tile scale"
+    if bf16_state:
+        assert np.all(serr <= 2.0 ** -8 * np.abs(ref_state) + 1e-6), \
+            f"bf16 state outside the stated tolerance: max {serr.max()}"
+        if strict and S.size:
+            assert np.all(serr <= bf16_ulp(ref_state) + 2e-6 * tile_max), "bf16 state beyond one ulp"
+    else:
+        assert np.all(serr <= 1e-4 * np.abs(ref_state) + 1e-6), f"state outside the stated tolerance: max {serr.max()}"
+        if strict:
+            assert rel_tile <= 2e-6, f"state error {rel_tile} of the tile scale"
     ulps = (err / bf16_ulp(r)).max() if r.size else 0.0
     return Report(float(err.max()) if err.size else 0.0, float(ulps), float(rel_tile),
                   float(serr.max()) if serr.size else 0.0)
 
 
-def parity(p: ki.Problem, packed: bool | None = None, flags: int = 0) -> Report:
-    d = upload(p)
+def parity(p: ki.Problem, packed: bool | None = None, flags: int = 0, state_dtype=torch.float32) -> Report:
+    d = upload(p, state_dtype=state_dtype)
     before = d.state.clone()
     run_gpu(d, packed=packed, flags=flags)
     torch.cuda.synchronize()
-    ref_out, ref_state = run_oracle(p)
+    ref_out, ref_state = run_oracle(p, state_bf16=state_dtype == torch.bfloat16)
     rep = compare(d, ref_out, ref_state)
     # every slot no live request owns is bit-for-bit untouched
     untouched = torch.ones(p.num_slots, dtype=torch.bool, device=DEV)

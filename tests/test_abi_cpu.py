@@ -137,6 +137,18 @@ def test_alignment():
         assert _step(a) == ALIGN, field
 
 
+def test_bf16_state_flag():
+    a, _ = _valid_args()
+    a.state += 8                                   # 8-byte aligned: enough for bf16 rows only
+    assert _step(a) == ALIGN
+    assert _step(a, flags=kda.KDA_FLAG_STATE_BF16) == DEVICE
+    a, _ = _valid_args()
+    # a bf16 pool is half as long: out may start right after it
+    a.out = a.state + 8 * 4 * 128 * 128 * 2
+    assert _step(a) == ALIAS
+    assert _step(a, flags=kda.KDA_FLAG_STATE_BF16) == DEVICE
+
+
 def test_aliasing():
     a, _ = _valid_args()
     a.out = a.q + 256                              # out inside q
@@ -163,7 +175,9 @@ def test_aliasing():
 
 def test_unknown_flags():
     a, _ = _valid_args()
-    assert _step(a, flags=1) == UNSUP
+    assert _step(a, flags=2) == UNSUP
+    a, _ = _valid_args()
+    assert _step(a, flags=1 << 12) == UNSUP
     a, _ = _valid_args()
     a.gate, a.gate_stride, a.norm_weight = BASE + 40 * (1 << 26), 4 * 128, BASE + 41 * (1 << 26)
     assert _step(a, flags=kda.KDA_FLAG_VTILE(32)) == UNSUP      # the norm needs 128 columns

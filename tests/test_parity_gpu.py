@@ -83,6 +83,33 @@ def test_packed_and_step_bodies_bit_identical():
         assert torch.equal(a.out.view(torch.int16), b.out.view(torch.int16)), name
 
 
+# ------------------------------------------------------- bf16 state pool
+@pytest.mark.parametrize("name", ["n1_t1_h8", "n32_t1_h8", "n8_t4_h8", "n32_t1_h16_norm", "packed_n256_h12"])
+def test_bf16_state_workloads(name):
+    p = ki.workload(name)
+    _log(f"{name} bf16 state", parity(p, state_dtype=torch.bfloat16))
+
+
+@pytest.mark.parametrize("case", SMALL[1:4])
+def test_bf16_state_small_cases(case):
+    N, H, HV, T, slots, n_pad, norm = case
+    p = ki.make_problem("small", 177 + N, N=N, H=H, HV=HV, K=128, V=128, num_slots=slots, T=T,
+                        n_pad=n_pad, norm=norm)
+    parity(p, state_dtype=torch.bfloat16)
+
+
+def test_bf16_state_tile_widths_bit_identical():
+    p = ki.workload("n32_t1_h8")
+    results = []
+    for width in (32, 64, 128):
+        d = upload(p, state_dtype=torch.bfloat16)
+        run_gpu(d, flags=kda.KDA_FLAG_VTILE(width))
+        torch.cuda.synchronize()
+        results.append((d.out.view(torch.int16).clone(), d.state.view(torch.int16).clone()))
+    for o, s_ in results[1:]:
+        assert torch.equal(o, results[0][0]) and torch.equal(s_, results[0][1])
+
+
 # ------------------------------------------------------- edge cases
 def test_all_requests_padding():
     p = ki.make_problem("allpad", 5, N=4, H=2, HV=2, K=128, V=128, num_slots=6, T=None, n_pad=4)
