@@ -428,8 +428,14 @@ __device__ __forceinline__ void read_staged(TokenIn &in, const uint4 (&k)[KD / 8
 //     memory.  Fastest for packed batches of mixed lengths.
 constexpr int BODY_LOOP = 0, BODY_PEELED = 1, BODY_STAGED = 2;
 
+// The scalars on the critical path (slot lookup -> tile address) come first
+// as separate arguments: the library is built with kernarg preloading, so
+// they arrive in SGPRs at wave launch and the slot index load issues without
+// waiting for a kernel-argument fetch.  The rest travels in DecodeParams.
 template <int NW, bool NORM, int BODY, bool BF16S>
-__global__ __launch_bounds__(64 * NW) void kda_decode_kernel(DecodeParams p)
+__global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot_idx, const int32_t *cu_seqlens,
+                                                             void *state, int64_t slot_stride, int64_t num_slots,
+                                                             int32_t HV, int32_t T, DecodeParams p)
 {
     static_assert(NW == 1 || NW == 2 || NW == 4, "a workgroup is 1, 2 or 4 waves");
     static_assert(!NORM || NW == 4, "the norm epilogue needs all 128 columns in one workgroup");
@@ -440,20 +446,20 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(DecodeParams p)
     const int64_t block = blockIdx.x;
     const int vt = (int)(block % NVT);
     const int64_t unit = block / NVT;
-    const int64_t req = unit / p.HV;
-    const int hv = (int)(unit - req * p.HV);
+    const int64_t req = unit / HV;
+    const int hv = (int)(unit - req * HV);
 
     // slot gather: padding rows and slots outside the pool are skipped
-    const int64_t slot = p.slot_idx[req];
-    if (slot < 0 || slot >= p.num_slots)
+    const int64_t slot = slot_idx[req];
+    if (slot < 0 || slot >= num_slots)
         return;
     int64_t bos, eos;
-    if (p.cu_seqlens) {
-        bos = p.cu_seqlens[req];
-        eos = p.cu_seqlens[req + 1];
+    if (cu_seqlens) {
+        bos = cu_seqlens[req];
+        eos = cu_seqlens[req + 1];
     } else {
-        bos = req * p.T;
-        eos = bos + p.T;
+        bos = req * T;
+        eos = bos + T;
     }
     if (eos <= bos)
         return;
@@ -466,7 +472,7 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(DecodeParams p)
 
     // The tile is streamed: read once, written once, no reuse in this call,
     // so both directions use non-temporal accesses.
-    const TileIO<BF16S> tile(p.state, slot * p.slot_stride + (int64_t)hv * (KD * VD) + (int64_t)row0 * VD + col);
+    const TileIO<BF16S> tile(state, slot * slot_stride + (int64_t)hv * (KD * VD) + (int64_t)row0 * VD + col);
     f32x4 s[ROWS_PER_LANE];
     TokenIn in;
     __shared__ float norm_partial[2][4];
@@ -706,7 +712,12 @@ kda_status launch_decode(const DecodeParams &p, int64_t units, int body, hipStre
     const int64_t blocks = units * (4 / NW);
     if (blocks > 0x7FFFFFFF)
         return KDA_ERR_SHAPE;
-    void *args[] = {const_cast<DecodeParams *>(&p)};
+    const int32_t *slot_idx = p.slot_idx, *cu_seqlens = p.cu_seqlens;
+    void *state = p.state;
+    int64_t slot_stride = p.slot_stride, num_slots = p.num_slots;
+    int32_t HV = p.HV, T = p.T;
+    void *args[] = {&slot_idx, &cu_seqlens, &state, &slot_stride, &num_slots, &HV, &T,
+                    const_cast<DecodeParams *>(&p)};
     const void *fn =
         body == BODY_STAGED   ? reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_STAGED, BF16S>)
         : body == BODY_PEELED ? reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_PEELED, BF16S>)
