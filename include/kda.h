@@ -31,9 +31,9 @@
  * Conventions for every entry point.
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
  *     library allocates nothing, never synchronises and never copies to or
- *     from the host.  Each call enqueues one kernel on `stream` (a
- *     hipStream_t; NULL = the default stream) and returns; it can be
- *     captured into a HIP graph.
+ *     from the host.  Each call enqueues one kernel on `stream` (two with
+ *     KDA_FLAG_VALIDATE; a hipStream_t, NULL = the default stream) and
+ *     returns; it can be captured into a HIP graph.
  *   - Arguments are validated on the host in O(1) before anything is
  *     launched.  On any error status nothing was launched and no buffer was
  *     touched.  KDA_ERR_LAUNCH reports a failed launch.
@@ -65,6 +65,19 @@ typedef enum kda_status {
  * call's tokens are recurred in fp32, and the state is rounded to nearest even
  * once, when it is written back. */
 #define KDA_FLAG_STATE_BF16 (1u << 0)
+
+/* flags: bit 1 validates the device metadata before the decode, all or
+ * nothing.  A one-workgroup check runs first on the call's stream and writes
+ * `device_status`: KDA_DEVICE_OK, or the lowest-numbered KDA_DEVICE_ERR_* it
+ * found.  The decode then runs only if the word is KDA_DEVICE_OK; otherwise
+ * no state, output or other buffer is touched.  Costs one extra launch; the
+ * duplicate check is O(N^2 / 1024) per call.  Without this flag the metadata
+ * is trusted (slots outside the pool are skipped). */
+#define KDA_FLAG_VALIDATE (1u << 1)
+#define KDA_DEVICE_OK 0
+#define KDA_DEVICE_ERR_SLOT_RANGE 1   /* a slot index outside [0, num_slots) other than -1 */
+#define KDA_DEVICE_ERR_SLOT_DUP 2     /* two live requests share one slot */
+#define KDA_DEVICE_ERR_CU_SEQLENS 3   /* cu_seqlens negative, decreasing, or past total_tokens */
 
 /* flags: bits 8..9 force the value-tile width of one workgroup
  * (1 = 32 columns, 2 = 64, 3 = 128; 0 = the library's choice).  Results are
@@ -108,6 +121,9 @@ typedef enum kda_status {
  *   norm_weight bf16 [V] (8-byte aligned), norm_eps > 0 or 0:
  *              out = o / sqrt(mean_j o^2 + eps) * w * silu(z).
  *
+ *   device_status  with KDA_FLAG_VALIDATE, a device int32 the call writes
+ *              (4-byte aligned, overlapping no other buffer); else ignored.
+ *
  * Aliasing: out and state may not overlap each other, or any input
  * (q, k, v, g, beta, slot_idx, cu_seqlens, gate, norm_weight); inputs may
  * overlap each other (q, k, v are often views of one projection).  Ranges are
@@ -127,6 +143,7 @@ typedef struct kda_decode_args {
     const void *gate;   int64_t gate_stride;
     const void *norm_weight;
     float norm_eps;
+    int32_t *device_status;   /* KDA_FLAG_VALIDATE only: caller-owned device int32 */
 } kda_decode_args;
 
 /*

@@ -22,7 +22,7 @@ __all__ = [
     "KdaError", "KdaDecodeArgs", "library", "library_path",
     "kda_decode_step", "kda_decode_packed", "kda_gated_rmsnorm",
     "kda_decode_plan", "kda_status_string", "decode_args",
-    "KDA_FLAG_VTILE", "KDA_FLAG_STATE_BF16",
+    "KDA_FLAG_VTILE", "KDA_FLAG_STATE_BF16", "KDA_FLAG_VALIDATE", "KDA_DEVICE_STATUS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -33,6 +33,9 @@ KDA_STATUS = {
     4: "KDA_ERR_ALIAS", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_DEVICE", 7: "KDA_ERR_LAUNCH",
 }
 KDA_FLAG_STATE_BF16 = 1 << 0
+KDA_FLAG_VALIDATE = 1 << 1
+KDA_DEVICE_STATUS = {0: "KDA_DEVICE_OK", 1: "KDA_DEVICE_ERR_SLOT_RANGE", 2: "KDA_DEVICE_ERR_SLOT_DUP",
+                     3: "KDA_DEVICE_ERR_CU_SEQLENS"}
 KDA_FLAG_VTILE_SHIFT = 8
 
 
@@ -65,6 +68,7 @@ class KdaDecodeArgs(ctypes.Structure):
         ("gate", ctypes.c_void_p), ("gate_stride", ctypes.c_int64),
         ("norm_weight", ctypes.c_void_p),
         ("norm_eps", ctypes.c_float),
+        ("device_status", ctypes.c_void_p),
     ]
 
 
@@ -139,7 +143,7 @@ def _state_flag(state: torch.Tensor, flags: int) -> int:
 
 
 def decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate=None, norm_weight=None,
-                eps: float = 1e-6) -> KdaDecodeArgs:
+                eps: float = 1e-6, device_status=None) -> KdaDecodeArgs:
     """Marshal tensors into a ``kda_decode_args`` struct (no validation of
     values; the library validates sizes, alignment and overlap)."""
     _check(q, "q", torch.bfloat16, 3)
@@ -176,14 +180,22 @@ def decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate=None, norm_w
         a.gate, a.gate_stride = gate.data_ptr(), _lead_stride(gate)
         a.norm_weight = norm_weight.data_ptr()
     a.norm_eps = float(eps)
+    if device_status is not None:
+        _check(device_status, "device_status", torch.int32, 1)
+        a.device_status = device_status.data_ptr()
     return a
 
 
 def kda_decode_step(q, k, v, g, beta, state, slot_idx, out, *, T: int, scale: float,
-                    gate=None, norm_weight=None, eps: float = 1e-6, flags: int = 0, stream=None):
+                    gate=None, norm_weight=None, eps: float = 1e-6, flags: int = 0, stream=None,
+                    device_status=None):
     """Decode T tokens for each of N requests (tokens request-major, N*T rows);
-    updates ``state`` in place and writes ``out`` for live requests."""
-    a = decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate, norm_weight, eps)
+    updates ``state`` in place and writes ``out`` for live requests.  With
+    ``device_status`` (an int32 device tensor of one element) the device
+    metadata is validated first, all or nothing (KDA_FLAG_VALIDATE)."""
+    a = decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate, norm_weight, eps, device_status)
+    if device_status is not None:
+        flags = int(flags) | KDA_FLAG_VALIDATE
     if q.shape[0] != a.N * int(T):
         raise ValueError("step call needs N*T token rows")
     flags = _state_flag(state, flags)
@@ -194,10 +206,14 @@ def kda_decode_step(q, k, v, g, beta, state, slot_idx, out, *, T: int, scale: fl
 
 
 def kda_decode_packed(q, k, v, g, beta, state, slot_idx, cu_seqlens, out, *, scale: float,
-                      gate=None, norm_weight=None, eps: float = 1e-6, flags: int = 0, stream=None):
+                      gate=None, norm_weight=None, eps: float = 1e-6, flags: int = 0, stream=None,
+                      device_status=None):
     """Packed variable-length decode: request n owns token rows
-    cu_seqlens[n] .. cu_seqlens[n+1]-1."""
-    a = decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate, norm_weight, eps)
+    cu_seqlens[n] .. cu_seqlens[n+1]-1.  ``device_status`` as for
+    kda_decode_step."""
+    a = decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate, norm_weight, eps, device_status)
+    if device_status is not None:
+        flags = int(flags) | KDA_FLAG_VALIDATE
     _check(cu_seqlens, "cu_seqlens", torch.int32, 1)
     if cu_seqlens.shape[0] != a.N + 1:
         raise ValueError("cu_seqlens must hold N+1 entries")

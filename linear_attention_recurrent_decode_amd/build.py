@@ -25,9 +25,9 @@ HIPCC_FLAGS = [
     # every fused multiply-add in the kernels is an explicit fmaf: no implicit
     # contraction, so inlined copies of the same code round the same way
     "-ffp-contract=off",
-    # the decode kernel's seven leading scalar arguments arrive in SGPRs at
+    # the decode kernel's eight leading scalar arguments arrive in SGPRs at
     # wave launch (gfx950 kernel-argument preloading)
-    "-mllvm", "-amdgpu-kernarg-preload-count=7",
+    "-mllvm", "-amdgpu-kernarg-preload-count=8",
     # no packed-fp32 instructions: scalar fp32 code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

@@ -66,6 +66,7 @@ struct DecodeParams {
     int64_t num_slots, slot_stride;
     int32_t HV, heads_per_qk, T;
     float scale, eps;
+    int32_t *status;             // KDA_FLAG_VALIDATE: the metadata check's verdict
 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -428,14 +429,16 @@ __device__ __forceinline__ void read_staged(TokenIn &in, const uint4 (&k)[KD / 8
 //     memory.  Fastest for packed batches of mixed lengths.
 constexpr int BODY_LOOP = 0, BODY_PEELED = 1, BODY_STAGED = 2;
 
-// The scalars on the critical path (slot lookup -> tile address) come first
-// as separate arguments: the library is built with kernarg preloading, so
-// they arrive in SGPRs at wave launch and the slot index load issues without
-// waiting for a kernel-argument fetch.  The rest travels in DecodeParams.
+// The scalars on the critical path (slot lookup -> tile address, and the
+// validation verdict) come first as separate arguments: the library is built
+// with kernarg preloading, so they arrive in SGPRs at wave launch and the slot
+// index load issues without waiting for a kernel-argument fetch.  The rest
+// travels in DecodeParams.
 template <int NW, bool NORM, int BODY, bool BF16S>
 __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot_idx, const int32_t *cu_seqlens,
                                                              void *state, int64_t slot_stride, int64_t num_slots,
-                                                             int32_t HV, int32_t T, DecodeParams p)
+                                                             int32_t HV, int32_t T, const int32_t *status,
+                                                             DecodeParams p)
 {
     static_assert(NW == 1 || NW == 2 || NW == 4, "a workgroup is 1, 2 or 4 waves");
     static_assert(!NORM || NW == 4, "the norm epilogue needs all 128 columns in one workgroup");
@@ -449,8 +452,11 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot
     const int64_t req = unit / HV;
     const int hv = (int)(unit - req * HV);
 
-    // slot gather: padding rows and slots outside the pool are skipped
+    // slot gather: padding rows and slots outside the pool are skipped; with
+    // validation, every block stops here unless the metadata check passed
     const int64_t slot = slot_idx[req];
+    if (status && *status != KDA_DEVICE_OK)
+        return;
     if (slot < 0 || slot >= num_slots)
         return;
     int64_t bos, eos;
@@ -539,6 +545,55 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot
 #pragma unroll
     for (int i = 0; i < ROWS_PER_LANE; ++i)
         tile.store(i, s[i]);
+}
+
+// Metadata check for KDA_FLAG_VALIDATE: one workgroup, lowest error code wins.
+constexpr int VALIDATE_THREADS = 1024;
+constexpr int VALIDATE_LDS_SLOTS = 8192;
+
+__global__ __launch_bounds__(VALIDATE_THREADS) void kda_validate_kernel(const int32_t *slot_idx,
+                                                                       const int32_t *cu_seqlens, int32_t N,
+                                                                       int64_t num_slots, int64_t total_tokens,
+                                                                       int32_t *status)
+{
+    __shared__ int32_t slots[VALIDATE_LDS_SLOTS];
+    __shared__ int32_t verdict;
+    const int tid = threadIdx.x;
+    const bool in_lds = N <= VALIDATE_LDS_SLOTS;
+    if (tid == 0)
+        verdict = 0x7FFFFFFF;
+    if (in_lds)
+        for (int i = tid; i < N; i += VALIDATE_THREADS)
+            slots[i] = slot_idx[i];
+    __syncthreads();
+    int32_t found = 0x7FFFFFFF;
+    for (int i = tid; i < N; i += VALIDATE_THREADS) {
+        const int32_t s = in_lds ? slots[i] : slot_idx[i];
+        if (s == -1)
+            continue;
+        if (s < 0 || (int64_t)s >= num_slots) {
+            found = min(found, KDA_DEVICE_ERR_SLOT_RANGE);
+            continue;
+        }
+        for (int j = i + 1; j < N; ++j) {
+            if ((in_lds ? slots[j] : slot_idx[j]) == s) {
+                found = min(found, KDA_DEVICE_ERR_SLOT_DUP);
+                break;
+            }
+        }
+    }
+    if (cu_seqlens) {
+        for (int i = tid; i <= N; i += VALIDATE_THREADS) {
+            const int32_t c = cu_seqlens[i];
+            const bool bad = (i == 0 ? c < 0 : cu_seqlens[i - 1] > c) || (int64_t)c > total_tokens;
+            if (bad)
+                found = min(found, KDA_DEVICE_ERR_CU_SEQLENS);
+        }
+    }
+    atomicMin(&verdict, found);
+    __syncthreads();
+    if (tid == 0)
+        *status = verdict == 0x7FFFFFFF ? KDA_DEVICE_OK : verdict;
 }
 
 // Standalone gated RMSNorm: one wave per row, 4 rows per workgroup.
@@ -635,7 +690,7 @@ int vtile_from_flags(uint32_t flags)
 
 kda_status validate(const kda_decode_args *a, int64_t tokens, const int32_t *cu_seqlens, uint32_t flags)
 {
-    if (flags & ~(KDA_FLAG_VTILE_MASK | KDA_FLAG_STATE_BF16))
+    if (flags & ~(KDA_FLAG_VTILE_MASK | KDA_FLAG_STATE_BF16 | KDA_FLAG_VALIDATE))
         return KDA_ERR_UNSUPPORTED;
     const int64_t state_elem = (flags & KDA_FLAG_STATE_BF16) ? 2 : 4;
     if (a->N < 0 || a->H < 1 || a->HV < 1 || a->HV % a->H != 0 || tokens < 0)
@@ -685,6 +740,18 @@ kda_status validate(const kda_decode_args *a, int64_t tokens, const int32_t *cu_
     for (const ByteRange &in : inputs)
         if (overlaps(out, in) || overlaps(state, in))
             return KDA_ERR_ALIAS;
+    if (flags & KDA_FLAG_VALIDATE) {
+        if (!a->device_status)
+            return KDA_ERR_NULL;
+        if (!aligned(a->device_status, 4))
+            return KDA_ERR_ALIGN;
+        const ByteRange st = span(a->device_status, 1, 0, 1, 4);
+        if (overlaps(st, out) || overlaps(st, state))
+            return KDA_ERR_ALIAS;
+        for (const ByteRange &in : inputs)
+            if (overlaps(st, in))
+                return KDA_ERR_ALIAS;
+    }
     return KDA_OK;
 }
 
@@ -716,7 +783,8 @@ kda_status launch_decode(const DecodeParams &p, int64_t units, int body, hipStre
     void *state = p.state;
     int64_t slot_stride = p.slot_stride, num_slots = p.num_slots;
     int32_t HV = p.HV, T = p.T;
-    void *args[] = {&slot_idx, &cu_seqlens, &state, &slot_stride, &num_slots, &HV, &T,
+    const int32_t *status = p.status;
+    void *args[] = {&slot_idx, &cu_seqlens, &state, &slot_stride, &num_slots, &HV, &T, &status,
                     const_cast<DecodeParams *>(&p)};
     const void *fn =
         body == BODY_STAGED   ? reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_STAGED, BF16S>)
@@ -785,8 +853,20 @@ kda_status run_decode(const kda_decode_args *a, int32_t T, const int32_t *cu_seq
     p.T = T;
     p.scale = a->scale;
     p.eps = a->norm_eps;
+    p.status = nullptr;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (flags & KDA_FLAG_VALIDATE) {
+        p.status = a->device_status;
+        const int32_t *slots = a->slot_idx;
+        int32_t n = a->N;
+        int64_t num_slots = a->num_slots;
+        int32_t *status = a->device_status;
+        void *vargs[] = {&slots, &cu_seqlens, &n, &num_slots, &tokens, &status};
+        if (hipLaunchKernel(reinterpret_cast<const void *>(&kda_validate_kernel), dim3(1), dim3(VALIDATE_THREADS),
+                            vargs, 0, s) != hipSuccess)
+            return KDA_ERR_LAUNCH;
+    }
     // packed batches: the staged body; step calls with several tokens per
     // request or fewer tiles than compute units: the peeled body; otherwise
     // the prefetching loop (all measured on MI355X, cold caches)

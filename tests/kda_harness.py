@@ -95,11 +95,12 @@ def upload(p: ki.Problem, background_seed: int = 1234, state_dtype=torch.float32
         live_slots=live_slots)
 
 
-def run_gpu(d: DeviceProblem, packed: bool | None = None, flags: int = 0, stream=None):
+def run_gpu(d: DeviceProblem, packed: bool | None = None, flags: int = 0, stream=None, device_status=None):
     p = d.p
     if packed is None:
         packed = p.T is None
-    kw = dict(scale=p.scale, gate=d.gate, norm_weight=d.norm_weight, eps=p.eps, flags=flags, stream=stream)
+    kw = dict(scale=p.scale, gate=d.gate, norm_weight=d.norm_weight, eps=p.eps, flags=flags, stream=stream,
+              device_status=device_status)
     if packed:
         kda.kda_decode_packed(d.q, d.k, d.v, d.g, d.beta, d.state, d.slot_idx, d.cu_seqlens, d.out, **kw)
     else:

@@ -149,6 +149,27 @@ def test_bf16_state_flag():
     assert _step(a, flags=kda.KDA_FLAG_STATE_BF16) == DEVICE
 
 
+def test_validate_flag_needs_a_status_word():
+    V = kda.KDA_FLAG_VALIDATE
+    a, _ = _valid_args()
+    assert _step(a, flags=V) == NULL
+    a, spare = _valid_args()
+    a.device_status = spare + 2
+    assert _step(a, flags=V) == ALIGN
+    a, _ = _valid_args()
+    a.device_status = a.slot_idx + 4                 # inside the slot indices
+    assert _step(a, flags=V) == ALIAS
+    a, _ = _valid_args()
+    a.device_status = a.state + 1024                 # inside the pool
+    assert _step(a, flags=V) == ALIAS
+    a, spare = _valid_args()
+    a.device_status = spare
+    assert _step(a, flags=V) == DEVICE
+    a, _ = _valid_args()
+    a.device_status = a.q                            # ignored without the flag
+    assert _step(a) == DEVICE
+
+
 def test_aliasing():
     a, _ = _valid_args()
     a.out = a.q + 256                              # out inside q
@@ -175,7 +196,7 @@ def test_aliasing():
 
 def test_unknown_flags():
     a, _ = _valid_args()
-    assert _step(a, flags=2) == UNSUP
+    assert _step(a, flags=4) == UNSUP
     a, _ = _valid_args()
     assert _step(a, flags=1 << 12) == UNSUP
     a, _ = _valid_args()

@@ -110,6 +110,108 @@ def test_bf16_state_tile_widths_bit_identical():
         assert torch.equal(o, results[0][0]) and torch.equal(s_, results[0][1])
 
 
+# ------------------------------------------------------- transactional validation
+def _status_word():
+    return torch.full((1,), -7, dtype=torch.int32, device=DEV)
+
+
+def test_validate_passes_valid_metadata_bit_identical():
+    for name in ("n32_t1_h8", "n8_t4_h8", "packed_n256_h12", "n32_t1_h16_norm"):
+        p = ki.workload(name)
+        a = _fresh(p)
+        run_gpu(a)
+        b = _fresh(p)
+        st = _status_word()
+        run_gpu(b, device_status=st)
+        torch.cuda.synchronize()
+        assert st.item() == 0, name
+        assert torch.equal(a.state, b.state) and torch.equal(a.out.view(torch.int16), b.out.view(torch.int16))
+
+
+def _corrupt(p, case):
+    live = p.live_requests()
+    if case == "duplicate":
+        p.slot_idx[live[5]] = p.slot_idx[live[2]]
+        return 2
+    if case == "past_pool":
+        p.slot_idx[live[1]] = p.num_slots
+        return 1
+    if case == "negative":
+        p.slot_idx[live[1]] = -3
+        return 1
+    if case == "both":                          # lowest code wins
+        p.slot_idx[live[5]] = p.slot_idx[live[2]]
+        p.slot_idx[live[7]] = p.num_slots + 9
+        return 1
+    if case == "decreasing":
+        p.cu_seqlens[4] = p.cu_seqlens[6]
+        return 3
+    raise ValueError(case)
+
+
+@pytest.mark.parametrize("case", ["duplicate", "past_pool", "negative", "both", "decreasing"])
+def test_validate_rejects_and_touches_nothing(case):
+    p = ki.workload("packed_n256_h12")
+    code = _corrupt(p, case)
+    d = upload(p)
+    before = d.state.clone()
+    st = _status_word()
+    run_gpu(d, device_status=st)
+    torch.cuda.synchronize()
+    assert st.item() == code
+    assert torch.equal(d.state, before)
+    assert torch.all(d.out.view(torch.int16) == np.int16(np.uint16(0xC640).view(np.int16)))
+
+
+def test_validate_rejects_cu_seqlens_past_the_tokens():
+    """cu_seqlens[N] beyond total_tokens: the call is given fewer token rows
+    than the tensors hold, so even an unvalidated run would stay in bounds."""
+    import ctypes
+    p = ki.workload("packed_n256_h12")
+    d = upload(p)
+    before = d.state.clone()
+    st = _status_word()
+    a = kda.decode_args(d.q, d.k, d.v, d.g, d.beta, d.state, d.slot_idx, d.out, p.scale, device_status=st)
+    rc = kda.library().kda_decode_packed(ctypes.byref(a), d.cu_seqlens.data_ptr(), p.tokens - 1,
+                                         kda.KDA_FLAG_VALIDATE, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0 and st.item() == 3
+    assert torch.equal(d.state, before)
+
+
+def test_validate_inside_a_graph():
+    """A captured validated call: replays with valid metadata decode, a replay
+    after the slot indices were corrupted in place touches nothing."""
+    p = ki.workload("n32_t1_h8")
+    ref = _fresh(p)
+    run_gpu(ref)
+    d = _fresh(p)
+    init = d.state.clone()
+    st = _status_word()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            run_gpu(d, device_status=st)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    assert st.item() == 0 and torch.equal(d.state, ref.state)
+    good = d.slot_idx.clone()
+    d.slot_idx[3] = d.slot_idx[9]
+    d.state.copy_(init)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    assert st.item() == 2 and torch.equal(d.state, init)
+    d.slot_idx.copy_(good)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    assert st.item() == 0 and torch.equal(d.state, ref.state)
+
+
 # ------------------------------------------------------- edge cases
 def test_all_requests_padding():
     p = ki.make_problem("allpad", 5, N=4, H=2, HV=2, K=128, V=128, num_slots=6, T=None, n_pad=4)
