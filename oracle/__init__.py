@@ -47,7 +47,7 @@ def _load():
         i64, i64, i64, i64, i64, p,
         p, i64, p, i64, p, i64, p, i64, p, i64,
         p, i64, i64, p, ctypes.c_double,
-        p, i64, p, ctypes.c_double, p, i64]
+        p, i64, p, ctypes.c_double, p, i64, p, i64]
     lib.kda_oracle_gated_rmsnorm.restype = ctypes.c_int
     lib.kda_oracle_gated_rmsnorm.argtypes = [i64, i64, p, p, p, ctypes.c_double, p]
     _lib = lib
@@ -74,7 +74,7 @@ def _tok_stride(a: np.ndarray, inner: int) -> int:
 
 
 def decode_packed(q, k, v, g, beta, state, slot_idx, cu_seqlens, scale, *,
-                  gate=None, norm_weight=None, eps=1e-6, out=None):
+                  gate=None, norm_weight=None, eps=1e-6, out=None, inter_state=None):
     """Run the oracle over a packed batch.
 
     q, k: uint16 bf16 bits [tokens, H, K]; v: uint16 [tokens, HV, V];
@@ -84,6 +84,8 @@ def decode_packed(q, k, v, g, beta, state, slot_idx, cu_seqlens, scale, *,
     gate: uint16 [tokens, HV, V] or None; norm_weight: uint16 [V].
     Returns out, float64 [tokens, HV, V] (NaN where a request was skipped,
     unless ``out`` is given, which is then left untouched there).
+    inter_state: None, or float64 [tokens, HV, K, V] that receives the state
+    after each token of each live request.
     """
     lib = _load()
     tokens, H, K = q.shape
@@ -110,6 +112,9 @@ def decode_packed(q, k, v, g, beta, state, slot_idx, cu_seqlens, scale, *,
             raise ValueError(f"dtype {a.dtype}, expected {dt}")
     if gate is not None:
         norm_weight = np.ascontiguousarray(norm_weight, dtype=np.uint16)
+    if inter_state is not None and (inter_state.dtype != np.float64 or not inter_state.flags.c_contiguous
+                                    or inter_state.shape != (tokens, HV, K, V)):
+        raise ValueError("inter_state must be C-contiguous float64 [tokens, HV, K, V]")
     rc = lib.kda_oracle_decode(
         N, H, HV, K, V, _ptr(cu_seqlens),
         _ptr(q), _tok_stride(q, H * K), _ptr(k), _tok_stride(k, H * K),
@@ -117,7 +122,8 @@ def decode_packed(q, k, v, g, beta, state, slot_idx, cu_seqlens, scale, *,
         _ptr(beta), _tok_stride(beta, HV),
         _ptr(state), num_slots, slot_stride, _ptr(slot_idx), float(scale),
         _ptr(gate), 0 if gate is None else _tok_stride(gate, HV * V),
-        _ptr(norm_weight), float(eps), _ptr(out), HV * V)
+        _ptr(norm_weight), float(eps), _ptr(out), HV * V,
+        _ptr(inter_state), HV * K * V)
     if rc != 0:
         raise ValueError(f"oracle rejected its arguments (code {rc})")
     return out

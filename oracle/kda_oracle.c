@@ -83,6 +83,9 @@ static void gated_rmsnorm_row(const double *o, const uint16_t *z, const uint16_t
  *   norm_weight bf16 bits [V] (used with gate)
  *   out    double, (t, hv, j) at t*out_stride + hv*V + j; written for live
  *          requests only
+ *   inter_state  NULL, or double (t, hv, i, j) at t*inter_stride + (hv*K + i)*V + j:
+ *          the state of each live request's value head right after token t
+ *          (what a speculative decoder restores when it accepts tokens up to t)
  *
  * Value head hv reads q/k head hv / (HV / H).
  * Returns 0, or a negative number for arguments it cannot interpret.
@@ -98,11 +101,12 @@ int kda_oracle_decode(int64_t N, int64_t H, int64_t HV, int64_t K, int64_t V,
                       const int32_t *slot_idx, double scale,
                       const uint16_t *gate, int64_t gate_stride,
                       const uint16_t *norm_weight, double eps,
-                      double *out, int64_t out_stride)
+                      double *out, int64_t out_stride,
+                      double *inter_state, int64_t inter_stride)
 {
     if (N < 0 || H < 1 || HV < 1 || K < 1 || V < 1 || HV % H != 0)
         return -1;
-    if (slot_stride < HV * K * V)
+    if (slot_stride < HV * K * V || (inter_state && inter_stride < HV * K * V))
         return -1;
     for (int64_t n = 0; n < N; ++n)
         if (cu_seqlens[n + 1] < cu_seqlens[n])
@@ -165,6 +169,8 @@ int kda_oracle_decode(int64_t N, int64_t H, int64_t HV, int64_t K, int64_t V,
                 } else {
                     memcpy(dst, o, sizeof(double) * (size_t)V);
                 }
+                if (inter_state)
+                    memcpy(inter_state + t * inter_stride + hv * K * V, S, sizeof(double) * (size_t)(K * V));
             }
         }
     }

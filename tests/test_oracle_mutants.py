@@ -54,6 +54,8 @@ MUTANTS = {
     "drop_last_token": ("t < cu_seqlens[n + 1]; ++t)", "t + 1 < cu_seqlens[n + 1]; ++t)"),
     "beta_of_head0": ("beta[t * beta_stride + hv]", "beta[t * beta_stride]"),
     "g_of_head0": ("g + t * g_stride + hv * K", "g + t * g_stride"),
+    "inter_state_of_head0": ("memcpy(inter_state + t * inter_stride + hv * K * V, S,",
+                             "memcpy(inter_state + t * inter_stride, S,"),
     "readout_before_update": "READOUT_BEFORE_UPDATE",
     "decay_after_correction": "DECAY_AFTER_CORRECTION",
 }
@@ -96,6 +98,7 @@ PINS = [
     pins.test_norm_constant_row_closed_form,
     pins.test_norm_scale_invariance_and_gate_symmetry,
     pins.test_norm_epilogue_wiring_in_decode,
+    pins.test_intermediate_states_are_the_chained_states,
 ]
 
 

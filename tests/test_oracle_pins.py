@@ -246,6 +246,25 @@ def test_chained_single_tokens_equal_one_multi_token_call():
     assert np.array_equal(st_a, st_b)
 
 
+def test_intermediate_states_are_the_chained_states():
+    """The state after token t of a multi-token call is the final state of the
+    chain of single-token calls that stops at t (pinned by the chaining pin)."""
+    p = ki.make_problem("inter", 24, N=3, H=1, HV=2, K=8, V=8, num_slots=5, T=3, n_pad=1)
+    st = p.state_pool().astype(np.float64)
+    chain = st.copy()
+    inter = np.full((p.tokens, p.HV, p.K, p.V), np.nan)
+    _run(p, st.copy(), inter_state=inter)
+    for t in range(3):
+        rows = np.arange(p.N) * 3 + t
+        oracle.decode_step(p.q[rows], p.k[rows], p.v[rows], p.g[rows], p.beta[rows], chain, p.slot_idx, 1, p.scale)
+        for n in range(p.N):
+            s_ = p.slot_idx[n]
+            if s_ < 0:
+                assert np.all(np.isnan(inter[n * 3 + t]))          # skipped: never written
+            else:
+                assert np.array_equal(inter[n * 3 + t], chain[s_])
+
+
 def test_skipped_rows_and_untouched_slots():
     p = ki.make_problem("skip", 18, N=6, H=1, HV=2, K=8, V=8, num_slots=10, T=None, n_pad=2)
     p.slot_idx[np.nonzero(p.slot_idx >= 0)[0][0]] = 10          # out of range: skipped too
