@@ -123,8 +123,17 @@ typedef enum kda_status {
  *
  *   device_status  with KDA_FLAG_VALIDATE, a device int32 the call writes
  *              (4-byte aligned, overlapping no other buffer); else ignored.
+ *   inter_state NULL, or the state of each live request's value head right
+ *              after each of its tokens: (t, hv, i, j) at
+ *              t*inter_stride + (hv*K + i)*V + j, the pool's element type and
+ *              alignment, inter_stride a multiple of 4, >= HV*K*V.  For
+ *              speculative decoding: the pool still ends with the state after
+ *              the last token; a caller that accepts a >= 1 of a request's
+ *              tokens restores row bos+a-1.  Rows of skipped requests are not
+ *              written.
  *
- * Aliasing: out and state may not overlap each other, or any input
+ * Aliasing: out, state, inter_state and device_status may not overlap each
+ * other or any input
  * (q, k, v, g, beta, slot_idx, cu_seqlens, gate, norm_weight); inputs may
  * overlap each other (q, k, v are often views of one projection).  Ranges are
  * the bounding byte ranges of each strided tensor.
@@ -144,6 +153,7 @@ typedef struct kda_decode_args {
     const void *norm_weight;
     float norm_eps;
     int32_t *device_status;   /* KDA_FLAG_VALIDATE only: caller-owned device int32 */
+    void *inter_state;  int64_t inter_stride;   /* NULL, or per-token states (below) */
 } kda_decode_args;
 
 /*

@@ -69,6 +69,7 @@ class KdaDecodeArgs(ctypes.Structure):
         ("norm_weight", ctypes.c_void_p),
         ("norm_eps", ctypes.c_float),
         ("device_status", ctypes.c_void_p),
+        ("inter_state", ctypes.c_void_p), ("inter_stride", ctypes.c_int64),
     ]
 
 
@@ -143,7 +144,7 @@ def _state_flag(state: torch.Tensor, flags: int) -> int:
 
 
 def decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate=None, norm_weight=None,
-                eps: float = 1e-6, device_status=None) -> KdaDecodeArgs:
+                eps: float = 1e-6, device_status=None, inter_state=None) -> KdaDecodeArgs:
     """Marshal tensors into a ``kda_decode_args`` struct (no validation of
     values; the library validates sizes, alignment and overlap)."""
     _check(q, "q", torch.bfloat16, 3)
@@ -183,17 +184,25 @@ def decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate=None, norm_w
     if device_status is not None:
         _check(device_status, "device_status", torch.int32, 1)
         a.device_status = device_status.data_ptr()
+    if inter_state is not None:
+        _check(inter_state, "inter_state", state.dtype, 4)
+        if inter_state.shape != (tokens, HV, K, V):
+            raise ValueError("inter_state must be [tokens, HV, K, V]")
+        a.inter_state, a.inter_stride = inter_state.data_ptr(), _lead_stride(inter_state)
     return a
 
 
 def kda_decode_step(q, k, v, g, beta, state, slot_idx, out, *, T: int, scale: float,
                     gate=None, norm_weight=None, eps: float = 1e-6, flags: int = 0, stream=None,
-                    device_status=None):
+                    device_status=None, inter_state=None):
     """Decode T tokens for each of N requests (tokens request-major, N*T rows);
     updates ``state`` in place and writes ``out`` for live requests.  With
     ``device_status`` (an int32 device tensor of one element) the device
-    metadata is validated first, all or nothing (KDA_FLAG_VALIDATE)."""
-    a = decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate, norm_weight, eps, device_status)
+    metadata is validated first, all or nothing (KDA_FLAG_VALIDATE).  With
+    ``inter_state`` ([tokens, HV, K, V], the pool's dtype) the state after
+    every token is written too (speculative decoding)."""
+    a = decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate, norm_weight, eps, device_status,
+                    inter_state)
     if device_status is not None:
         flags = int(flags) | KDA_FLAG_VALIDATE
     if q.shape[0] != a.N * int(T):
@@ -207,11 +216,12 @@ def kda_decode_step(q, k, v, g, beta, state, slot_idx, out, *, T: int, scale: fl
 
 def kda_decode_packed(q, k, v, g, beta, state, slot_idx, cu_seqlens, out, *, scale: float,
                       gate=None, norm_weight=None, eps: float = 1e-6, flags: int = 0, stream=None,
-                      device_status=None):
+                      device_status=None, inter_state=None):
     """Packed variable-length decode: request n owns token rows
-    cu_seqlens[n] .. cu_seqlens[n+1]-1.  ``device_status`` as for
-    kda_decode_step."""
-    a = decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate, norm_weight, eps, device_status)
+    cu_seqlens[n] .. cu_seqlens[n+1]-1.  ``device_status`` and
+    ``inter_state`` as for kda_decode_step."""
+    a = decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate, norm_weight, eps, device_status,
+                    inter_state)
     if device_status is not None:
         flags = int(flags) | KDA_FLAG_VALIDATE
     _check(cu_seqlens, "cu_seqlens", torch.int32, 1)

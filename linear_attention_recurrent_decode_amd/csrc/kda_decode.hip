@@ -67,6 +67,8 @@ struct DecodeParams {
     int32_t HV, heads_per_qk, T;
     float scale, eps;
     int32_t *status;             // KDA_FLAG_VALIDATE: the metadata check's verdict
+    void *inter_state;           // NULL, or the state after every token (pool element type)
+    int64_t inter_stride;
 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -480,6 +482,15 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot
     // so both directions use non-temporal accesses.
     const TileIO<BF16S> tile(state, slot * slot_stride + (int64_t)hv * (KD * VD) + (int64_t)row0 * VD + col);
     f32x4 s[ROWS_PER_LANE];
+    // per-token states for speculative decoding: the tile after token t
+    auto keep_state = [&](int64_t t) {
+        if (p.inter_state) {
+            const TileIO<BF16S> it(p.inter_state, t * p.inter_stride + (int64_t)hv * (KD * VD) + (int64_t)row0 * VD + col);
+#pragma unroll
+            for (int i = 0; i < ROWS_PER_LANE; ++i)
+                it.store(i, s[i]);
+        }
+    };
     TokenIn in;
     __shared__ float norm_partial[2][4];
 
@@ -489,8 +500,10 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot
 #pragma unroll
         for (int i = 0; i < ROWS_PER_LANE; ++i)
             s[i] = tile.load(i);
-        for (int64_t t = bos; t < eos; ++t)
+        for (int64_t t = bos; t < eos; ++t) {
             advance_token<NORM, true>(s, in, p, t, eos, h, hv, lane, wave, rg, row0, col, norm_partial);
+            keep_state(t);
+        }
     } else if constexpr (BODY == BODY_PEELED) {
         constexpr int FIRST_ROWS = 4;
 #pragma unroll
@@ -505,9 +518,11 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot
         // all 16 loads of the tile are in flight before any math starts
         __builtin_amdgcn_sched_barrier(0);
         advance_token<NORM, false>(s, in, p, bos, eos, h, hv, lane, wave, rg, row0, col, norm_partial);
+        keep_state(bos);
         for (int64_t t = bos + 1; t < eos; ++t) {
             load_token(in, p, t, h, hv, row0, col);
             advance_token<NORM, false>(s, in, p, t, eos, h, hv, lane, wave, rg, row0, col, norm_partial);
+            keep_state(t);
         }
     } else {
         __shared__ TokenStage<NW> st;
@@ -533,6 +548,7 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot
                 read_staged(in, st.k[j], st.q[j], st.g[j], st.v[j][wave * 8 + cg], st.beta[j], rg);
                 advance_token<NORM, false>(s, in, p, t0 + j, eos, h, hv, lane, wave, rg, row0, col,
                                            norm_partial);
+                keep_state(t0 + j);
             }
         }
     }
@@ -740,13 +756,26 @@ kda_status validate(const kda_decode_args *a, int64_t tokens, const int32_t *cu_
     for (const ByteRange &in : inputs)
         if (overlaps(out, in) || overlaps(state, in))
             return KDA_ERR_ALIAS;
+    ByteRange inter;
+    if (a->inter_state) {
+        if (!aligned(a->inter_state, 4 * state_elem) || a->inter_stride % 4)
+            return KDA_ERR_ALIGN;
+        if (a->inter_stride < hvk * a->V)
+            return KDA_ERR_SHAPE;
+        inter = span(a->inter_state, tokens, a->inter_stride, hvk * a->V, state_elem);
+        if (overlaps(inter, out) || overlaps(inter, state))
+            return KDA_ERR_ALIAS;
+        for (const ByteRange &in : inputs)
+            if (overlaps(inter, in))
+                return KDA_ERR_ALIAS;
+    }
     if (flags & KDA_FLAG_VALIDATE) {
         if (!a->device_status)
             return KDA_ERR_NULL;
         if (!aligned(a->device_status, 4))
             return KDA_ERR_ALIGN;
         const ByteRange st = span(a->device_status, 1, 0, 1, 4);
-        if (overlaps(st, out) || overlaps(st, state))
+        if (overlaps(st, out) || overlaps(st, state) || overlaps(st, inter))
             return KDA_ERR_ALIAS;
         for (const ByteRange &in : inputs)
             if (overlaps(st, in))
@@ -854,6 +883,8 @@ kda_status run_decode(const kda_decode_args *a, int32_t T, const int32_t *cu_seq
     p.scale = a->scale;
     p.eps = a->norm_eps;
     p.status = nullptr;
+    p.inter_state = a->inter_state;
+    p.inter_stride = a->inter_stride;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (flags & KDA_FLAG_VALIDATE) {

@@ -95,22 +95,24 @@ def upload(p: ki.Problem, background_seed: int = 1234, state_dtype=torch.float32
         live_slots=live_slots)
 
 
-def run_gpu(d: DeviceProblem, packed: bool | None = None, flags: int = 0, stream=None, device_status=None):
+def run_gpu(d: DeviceProblem, packed: bool | None = None, flags: int = 0, stream=None, device_status=None,
+            inter_state=None):
     p = d.p
     if packed is None:
         packed = p.T is None
     kw = dict(scale=p.scale, gate=d.gate, norm_weight=d.norm_weight, eps=p.eps, flags=flags, stream=stream,
-              device_status=device_status)
+              device_status=device_status, inter_state=inter_state)
     if packed:
         kda.kda_decode_packed(d.q, d.k, d.v, d.g, d.beta, d.state, d.slot_idx, d.cu_seqlens, d.out, **kw)
     else:
         kda.kda_decode_step(d.q, d.k, d.v, d.g, d.beta, d.state, d.slot_idx, d.out, T=p.T, **kw)
 
 
-def run_oracle(p: ki.Problem, state_bf16: bool = False):
+def run_oracle(p: ki.Problem, state_bf16: bool = False, inter_state=None):
     """Oracle over the live requests only, on a compact double pool holding
     just their slots.  Returns (out [tokens, HV, V] with NaN on skipped rows,
-    final state [n_live, HV, K, V] in request order)."""
+    final state [n_live, HV, K, V] in request order).  ``inter_state``: an
+    optional float64 [tokens, HV, K, V] array that receives each token's state."""
     live = p.live_requests()
     slots = p.slot_idx[live].astype(np.int64)
     pool = p.state_slots(slots)
@@ -122,7 +124,8 @@ def run_oracle(p: ki.Problem, state_bf16: bool = False):
     kw = {}
     if p.gate is not None:
         kw = dict(gate=p.gate, norm_weight=p.norm_weight, eps=p.eps)
-    out = oracle.decode_packed(p.q, p.k, p.v, p.g, p.beta, pool, remap, p.cu_seqlens, p.scale, **kw)
+    out = oracle.decode_packed(p.q, p.k, p.v, p.g, p.beta, pool, remap, p.cu_seqlens, p.scale,
+                               inter_state=inter_state, **kw)
     return out, pool
 
 

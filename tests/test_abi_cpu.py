@@ -170,6 +170,28 @@ def test_validate_flag_needs_a_status_word():
     assert _step(a) == DEVICE
 
 
+def test_intermediate_state_buffer():
+    a, spare = _valid_args()
+    a.inter_state, a.inter_stride = spare, 4 * 128 * 128
+    assert _step(a) == DEVICE
+    a.inter_state = spare + 8
+    assert _step(a) == ALIGN
+    assert _step(a, flags=kda.KDA_FLAG_STATE_BF16) == DEVICE     # 8 bytes is enough for bf16
+    a.inter_state, a.inter_stride = spare, 4 * 128 * 128 - 4
+    assert _step(a) == SHAPE
+    a.inter_stride = 4 * 128 * 128 + 2
+    assert _step(a) == ALIGN
+    a, _ = _valid_args()
+    a.inter_state, a.inter_stride = a.state + (1 << 20), 4 * 128 * 128   # inside the pool
+    assert _step(a) == ALIAS
+    a, _ = _valid_args()
+    a.inter_state, a.inter_stride = a.out, 4 * 128 * 128
+    assert _step(a) == ALIAS
+    a, _ = _valid_args()
+    a.inter_state, a.inter_stride = a.g, 4 * 128 * 128
+    assert _step(a) == ALIAS
+
+
 def test_aliasing():
     a, _ = _valid_args()
     a.out = a.q + 256                              # out inside q

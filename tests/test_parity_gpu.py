@@ -110,6 +110,48 @@ def test_bf16_state_tile_widths_bit_identical():
         assert torch.equal(o, results[0][0]) and torch.equal(s_, results[0][1])
 
 
+# ------------------------------------------------------- per-token states (speculative decoding)
+INTER_CASES = [
+    ("n8_t4_h8", torch.float32),
+    ("n32_t4_h8", torch.bfloat16),
+    ("packed_small", torch.float32),
+    ("packed_small", torch.bfloat16),
+    ("n32_t1_h16_norm", torch.float32),
+]
+
+
+@pytest.mark.parametrize("name,dtype", INTER_CASES)
+def test_intermediate_states(name, dtype):
+    if name == "packed_small":
+        p = ki.make_problem("ps", 61, N=40, H=4, HV=4, K=128, V=128, num_slots=64, T=None, t_max=6, n_pad=5)
+    else:
+        p = ki.workload(name)
+    d = upload(p, state_dtype=dtype)
+    sentinel = 1232.0                         # exact in fp32 and bf16
+    inter = torch.full((p.tokens, p.HV, p.K, p.V), sentinel, dtype=dtype, device=DEV)
+    run_gpu(d, inter_state=inter)
+    torch.cuda.synchronize()
+    ref_inter = np.full((p.tokens, p.HV, p.K, p.V), np.nan)
+    ref_out, ref_state = run_oracle(p, state_bf16=dtype == torch.bfloat16, inter_state=ref_inter)
+    compare(d, ref_out, ref_state)
+    got = inter.float().cpu().numpy().astype(np.float64)
+    live_rows = np.isfinite(ref_inter[:, 0, 0, 0])
+    assert np.all(got[~live_rows] == sentinel)                    # skipped requests: not written
+    err = np.abs(got[live_rows] - ref_inter[live_rows])
+    r = np.abs(ref_inter[live_rows])
+    if dtype == torch.bfloat16:
+        assert np.all(err <= 2.0 ** -8 * r + 1e-6)
+    else:
+        assert np.all(err <= 1e-4 * r + 1e-6)
+        assert err.max() <= 2e-6 * r.max()
+    # the last token's state is the final pool state, bit for bit
+    for n in p.live_requests():
+        last = int(p.cu_seqlens[n + 1]) - 1
+        if last >= int(p.cu_seqlens[n]):
+            assert torch.equal(inter[last], d.state[int(p.slot_idx[n])])
+    _log(f"inter {name} {dtype}: max|d| {err.max():.3e}", "")
+
+
 # ------------------------------------------------------- transactional validation
 def _status_word():
     return torch.full((1,), -7, dtype=torch.int32, device=DEV)
