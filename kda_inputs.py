@@ -29,6 +29,17 @@ kernel must skip.  Recipe:
   state   fp32, N(0, 0.05) in every pool slot (0.05 is the standard deviation)
   gate    bf16, N(0,1); norm weight bf16, 1 + N(0, 0.02); eps 1e-6
   scale   1/sqrt(K)
+
+Raw-projection problems (``raw_gates=True``) carry the gate inputs before
+activation instead of g and beta (FlashInfer PR 4562, inline review of the
+binding: bf16 raw_gate and raw_beta, fp32 A_log and dt_bias):
+
+  raw_gate  bf16, N(0,1) per key channel (the same draws as g's x above)
+  raw_beta  bf16, N(0,1) per (token, value head) (the same draws as beta's)
+  A_log     fp32, N(0, a_log_std) per value head
+  dt_bias   fp32, N(0, dt_bias_std) per (value head, key channel)
+
+The activation itself is the decode's business: this module only draws.
 """
 from __future__ import annotations
 
@@ -46,6 +57,7 @@ _M2 = np.uint64(0x94D049BB133111EB)
 STREAM_STATE, STREAM_SLOTS, STREAM_T, STREAM_PAD = 1, 2, 3, 4
 STREAM_Q, STREAM_K, STREAM_V, STREAM_G, STREAM_BETA = 5, 6, 7, 8, 9
 STREAM_GATE, STREAM_WEIGHT = 10, 11
+STREAM_ALOG, STREAM_DTBIAS = 12, 13
 
 SEED_BASE = 0x4B444100  # "KDA\0"
 
@@ -119,6 +131,9 @@ class Problem:
     Token-major layouts, contiguous: q, k [tokens, H, K] bf16 bits; v
     [tokens, HV, V] bf16 bits; g [tokens, HV, K] fp32; beta [tokens, HV] fp32;
     gate [tokens, HV, V] bf16 bits or None; norm_weight [V] bf16 bits or None.
+    Raw-projection problems have g = beta = None and instead raw_gate
+    [tokens, HV, K] and raw_beta [tokens, HV] bf16 bits, A_log [HV] and
+    dt_bias [HV, K] fp32.
     Request i owns tokens cu_seqlens[i] .. cu_seqlens[i+1]-1 and pool slot
     slot_idx[i] (-1: inactive padding row).  The state pool is
     [num_slots, HV, K, V] fp32 and is generated on demand (``state_slots``).
@@ -138,13 +153,21 @@ class Problem:
     q: np.ndarray
     k: np.ndarray
     v: np.ndarray
-    g: np.ndarray
-    beta: np.ndarray
+    g: Optional[np.ndarray]
+    beta: Optional[np.ndarray]
     gate: Optional[np.ndarray]
     norm_weight: Optional[np.ndarray]
     eps: float
     scale: float
     state_std: float = 0.05
+    raw_gate: Optional[np.ndarray] = None
+    raw_beta: Optional[np.ndarray] = None
+    A_log: Optional[np.ndarray] = None
+    dt_bias: Optional[np.ndarray] = None
+
+    @property
+    def raw(self) -> bool:
+        return self.raw_gate is not None
 
     @property
     def tokens(self) -> int:
@@ -182,11 +205,13 @@ def _unit_rows(x: np.ndarray) -> np.ndarray:
 def make_problem(name: str, seed: int, N: int, H: int, HV: int, K: int, V: int,
                  num_slots: int, T: Optional[int] = None, t_max: int = 4,
                  n_pad: int = 0, norm: bool = False, first_slots: bool = False,
-                 eps: float = 1e-6) -> Problem:
+                 eps: float = 1e-6, raw_gates: bool = False, a_log_std: float = 0.5,
+                 dt_bias_std: float = 0.5) -> Problem:
     """Draw one problem.  ``T`` fixed -> step call; ``T is None`` -> packed call
     with per-request T uniform on {1..t_max}.  ``n_pad`` requests (at seeded
     random positions) get slot -1.  Live requests get distinct pool slots, the
-    first ones (``first_slots``) or a seeded random subset."""
+    first ones (``first_slots``) or a seeded random subset.  ``raw_gates``:
+    raw projections for the fused gate activation instead of g and beta."""
     if HV % H:
         raise ValueError("HV must be a multiple of H")
     if T is not None:
@@ -215,9 +240,16 @@ def make_problem(name: str, seed: int, N: int, H: int, HV: int, K: int, V: int,
     k = _unit_rows(normal(seed, STREAM_K, tokens * H * K).reshape(tokens, H, K))
     v = normal(seed, STREAM_V, tokens * HV * V).reshape(tokens, HV, V)
     x = normal(seed, STREAM_G, tokens * HV * K).reshape(tokens, HV, K)
-    g = -(np.log1p(np.exp(-np.abs(x))) + np.maximum(x, 0.0))          # -softplus(x)
     xb = normal(seed, STREAM_BETA, tokens * HV).reshape(tokens, HV)
-    beta = 1.0 / (1.0 + np.exp(-xb))                                   # sigmoid(x)
+    raw = {}
+    if raw_gates:
+        g = beta = None
+        raw = dict(raw_gate=to_bf16_bits(x), raw_beta=to_bf16_bits(xb),
+                   A_log=(a_log_std * normal(seed, STREAM_ALOG, HV)).astype(np.float32),
+                   dt_bias=(dt_bias_std * normal(seed, STREAM_DTBIAS, HV * K)).astype(np.float32).reshape(HV, K))
+    else:
+        g = (-(np.log1p(np.exp(-np.abs(x))) + np.maximum(x, 0.0))).astype(np.float32)   # -softplus(x)
+        beta = (1.0 / (1.0 + np.exp(-xb))).astype(np.float32)                            # sigmoid(x)
     gate = w = None
     if norm:
         gate = to_bf16_bits(normal(seed, STREAM_GATE, tokens * HV * V).reshape(tokens, HV, V))
@@ -226,8 +258,7 @@ def make_problem(name: str, seed: int, N: int, H: int, HV: int, K: int, V: int,
         name=name, seed=seed, N=N, H=H, HV=HV, K=K, V=V, num_slots=num_slots, T=T,
         cu_seqlens=cu.astype(np.int32), slot_idx=slot_idx.astype(np.int32),
         q=to_bf16_bits(q), k=to_bf16_bits(k), v=to_bf16_bits(v),
-        g=g.astype(np.float32), beta=beta.astype(np.float32),
-        gate=gate, norm_weight=w, eps=eps, scale=1.0 / math.sqrt(K))
+        g=g, beta=beta, gate=gate, norm_weight=w, eps=eps, scale=1.0 / math.sqrt(K), **raw)
 
 
 # The five serving workloads, named by what they are.

@@ -47,7 +47,10 @@ def _load():
         i64, i64, i64, i64, i64, p,
         p, i64, p, i64, p, i64, p, i64, p, i64,
         p, i64, i64, p, ctypes.c_double,
-        p, i64, p, ctypes.c_double, p, i64, p, i64]
+        p, i64, p, ctypes.c_double, p, i64, p, i64,
+        p, i64, p, i64, p, p]
+    lib.kda_oracle_gate_activation.restype = ctypes.c_int
+    lib.kda_oracle_gate_activation.argtypes = [i64, i64, i64, p, i64, p, i64, p, p, p, p]
     lib.kda_oracle_gated_rmsnorm.restype = ctypes.c_int
     lib.kda_oracle_gated_rmsnorm.argtypes = [i64, i64, p, p, p, ctypes.c_double, p]
     _lib = lib
@@ -73,8 +76,39 @@ def _tok_stride(a: np.ndarray, inner: int) -> int:
     return a.strides[0] // item
 
 
+def _raw_gate_args(raw_gate, raw_beta, A_log, dt_bias, tokens, HV, K):
+    """Validate the raw-projection inputs of the gate activation."""
+    if raw_gate.dtype != np.uint16 or raw_beta.dtype != np.uint16:
+        raise ValueError("raw_gate and raw_beta are bf16 bits (uint16)")
+    if raw_gate.shape != (tokens, HV, K) or raw_beta.shape != (tokens, HV):
+        raise ValueError("raw_gate must be [tokens, HV, K] and raw_beta [tokens, HV]")
+    A_log = np.ascontiguousarray(A_log, dtype=np.float32)
+    dt_bias = np.ascontiguousarray(dt_bias, dtype=np.float32)
+    if A_log.shape != (HV,) or dt_bias.reshape(-1).shape != (HV * K,):
+        raise ValueError("A_log must be [HV] and dt_bias [HV, K]")
+    return A_log, dt_bias
+
+
+def gate_activation(raw_gate, raw_beta, A_log, dt_bias):
+    """Step 0 alone: raw_gate uint16 [tokens, HV, K], raw_beta uint16
+    [tokens, HV], A_log float32 [HV], dt_bias float32 [HV, K] ->
+    (g float64 [tokens, HV, K], beta float64 [tokens, HV])."""
+    lib = _load()
+    tokens, HV, K = raw_gate.shape
+    A_log, dt_bias = _raw_gate_args(raw_gate, raw_beta, A_log, dt_bias, tokens, HV, K)
+    g = np.empty((tokens, HV, K), dtype=np.float64)
+    beta = np.empty((tokens, HV), dtype=np.float64)
+    rc = lib.kda_oracle_gate_activation(
+        tokens, HV, K, _ptr(raw_gate), _tok_stride(raw_gate, HV * K), _ptr(raw_beta),
+        _tok_stride(raw_beta, HV), _ptr(A_log), _ptr(dt_bias), _ptr(g), _ptr(beta))
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (code {rc})")
+    return g, beta
+
+
 def decode_packed(q, k, v, g, beta, state, slot_idx, cu_seqlens, scale, *,
-                  gate=None, norm_weight=None, eps=1e-6, out=None, inter_state=None):
+                  gate=None, norm_weight=None, eps=1e-6, out=None, inter_state=None,
+                  raw_gate=None, raw_beta=None, A_log=None, dt_bias=None):
     """Run the oracle over a packed batch.
 
     q, k: uint16 bf16 bits [tokens, H, K]; v: uint16 [tokens, HV, V];
@@ -86,6 +120,9 @@ def decode_packed(q, k, v, g, beta, state, slot_idx, cu_seqlens, scale, *,
     unless ``out`` is given, which is then left untouched there).
     inter_state: None, or float64 [tokens, HV, K, V] that receives the state
     after each token of each live request.
+    raw_gate (uint16 [tokens, HV, K]), raw_beta (uint16 [tokens, HV]), A_log
+    (float32 [HV]), dt_bias (float32 [HV, K]): all four or none; with them
+    the log-decay and beta are activated from these and g, beta may be None.
     """
     lib = _load()
     tokens, H, K = q.shape
@@ -107,7 +144,20 @@ def decode_packed(q, k, v, g, beta, state, slot_idx, cu_seqlens, scale, *,
         raise ValueError("out must be C-contiguous float64 [tokens, HV, V]")
     if (gate is None) != (norm_weight is None):
         raise ValueError("gate and norm_weight go together")
-    for a, dt in ((q, np.uint16), (k, np.uint16), (v, np.uint16), (g, np.float32), (beta, np.float32)):
+    raw = raw_gate is not None
+    if raw != (raw_beta is not None) or raw != (A_log is not None) or raw != (dt_bias is not None):
+        raise ValueError("raw_gate, raw_beta, A_log and dt_bias go together")
+    if raw:
+        A_log, dt_bias = _raw_gate_args(raw_gate, raw_beta, A_log, dt_bias, tokens, HV, K)
+        g_args = (None, HV * K, None, HV)
+        raw_args = (_ptr(raw_gate), _tok_stride(raw_gate, HV * K), _ptr(raw_beta), _tok_stride(raw_beta, HV),
+                    _ptr(A_log), _ptr(dt_bias))
+    else:
+        if g is None or beta is None or g.dtype != np.float32 or beta.dtype != np.float32:
+            raise ValueError("g and beta must be float32 arrays")
+        g_args = (_ptr(g), _tok_stride(g, HV * K), _ptr(beta), _tok_stride(beta, HV))
+        raw_args = (None, 0, None, 0, None, None)
+    for a, dt in ((q, np.uint16), (k, np.uint16), (v, np.uint16)):
         if a.dtype != dt:
             raise ValueError(f"dtype {a.dtype}, expected {dt}")
     if gate is not None:
@@ -118,12 +168,11 @@ def decode_packed(q, k, v, g, beta, state, slot_idx, cu_seqlens, scale, *,
     rc = lib.kda_oracle_decode(
         N, H, HV, K, V, _ptr(cu_seqlens),
         _ptr(q), _tok_stride(q, H * K), _ptr(k), _tok_stride(k, H * K),
-        _ptr(v), _tok_stride(v, HV * V), _ptr(g), _tok_stride(g, HV * K),
-        _ptr(beta), _tok_stride(beta, HV),
+        _ptr(v), _tok_stride(v, HV * V), *g_args,
         _ptr(state), num_slots, slot_stride, _ptr(slot_idx), float(scale),
         _ptr(gate), 0 if gate is None else _tok_stride(gate, HV * V),
         _ptr(norm_weight), float(eps), _ptr(out), HV * V,
-        _ptr(inter_state), HV * K * V)
+        _ptr(inter_state), HV * K * V, *raw_args)
     if rc != 0:
         raise ValueError(f"oracle rejected its arguments (code {rc})")
     return out

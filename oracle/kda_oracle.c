@@ -27,6 +27,22 @@
  * written to the caller's buffer: y[j] = o[j] / sqrt(mean_j o^2 + eps) *
  * w[j] * silu(z[j]), silu(x) = x / (1 + exp(-x)).
  *
+ * Gate activation (optional step 0).  The log-decay g_t and beta_t arrive
+ * either already activated (fp32) or as raw projections: FlashInfer PR 4562
+ * (inline review of the binding's launch arguments) hands its kernel a bf16
+ * raw_gate and raw_beta with fp32 A_log and dt_bias, and b12x PR 249 (its
+ * review of the aliasing checks) lists raw_g and raw_beta among the decode's
+ * inputs.  Neither page prints the activation.  The reading taken here is
+ * the gate of Kimi Delta Attention:
+ *
+ *   g_t[i]  = -exp(A_log[hv]) * softplus(raw_gate_t[hv][i] + dt_bias[hv][i])
+ *   beta_t  = sigmoid(raw_beta_t[hv])
+ *   softplus(x) = log(1 + exp(x)),  sigmoid(x) = 1 / (1 + exp(-x))
+ *
+ * A_log is one value per value head, dt_bias one per (value head, key
+ * channel).  With A_log = 0 and dt_bias = 0 it reduces to g = -softplus(x)
+ * and beta = sigmoid(x) of the raw values.
+ *
  * Slots.  Request n reads and writes state slot slot_idx[n]; a slot outside
  * [0, num_slots) (the value -1 marks a padding row) means the request is
  * skipped: its state is neither read nor written and none of its output
@@ -54,6 +70,36 @@ static double bf16_value(uint16_t bits)
 static double silu(double x)
 {
     return x / (1.0 + exp(-x));
+}
+
+/* softplus(x) = log(1 + e^x), evaluated as max(x, 0) + log(1 + e^-|x|) so
+ * that no exponential overflows; +inf maps to +inf and -inf to 0. */
+static double softplus(double x)
+{
+    return (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));
+}
+
+/* the logistic function; -inf maps to 0 and +inf to 1 */
+static double sigmoid(double r)
+{
+    return 1.0 / (1.0 + exp(-r));
+}
+
+/* Step 0 for value head hv of token t: the log-decay of every key channel
+ * and beta from the raw projections (reading at the top of this file).
+ * raw_gate (t, hv, i) at t*raw_gate_stride + hv*K + i; raw_beta (t, hv) at
+ * t*raw_beta_stride + hv; A_log [HV]; dt_bias (hv, i) at hv*K + i. */
+static void activate_gates(int64_t t, int64_t hv, int64_t K,
+                           const uint16_t *raw_gate, int64_t raw_gate_stride,
+                           const uint16_t *raw_beta, int64_t raw_beta_stride,
+                           const float *A_log, const float *dt_bias,
+                           double *g_out, double *beta_out)
+{
+    const double A = exp((double)A_log[hv]);
+    const uint16_t *rg = raw_gate + t * raw_gate_stride + hv * K;
+    for (int64_t i = 0; i < K; ++i)
+        g_out[i] = -A * softplus(bf16_value(rg[i]) + (double)dt_bias[hv * K + i]);
+    *beta_out = sigmoid(bf16_value(raw_beta[t * raw_beta_stride + hv]));
 }
 
 /* Gated RMSNorm of one row of V values (b12x PR 249, walkthrough: the
@@ -86,6 +132,9 @@ static void gated_rmsnorm_row(const double *o, const uint16_t *z, const uint16_t
  *   inter_state  NULL, or double (t, hv, i, j) at t*inter_stride + (hv*K + i)*V + j:
  *          the state of each live request's value head right after token t
  *          (what a speculative decoder restores when it accepts tokens up to t)
+ *   raw_gate  NULL: g and beta are used as given.  Otherwise step 0 computes
+ *          the log-decay and beta from raw_gate, raw_beta (bf16 bits), A_log
+ *          and dt_bias (layouts at activate_gates) and g, beta are ignored.
  *
  * Value head hv reads q/k head hv / (HV / H).
  * Returns 0, or a negative number for arguments it cannot interpret.
@@ -102,7 +151,10 @@ int kda_oracle_decode(int64_t N, int64_t H, int64_t HV, int64_t K, int64_t V,
                       const uint16_t *gate, int64_t gate_stride,
                       const uint16_t *norm_weight, double eps,
                       double *out, int64_t out_stride,
-                      double *inter_state, int64_t inter_stride)
+                      double *inter_state, int64_t inter_stride,
+                      const uint16_t *raw_gate, int64_t raw_gate_stride,
+                      const uint16_t *raw_beta, int64_t raw_beta_stride,
+                      const float *A_log, const float *dt_bias)
 {
     if (N < 0 || H < 1 || HV < 1 || K < 1 || V < 1 || HV % H != 0)
         return -1;
@@ -112,11 +164,15 @@ int kda_oracle_decode(int64_t N, int64_t H, int64_t HV, int64_t K, int64_t V,
         if (cu_seqlens[n + 1] < cu_seqlens[n])
             return -2;
 
+    if (raw_gate && (!raw_beta || !A_log || !dt_bias))
+        return -1;
+
     double *vp = malloc(sizeof(double) * (size_t)V);   /* v' */
     double *o = malloc(sizeof(double) * (size_t)V);
     double *y = malloc(sizeof(double) * (size_t)V);
-    if (!vp || !o || !y) {
-        free(vp); free(o); free(y);
+    double *gd = malloc(sizeof(double) * (size_t)K);   /* log-decay of the token */
+    if (!vp || !o || !y || !gd) {
+        free(vp); free(o); free(y); free(gd);
         return -3;
     }
     const int64_t heads_per_qk = HV / H;
@@ -132,12 +188,22 @@ int kda_oracle_decode(int64_t N, int64_t H, int64_t HV, int64_t K, int64_t V,
                 const uint16_t *qt = q + t * q_stride + h * K;
                 const uint16_t *kt = k + t * k_stride + h * K;
                 const uint16_t *vt = v + t * v_stride + hv * V;
-                const float *gt = g + t * g_stride + hv * K;
-                const double bt = (double)beta[t * beta_stride + hv];
+                double bt;
+
+                /* 0. log-decay and beta: given, or activated from raw projections */
+                if (raw_gate) {
+                    activate_gates(t, hv, K, raw_gate, raw_gate_stride, raw_beta, raw_beta_stride,
+                                   A_log, dt_bias, gd, &bt);
+                } else {
+                    const float *gt = g + t * g_stride + hv * K;
+                    for (int64_t i = 0; i < K; ++i)
+                        gd[i] = (double)gt[i];
+                    bt = (double)beta[t * beta_stride + hv];
+                }
 
                 /* 1. decay: row i of S scaled by exp(g_t[i]) */
                 for (int64_t i = 0; i < K; ++i) {
-                    const double a = exp((double)gt[i]);
+                    const double a = exp(gd[i]);
                     for (int64_t j = 0; j < V; ++j)
                         S[i * V + j] = a * S[i * V + j];
                 }
@@ -174,7 +240,27 @@ int kda_oracle_decode(int64_t N, int64_t H, int64_t HV, int64_t K, int64_t V,
             }
         }
     }
-    free(vp); free(o); free(y);
+    free(vp); free(o); free(y); free(gd);
+    return 0;
+}
+
+/*
+ * Step 0 alone over a batch of token rows: g (double [tokens][HV][K]) and
+ * beta (double [tokens][HV]) from the raw projections, with the layouts of
+ * activate_gates.
+ */
+int kda_oracle_gate_activation(int64_t tokens, int64_t HV, int64_t K,
+                               const uint16_t *raw_gate, int64_t raw_gate_stride,
+                               const uint16_t *raw_beta, int64_t raw_beta_stride,
+                               const float *A_log, const float *dt_bias,
+                               double *g, double *beta)
+{
+    if (tokens < 0 || HV < 1 || K < 1 || raw_gate_stride < HV * K || raw_beta_stride < HV)
+        return -1;
+    for (int64_t t = 0; t < tokens; ++t)
+        for (int64_t hv = 0; hv < HV; ++hv)
+            activate_gates(t, hv, K, raw_gate, raw_gate_stride, raw_beta, raw_beta_stride, A_log, dt_bias,
+                           g + (t * HV + hv) * K, beta + t * HV + hv);
     return 0;
 }
 

@@ -13,32 +13,13 @@ import test_oracle_pins as pins
 with open(oracle.SRC) as f:
     SOURCE = f.read()
 
-DECAY = """                for (int64_t i = 0; i < K; ++i) {
-                    const double a = exp((double)gt[i]);
-                    for (int64_t j = 0; j < V; ++j)
-                        S[i * V + j] = a * S[i * V + j];
-                }
-"""
-UPDATE = """                for (int64_t i = 0; i < K; ++i) {
-                    const double ki = bf16_value(kt[i]);
-                    for (int64_t j = 0; j < V; ++j)
-                        S[i * V + j] = S[i * V + j] + ki * vp[j];
-                }
-"""
 CORRECTION_HEAD = "                /* 2. delta correction against the decayed state */\n"
 READOUT_HEAD = "                /* 4. readout from the updated state */\n"
 
 
-def _swap_blocks(src, first, second_head, second):
-    """Move block ``first`` to just after block ``second`` (which follows it)."""
-    assert first in src and second in src
-    src = src.replace(first, "", 1)
-    return src.replace(second, second + first, 1)
-
-
 MUTANTS = {
     "no_decay": ("S[i * V + j] = a * S[i * V + j];", "S[i * V + j] = S[i * V + j];"),
-    "exp_of_minus_g": ("exp((double)gt[i])", "exp(-(double)gt[i])"),
+    "exp_of_minus_g": ("const double a = exp(gd[i]);", "const double a = exp(-gd[i]);"),
     "plus_u": ("bt * (bf16_value(vt[j]) - u)", "bt * (bf16_value(vt[j]) + u)"),
     "no_beta": ("vp[j] = bt * (bf16_value(vt[j]) - u);", "vp[j] = (bf16_value(vt[j]) - u);"),
     "transposed_state": ("u += S[i * V + j] * bf16_value(kt[i]);", "u += S[j * V + i] * bf16_value(kt[i]);"),
@@ -56,6 +37,17 @@ MUTANTS = {
     "g_of_head0": ("g + t * g_stride + hv * K", "g + t * g_stride"),
     "inter_state_of_head0": ("memcpy(inter_state + t * inter_stride + hv * K * V, S,",
                              "memcpy(inter_state + t * inter_stride, S,"),
+    "softplus_even_sign": ("log1p(exp(-fabs(x)))", "log1p(exp(fabs(x)))"),
+    "softplus_no_relu": ("return (x > 0.0 ? x : 0.0) + log1p", "return log1p"),
+    "A_not_exponentiated": ("const double A = exp((double)A_log[hv]);", "const double A = (double)A_log[hv];"),
+    "A_log_of_head0": ("exp((double)A_log[hv])", "exp((double)A_log[0])"),
+    "g_positive": ("g_out[i] = -A * softplus", "g_out[i] = A * softplus"),
+    "dt_bias_dropped": ("softplus(bf16_value(rg[i]) + (double)dt_bias[hv * K + i])", "softplus(bf16_value(rg[i]))"),
+    "dt_bias_of_head0": ("(double)dt_bias[hv * K + i]", "(double)dt_bias[i]"),
+    "raw_gate_of_head0": ("raw_gate + t * raw_gate_stride + hv * K;", "raw_gate + t * raw_gate_stride;"),
+    "raw_gate_of_token0": ("raw_gate + t * raw_gate_stride + hv * K;", "raw_gate + hv * K;"),
+    "sigmoid_sign": ("return 1.0 / (1.0 + exp(-r));", "return 1.0 / (1.0 + exp(r));"),
+    "raw_beta_of_head0": ("raw_beta[t * raw_beta_stride + hv]", "raw_beta[t * raw_beta_stride]"),
     "readout_before_update": "READOUT_BEFORE_UPDATE",
     "decay_after_correction": "DECAY_AFTER_CORRECTION",
 }
@@ -99,6 +91,13 @@ PINS = [
     pins.test_norm_scale_invariance_and_gate_symmetry,
     pins.test_norm_epilogue_wiring_in_decode,
     pins.test_intermediate_states_are_the_chained_states,
+    pins.test_gate_activation_logistic_closed_form,
+    pins.test_gate_activation_odd_part_and_scaling,
+    pins.test_gate_activation_bias_shift,
+    pins.test_gate_activation_beta_logistic,
+    pins.test_gate_activation_saturates_at_infinity,
+    pins.test_fused_gate_decode_equals_exact_activated_inputs,
+    pins.test_fused_gate_pure_decay_closed_form,
 ]
 
 

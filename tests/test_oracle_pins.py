@@ -45,6 +45,8 @@ def _run(p, state64, **kw):
     extra = {}
     if p.gate is not None:
         extra = dict(gate=p.gate, norm_weight=p.norm_weight, eps=p.eps)
+    if p.raw:
+        extra.update(raw_gate=p.raw_gate, raw_beta=p.raw_beta, A_log=p.A_log, dt_bias=p.dt_bias)
     extra.update(kw)
     return oracle.decode_packed(p.q, p.k, p.v, p.g, p.beta, state64, p.slot_idx, p.cu_seqlens, p.scale, **extra)
 
@@ -406,3 +408,151 @@ def test_bf16_widening_is_exact():
     st = np.zeros((1, 1, 5, 5))
     oracle.decode_step(q, k, v, g, beta, st, np.array([0], np.int32), 1, 1.0)
     assert list(st[0, 0, 0]) == [1.0, -2.0, 2.0 ** -133, (2.0 - 2.0 ** -7) * 2.0 ** 127, 3.140625]
+
+
+# ------------------------------------------------------------ gate activation
+# Raw-projection inputs (FlashInfer PR 4562, inline review of the binding:
+# raw_gate, raw_beta, A_log, dt_bias).  The activation is not printed on the
+# pages; the oracle takes the Kimi Delta Attention gate.  These pins fix it
+# through facts that do not evaluate that formula: the logistic closed form
+# of exp(-softplus(x)), the odd part of softplus, the shift by dt_bias, the
+# scaling by exp(A_log), the logistic function's symmetry and saturation.
+def _raw_inputs(seed, tokens=3, HV=3, K=16, bias=None):
+    """raw gate values in +/- pairs (channel i and i + K/2), A_log exact in
+    fp32, optional dt_bias."""
+    half = ki.normal(seed, 31, tokens * HV * (K // 2)).reshape(tokens, HV, K // 2) * 3.0
+    half[0, 0, :4] = [0.0, 40.0, -40.0, 0.5]
+    raw_gate = _bf(np.concatenate([half, -half], axis=-1))
+    raw_beta = _bf(ki.normal(seed, 32, tokens * HV).reshape(tokens, HV) * 3.0)
+    A_log = np.array([0.0, 0.75, -1.25, 1.5, -0.5][:HV], dtype=np.float32)
+    dt_bias = np.zeros((HV, K), np.float32) if bias is None else bias
+    return raw_gate, raw_beta, A_log, dt_bias
+
+
+def test_gate_activation_logistic_closed_form():
+    """exp(-softplus(x)) = 1 / (1 + e^x), so with A = exp(A_log) the decay
+    factor is (1 + e^x)^-A: head by head, token by token, channel by channel."""
+    raw_gate, raw_beta, A_log, dt_bias = _raw_inputs(7)
+    g, _ = oracle.gate_activation(raw_gate, raw_beta, A_log, dt_bias)
+    x = _f(raw_gate)
+    logistic = 1.0 / (1.0 + np.exp(x))
+    A = np.array([1.0, math.exp(0.75), math.exp(-1.25)])
+    np.testing.assert_allclose(np.exp(g), logistic ** A[None, :, None], rtol=1e-12, atol=0)
+    assert np.all(g <= 0)
+    # A_log = 0: softplus(0) = ln 2
+    assert abs(g[0, 0, 0] + math.log(2.0)) <= 1e-16
+
+
+def test_gate_activation_odd_part_and_scaling():
+    """softplus(x) - softplus(-x) = x, so g(x) - g(-x) = -exp(A_log) x; and
+    g scales with exp(A_log) head by head."""
+    raw_gate, raw_beta, A_log, dt_bias = _raw_inputs(8)
+    g, _ = oracle.gate_activation(raw_gate, raw_beta, A_log, dt_bias)
+    x = _f(raw_gate)
+    K2 = raw_gate.shape[-1] // 2
+    A = np.exp(A_log.astype(np.float64))
+    diff = g[..., :K2] - g[..., K2:]
+    np.testing.assert_allclose(diff, -A[None, :, None] * x[..., :K2], rtol=1e-13, atol=1e-300)
+    # same raw values on every head: the heads differ by the factor exp(A_log[hv]) alone
+    same = np.repeat(raw_gate[:, :1], 3, axis=1)
+    gs, _ = oracle.gate_activation(same, raw_beta, A_log, dt_bias)
+    for hv, a in enumerate((0.0, 0.75, -1.25)):
+        np.testing.assert_allclose(gs[:, hv], gs[:, 0] * math.exp(a), rtol=1e-15)
+
+
+def test_gate_activation_bias_shift():
+    """dt_bias[hv][i] is added to the raw value of channel i of head hv:
+    raw r with bias b gives exactly the g of raw r + b with no bias (values
+    chosen so that r, b and r + b are exact)."""
+    tokens, HV, K = 2, 3, 16
+    r = (np.arange(tokens * HV * K).reshape(tokens, HV, K) % 29 - 14) * 0.25
+    b = ((np.arange(HV * K).reshape(HV, K) * 7) % 17 - 8) * 0.125
+    raw_beta = _bf(np.zeros((tokens, HV)))
+    A_log = np.array([0.0, 0.75, -1.25], np.float32)
+    g_bias, _ = oracle.gate_activation(_bf(r), raw_beta, A_log, b.astype(np.float32))
+    g_shift, _ = oracle.gate_activation(_bf(r + b[None]), raw_beta, A_log, np.zeros((HV, K), np.float32))
+    assert np.array_equal(g_bias, g_shift)
+    g_none, _ = oracle.gate_activation(_bf(r), raw_beta, A_log, np.zeros((HV, K), np.float32))
+    assert not np.array_equal(g_bias, g_none)
+
+
+def test_gate_activation_beta_logistic():
+    """beta = sigmoid(raw_beta): 1/2 at 0, beta(r) + beta(-r) = 1,
+    beta(r) = e^r / (1 + e^r), and the infinities saturate to 0 and 1."""
+    raw_gate, raw_beta, A_log, dt_bias = _raw_inputs(9)
+    raw_beta[0, :3] = _bf([0.0, -np.inf, np.inf])
+    _, beta = oracle.gate_activation(raw_gate, raw_beta, A_log, dt_bias)
+    r = _f(raw_beta)
+    assert beta[0, 0] == 0.5 and beta[0, 1] == 0.0 and beta[0, 2] == 1.0
+    fin = np.isfinite(r)
+    np.testing.assert_allclose(beta[fin], np.exp(r[fin]) / (1.0 + np.exp(r[fin])), rtol=1e-15)
+    neg = raw_beta ^ np.uint16(0x8000)
+    _, beta_neg = oracle.gate_activation(raw_gate, neg, A_log, dt_bias)
+    np.testing.assert_allclose(beta + beta_neg, 1.0, rtol=0, atol=2e-16)
+
+
+def test_gate_activation_saturates_at_infinity():
+    """A raw gate of +inf clears the key channel (g = -inf, decay 0), -inf
+    keeps it (g = 0, decay 1), for every A_log."""
+    raw_gate, raw_beta, A_log, dt_bias = _raw_inputs(10)
+    raw_gate[:, :, 0] = _bf(np.inf)
+    raw_gate[:, :, 1] = _bf(-np.inf)
+    g, _ = oracle.gate_activation(raw_gate, raw_beta, A_log, dt_bias)
+    assert np.all(g[:, :, 0] == -np.inf)
+    assert np.all(g[:, :, 1] == 0.0)
+
+
+def test_fused_gate_decode_equals_exact_activated_inputs():
+    """Raw values whose activation is exact (raw gate +/-inf: g = -inf or 0;
+    raw beta 0, +inf, -inf: beta = 1/2, 1, 0) give bit for bit the decode of
+    the activated inputs, per token, head and channel."""
+    p = _small(21, N=3, H=2, HV=4, K=8, V=4, T=3, num_slots=5)
+    tokens = p.tokens
+    pick = ki.draws(77, 1, np.arange(tokens * p.HV * p.K, dtype=np.uint64)).reshape(tokens, p.HV, p.K)
+    clear = (pick % np.uint64(5)) == 0                   # about one channel in five cleared
+    raw_gate = np.where(clear, _bf(np.inf), _bf(-np.inf)).astype(np.uint16)
+    g = np.where(clear, -np.inf, 0.0).astype(np.float32)
+    choice = ki.draws(77, 2, np.arange(tokens * p.HV, dtype=np.uint64)).reshape(tokens, p.HV) % np.uint64(3)
+    raw_beta = _bf(np.choose(choice.astype(np.int64), [0.0, np.inf, -np.inf]))
+    beta = np.choose(choice.astype(np.int64), [0.5, 1.0, 0.0]).astype(np.float32)
+    A_log = (0.5 * ki.normal(77, 3, p.HV)).astype(np.float32)
+    dt_bias = (0.5 * ki.normal(77, 4, p.HV * p.K)).astype(np.float32).reshape(p.HV, p.K)
+    s_raw = p.state_pool().astype(np.float64)
+    s_act = s_raw.copy()
+    out_raw = oracle.decode_packed(p.q, p.k, p.v, None, None, s_raw, p.slot_idx, p.cu_seqlens, p.scale,
+                                   raw_gate=raw_gate, raw_beta=raw_beta, A_log=A_log, dt_bias=dt_bias)
+    out_act = oracle.decode_packed(p.q, p.k, p.v, g, beta, s_act, p.slot_idx, p.cu_seqlens, p.scale)
+    assert np.array_equal(out_raw, out_act, equal_nan=True)
+    assert np.array_equal(s_raw, s_act)
+
+
+def test_fused_gate_pure_decay_closed_form():
+    """raw beta = -inf (beta = 0): T tokens only decay the state, each key row
+    by prod_t (1 + e^(raw_t + bias))^(-exp(A_log))."""
+    p = _small(22, N=2, H=1, HV=3, K=8, V=4, T=3, num_slots=4, raw_gates=True)
+    raw_beta = np.full_like(p.raw_beta, _bf(-np.inf))
+    s = p.state_pool().astype(np.float64)
+    s0 = s.copy()
+    oracle.decode_packed(p.q, p.k, p.v, None, None, s, p.slot_idx, p.cu_seqlens, p.scale,
+                         raw_gate=p.raw_gate, raw_beta=raw_beta, A_log=p.A_log, dt_bias=p.dt_bias)
+    A = np.exp(p.A_log.astype(np.float64))
+    for n in range(p.N):
+        slot = p.slot_idx[n]
+        x = _f(p.raw_gate[p.cu_seqlens[n]:p.cu_seqlens[n + 1]]) + p.dt_bias.astype(np.float64)[None]
+        factor = np.prod((1.0 + np.exp(x)) ** -A[None, :, None], axis=0)     # [HV, K]
+        np.testing.assert_allclose(s[slot], s0[slot] * factor[:, :, None], rtol=1e-13, atol=0)
+
+
+def test_fused_gate_with_zero_parameters_is_the_activated_recipe():
+    """A_log = 0 and dt_bias = 0 give g = -softplus(x), beta = sigmoid(x):
+    the activated workloads' recipe, drawn from the same raw values, agrees to
+    the float32 rounding of its g and beta."""
+    raw = _small(23, N=2, H=2, HV=2, K=8, V=4, T=2, num_slots=4, raw_gates=True, a_log_std=0.0, dt_bias_std=0.0)
+    act = _small(23, N=2, H=2, HV=2, K=8, V=4, T=2, num_slots=4)
+    g, beta = oracle.gate_activation(raw.raw_gate, raw.raw_beta, raw.A_log, raw.dt_bias)
+    # the activated recipe evaluates the same draws before the bf16 rounding of
+    # the raw values: |d softplus / dx| <= 1 and a bf16 rounding moves x by at
+    # most 2^-9 |x|
+    x, xb = _f(raw.raw_gate), _f(raw.raw_beta)
+    assert np.all(np.abs(g - act.g) <= 2.0 ** -8 * np.abs(x) + 1e-6)
+    assert np.all(np.abs(beta - act.beta) <= 2.0 ** -10 * np.abs(xb) + 1e-6)
