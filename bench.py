@@ -51,12 +51,15 @@ def algorithmic_bytes(p, state_elem: int = 4) -> dict:
     """Bytes the call must move at least: each live (request, value head)
     reads and writes its K x V fp32 state once; each live token reads q, k
     (per q/k head), v, g, beta (per value head) and writes out (plus the gate
-    with the norm); slot indices, cu_seqlens and the norm weight once."""
+    with the norm); slot indices, cu_seqlens and the norm weight once.  With
+    the fused gate activation each token reads the bf16 raw gate and raw beta
+    instead of g and beta, and A_log and dt_bias are read once."""
     live = p.live_requests()
     lens = np.diff(p.cu_seqlens.astype(np.int64))
     live_tokens = int(lens[live].sum())
     state = 2 * len(live) * p.HV * p.K * p.V * state_elem
-    per_token = 2 * p.H * p.K * 2 + p.HV * p.V * 2 + p.HV * p.K * 4 + p.HV * 4 + p.HV * p.V * 2
+    gate_elem = 2 if p.raw else 4
+    per_token = 2 * p.H * p.K * 2 + p.HV * p.V * 2 + p.HV * p.K * gate_elem + p.HV * gate_elem + p.HV * p.V * 2
     if p.gate is not None:
         per_token += p.HV * p.V * 2
     io = live_tokens * per_token + p.N * 4
@@ -64,6 +67,8 @@ def algorithmic_bytes(p, state_elem: int = 4) -> dict:
         io += (p.N + 1) * 4
     if p.gate is not None:
         io += p.V * 2
+    if p.raw:
+        io += p.HV * 4 + p.HV * p.K * 4
     return {"state": state, "io": io, "total": state + io, "units": len(live) * p.HV}
 
 
@@ -107,6 +112,8 @@ def cpu_baseline(p, pool_live: np.ndarray, budget_s: float) -> dict:
     kw = {}
     if p.gate is not None:
         kw = dict(gate=p.gate, norm_weight=p.norm_weight, eps=p.eps)
+    if p.raw:
+        kw.update(raw_gate=p.raw_gate, raw_beta=p.raw_beta, A_log=p.A_log, dt_bias=p.dt_bias)
     pool = pool_live.astype(np.float64)
     oracle.decode_packed(p.q, p.k, p.v, p.g, p.beta, pool, remap, p.cu_seqlens, p.scale, **kw)  # warm-up
     n, t0 = 0, time.perf_counter()
@@ -172,8 +179,14 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
 
     q, k, v = bf(p.q), bf(p.k), bf(p.v)
-    g = torch.from_numpy(p.g).to(dev)
-    beta = torch.from_numpy(p.beta).to(dev)
+    g = beta = None
+    raw = {}
+    if p.raw:
+        raw = dict(raw_gate=bf(p.raw_gate), raw_beta=bf(p.raw_beta), A_log=torch.from_numpy(p.A_log).to(dev),
+                   dt_bias=torch.from_numpy(p.dt_bias).to(dev))
+    else:
+        g = torch.from_numpy(p.g).to(dev)
+        beta = torch.from_numpy(p.beta).to(dev)
     gate = bf(p.gate) if p.gate is not None else None
     w = bf(p.norm_weight) if p.norm_weight is not None else None
     cu = torch.from_numpy(p.cu_seqlens.astype(np.int32)).to(dev)
@@ -195,7 +208,7 @@ def main():
     combos = []
     for r in range(R):
         for s in set_t:
-            a = kda.decode_args(q, k, v, g, beta, pools[r], s, out, p.scale, gate, w, p.eps)
+            a = kda.decode_args(q, k, v, g, beta, pools[r], s, out, p.scale, gate, w, p.eps, **raw)
             combos.append(a)
     T = p.T if p.T is not None else 0
     packed = p.T is None
@@ -288,6 +301,7 @@ def main():
         "config": {"workload": p.name, "N": p.N, "T": p.T if p.T is not None else "1..4 packed",
                    "H": p.H, "HV": p.HV, "K": p.K, "V": p.V, "num_slots": p.num_slots,
                    "norm": p.gate is not None, "state_dtype": args.state,
+                   "gate_input": "raw, activated in the kernel" if p.raw else "activated",
                    "cold_slot_sets": len(sets), "cold_pool_copies": R,
                    "vtile": kda.kda_decode_plan(p.N * p.HV, T or 1, p.gate is not None)},
         "state_GBps": round(state_gbps, 1),

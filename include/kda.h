@@ -55,7 +55,7 @@ typedef enum kda_status {
     KDA_ERR_SHAPE = 2,        /* a size is out of range, or K, V are not 128         */
     KDA_ERR_ALIGN = 3,        /* a pointer or stride breaks the alignment rules      */
     KDA_ERR_ALIAS = 4,        /* out or state overlaps another buffer of the call    */
-    KDA_ERR_UNSUPPORTED = 5,  /* unknown flag bits                                   */
+    KDA_ERR_UNSUPPORTED = 5,  /* unknown flag bits, or a mixed gate input form        */
     KDA_ERR_DEVICE = 6,       /* the current device is not gfx950, or a HIP query failed */
     KDA_ERR_LAUNCH = 7        /* the kernel launch failed                            */
 } kda_status;
@@ -90,7 +90,7 @@ typedef enum kda_status {
  * One decode call.  Token t of the call is row t of every per-token tensor.
  *
  *   N          requests in the call (N = 0: nothing to do, returns KDA_OK)
- *   H          q/k heads;  HV value heads, a multiple of H; value head hv
+ *   H          q/k heads;  HV value heads (at most 65535), a multiple of H; value head hv
  *              reads q/k head hv / (HV / H)
  *   K, V       key and value head size; the GPU kernels take K = V = 128
  *   scale      readout scale (1/sqrt(K) in the serving models)
@@ -121,6 +121,22 @@ typedef enum kda_status {
  *   norm_weight bf16 [V] (8-byte aligned), norm_eps > 0 or 0:
  *              out = o / sqrt(mean_j o^2 + eps) * w * silu(z).
  *
+ *   raw_gate   NULL: g and beta are given activated (above).  Otherwise the
+ *              kernel activates them from raw projections itself (FlashInfer
+ *              PR 4562, inline review of the binding: bf16 raw_gate and
+ *              raw_beta, fp32 A_log and dt_bias; the pages do not print the
+ *              activation, the one used is the gate of Kimi Delta Attention):
+ *                g_t[hv][i] = -exp(A_log[hv]) * softplus(raw_gate_t[hv][i] + dt_bias[hv][i])
+ *                beta_t[hv] = sigmoid(raw_beta_t[hv])
+ *              in fp32.  g and beta must then be NULL, and
+ *              raw_gate   bf16, (t, hv, i) at t*raw_gate_stride + hv*K + i;
+ *                         16-byte aligned, raw_gate_stride a multiple of 8, >= HV*K
+ *              raw_beta   bf16, (t, hv) at t*raw_beta_stride + hv; raw_beta_stride >= HV
+ *              A_log      fp32 [HV], 4-byte aligned
+ *              dt_bias    fp32 [HV][K], 16-byte aligned
+ *              are all required.  raw_beta, A_log or dt_bias without
+ *              raw_gate, or g/beta with it, is KDA_ERR_UNSUPPORTED.
+ *
  *   device_status  with KDA_FLAG_VALIDATE, a device int32 the call writes
  *              (4-byte aligned, overlapping no other buffer); else ignored.
  *   inter_state NULL, or the state of each live request's value head right
@@ -133,8 +149,8 @@ typedef enum kda_status {
  *              written.
  *
  * Aliasing: out, state, inter_state and device_status may not overlap each
- * other or any input
- * (q, k, v, g, beta, slot_idx, cu_seqlens, gate, norm_weight); inputs may
+ * other or any input (q, k, v, g, beta, slot_idx, cu_seqlens, gate,
+ * norm_weight, raw_gate, raw_beta, A_log, dt_bias); inputs may
  * overlap each other (q, k, v are often views of one projection).  Ranges are
  * the bounding byte ranges of each strided tensor.
  */
@@ -154,6 +170,10 @@ typedef struct kda_decode_args {
     float norm_eps;
     int32_t *device_status;   /* KDA_FLAG_VALIDATE only: caller-owned device int32 */
     void *inter_state;  int64_t inter_stride;   /* NULL, or per-token states (below) */
+    const void *raw_gate;  int64_t raw_gate_stride;   /* NULL, or the fused gate activation */
+    const void *raw_beta;  int64_t raw_beta_stride;
+    const float *A_log;
+    const float *dt_bias;
 } kda_decode_args;
 
 /*

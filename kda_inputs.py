@@ -273,6 +273,10 @@ WORKLOADS = {
     "n32_t1_h16_norm": dict(cid=3, N=32, H=16, HV=16, num_slots=512, T=1, norm=True),
     # packed varlen: 256 requests, 12 heads, T_i in {1..4}, 26 padding rows, 2048-slot pool
     "packed_n256_h12": dict(cid=4, N=256, H=12, HV=12, num_slots=2048, T=None, n_pad=26),
+    # the dominant shape and the packed batch with the gate activation fused
+    # into the decode: raw projections instead of activated g and beta
+    "n32_t1_h8_rawgate": dict(cid=1, N=32, H=8, HV=8, num_slots=512, T=1, raw_gates=True),
+    "packed_n256_h12_rawgate": dict(cid=4, N=256, H=12, HV=12, num_slots=2048, T=None, n_pad=26, raw_gates=True),
 }
 
 

@@ -70,6 +70,10 @@ class KdaDecodeArgs(ctypes.Structure):
         ("norm_eps", ctypes.c_float),
         ("device_status", ctypes.c_void_p),
         ("inter_state", ctypes.c_void_p), ("inter_stride", ctypes.c_int64),
+        ("raw_gate", ctypes.c_void_p), ("raw_gate_stride", ctypes.c_int64),
+        ("raw_beta", ctypes.c_void_p), ("raw_beta_stride", ctypes.c_int64),
+        ("A_log", ctypes.c_void_p),
+        ("dt_bias", ctypes.c_void_p),
     ]
 
 
@@ -144,30 +148,49 @@ def _state_flag(state: torch.Tensor, flags: int) -> int:
 
 
 def decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate=None, norm_weight=None,
-                eps: float = 1e-6, device_status=None, inter_state=None) -> KdaDecodeArgs:
+                eps: float = 1e-6, device_status=None, inter_state=None, raw_gate=None, raw_beta=None,
+                A_log=None, dt_bias=None) -> KdaDecodeArgs:
     """Marshal tensors into a ``kda_decode_args`` struct (no validation of
-    values; the library validates sizes, alignment and overlap)."""
+    values; the library validates sizes, alignment and overlap).  The gate
+    inputs come either activated (g, beta) or raw (raw_gate, raw_beta, A_log,
+    dt_bias, with g = beta = None): the kernel then activates them."""
     _check(q, "q", torch.bfloat16, 3)
     _check(k, "k", torch.bfloat16, 3)
     _check(v, "v", torch.bfloat16, 3)
-    _check(g, "g", torch.float32, 3)
-    _check(beta, "beta", torch.float32, 2)
     _check(state, "state", state.dtype if state.dtype in (torch.float32, torch.bfloat16) else torch.float32, 4)
     _check(slot_idx, "slot_idx", torch.int32, 1)
     _check(out, "out", torch.bfloat16, 3)
     tokens, H, K = q.shape
     HV, V = v.shape[1], v.shape[2]
-    if k.shape != q.shape or v.shape[0] != tokens or g.shape != (tokens, HV, K) or \
-            beta.shape != (tokens, HV) or out.shape != (tokens, HV, V) or state.shape[1:] != (HV, K, V):
+    if k.shape != q.shape or v.shape[0] != tokens or out.shape != (tokens, HV, V) or state.shape[1:] != (HV, K, V):
         raise ValueError("inconsistent shapes")
+    raw = raw_gate is not None
+    if any((t is not None) != raw for t in (raw_beta, A_log, dt_bias)) or (raw and (g is not None or beta is not None)):
+        raise ValueError("give either g and beta, or raw_gate, raw_beta, A_log and dt_bias")
     a = KdaDecodeArgs()
     a.N, a.H, a.HV, a.K, a.V = slot_idx.shape[0], H, HV, K, V
     a.scale = float(scale)
     a.q, a.q_stride = q.data_ptr(), _lead_stride(q)
     a.k, a.k_stride = k.data_ptr(), _lead_stride(k)
     a.v, a.v_stride = v.data_ptr(), _lead_stride(v)
-    a.g, a.g_stride = g.data_ptr(), _lead_stride(g)
-    a.beta, a.beta_stride = beta.data_ptr(), _lead_stride(beta)
+    if raw:
+        _check(raw_gate, "raw_gate", torch.bfloat16, 3)
+        _check(raw_beta, "raw_beta", torch.bfloat16, 2)
+        _check(A_log, "A_log", torch.float32, 1)
+        _check(dt_bias, "dt_bias", torch.float32, 2)
+        if raw_gate.shape != (tokens, HV, K) or raw_beta.shape != (tokens, HV) or A_log.shape != (HV,) or \
+                dt_bias.shape != (HV, K):
+            raise ValueError("inconsistent raw gate shapes")
+        a.raw_gate, a.raw_gate_stride = raw_gate.data_ptr(), _lead_stride(raw_gate)
+        a.raw_beta, a.raw_beta_stride = raw_beta.data_ptr(), _lead_stride(raw_beta)
+        a.A_log, a.dt_bias = A_log.data_ptr(), dt_bias.data_ptr()
+    else:
+        _check(g, "g", torch.float32, 3)
+        _check(beta, "beta", torch.float32, 2)
+        if g.shape != (tokens, HV, K) or beta.shape != (tokens, HV):
+            raise ValueError("inconsistent shapes")
+        a.g, a.g_stride = g.data_ptr(), _lead_stride(g)
+        a.beta, a.beta_stride = beta.data_ptr(), _lead_stride(beta)
     a.state, a.num_slots, a.slot_stride = state.data_ptr(), state.shape[0], _lead_stride(state)
     a.slot_idx = slot_idx.data_ptr()
     a.out, a.out_stride = out.data_ptr(), _lead_stride(out)
@@ -194,15 +217,19 @@ def decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate=None, norm_w
 
 def kda_decode_step(q, k, v, g, beta, state, slot_idx, out, *, T: int, scale: float,
                     gate=None, norm_weight=None, eps: float = 1e-6, flags: int = 0, stream=None,
-                    device_status=None, inter_state=None):
+                    device_status=None, inter_state=None, raw_gate=None, raw_beta=None, A_log=None,
+                    dt_bias=None):
     """Decode T tokens for each of N requests (tokens request-major, N*T rows);
     updates ``state`` in place and writes ``out`` for live requests.  With
     ``device_status`` (an int32 device tensor of one element) the device
     metadata is validated first, all or nothing (KDA_FLAG_VALIDATE).  With
     ``inter_state`` ([tokens, HV, K, V], the pool's dtype) the state after
-    every token is written too (speculative decoding)."""
+    every token is written too (speculative decoding).  With ``raw_gate``
+    (bf16 [tokens, HV, K]), ``raw_beta`` (bf16 [tokens, HV]), ``A_log`` (fp32
+    [HV]) and ``dt_bias`` (fp32 [HV, K]) instead of g and beta (both None)
+    the kernel activates the gates itself."""
     a = decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate, norm_weight, eps, device_status,
-                    inter_state)
+                    inter_state, raw_gate, raw_beta, A_log, dt_bias)
     if device_status is not None:
         flags = int(flags) | KDA_FLAG_VALIDATE
     if q.shape[0] != a.N * int(T):
@@ -216,12 +243,13 @@ def kda_decode_step(q, k, v, g, beta, state, slot_idx, out, *, T: int, scale: fl
 
 def kda_decode_packed(q, k, v, g, beta, state, slot_idx, cu_seqlens, out, *, scale: float,
                       gate=None, norm_weight=None, eps: float = 1e-6, flags: int = 0, stream=None,
-                      device_status=None, inter_state=None):
+                      device_status=None, inter_state=None, raw_gate=None, raw_beta=None, A_log=None,
+                      dt_bias=None):
     """Packed variable-length decode: request n owns token rows
-    cu_seqlens[n] .. cu_seqlens[n+1]-1.  ``device_status`` and
-    ``inter_state`` as for kda_decode_step."""
+    cu_seqlens[n] .. cu_seqlens[n+1]-1.  ``device_status``, ``inter_state``
+    and the raw gate inputs as for kda_decode_step."""
     a = decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate, norm_weight, eps, device_status,
-                    inter_state)
+                    inter_state, raw_gate, raw_beta, A_log, dt_bias)
     if device_status is not None:
         flags = int(flags) | KDA_FLAG_VALIDATE
     _check(cu_seqlens, "cu_seqlens", torch.int32, 1)

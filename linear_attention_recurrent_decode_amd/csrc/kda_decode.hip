@@ -50,22 +50,31 @@ constexpr int VD = 128;           // value head size handled by the kernels
 constexpr int ROWS_PER_LANE = 16;  // 128 key rows over 8 row groups
 constexpr int MAX_DEVICES = 64;
 
+// Field order matters: what a workgroup needs before its first token's loads
+// (the token inputs and their strides) comes first, so that it arrives in
+// one batch of scalar loads from the kernel arguments.
 struct DecodeParams {
     const uint16_t *q;
     const uint16_t *k;
     const uint16_t *v;
     const float *g;
     const float *beta;
+    const uint16_t *raw_gate;    // fused gate activation (template parameter RAWG)
+    const uint16_t *raw_beta;
+    const float *A_log;
+    const float *dt_bias;
+    int64_t q_stride, k_stride, v_stride, g_stride, beta_stride, raw_gate_stride, raw_beta_stride;
+    int32_t HV, T;
+    uint32_t qk_magic, qk_magic_hi;   // q/k head of value head hv: qk_head(hv)
+    float scale, eps;
     void *state;                 // fp32 or bf16 pool (template parameter BF16S)
     const int32_t *slot_idx;
     const int32_t *cu_seqlens;   // NULL: fixed T tokens per request
     uint16_t *out;
     const uint16_t *gate;
     const uint16_t *norm_weight;
-    int64_t q_stride, k_stride, v_stride, g_stride, beta_stride, out_stride, gate_stride;
+    int64_t out_stride, gate_stride;
     int64_t num_slots, slot_stride;
-    int32_t HV, heads_per_qk, T;
-    float scale, eps;
     int32_t *status;             // KDA_FLAG_VALIDATE: the metadata check's verdict
     void *inter_state;           // NULL, or the state after every token (pool element type)
     int64_t inter_stride;
@@ -95,6 +104,35 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 __device__ __forceinline__ float silu(float z)
 {
     return z / (1.0f + __expf(-z));
+}
+
+// Fused gate activation (FlashInfer PR 4562, inline review of the binding:
+// the kernel takes raw_gate, raw_beta, A_log and dt_bias; the activation is
+// the gate of Kimi Delta Attention):
+//   g = -A softplus(raw + bias),  A = exp(A_log),  beta = sigmoid(raw_beta).
+// softplus is taken as max(x, 0) + log(1 + e^-|x|), which cannot overflow:
+// +inf gives g = -inf (the key row is cleared), -inf gives g = 0.  Both
+// transcendentals are the hardware's base-2 exp and log (one instruction
+// each; the log's argument 1 + e^-|x| lies in [1, 2], where v_log_f32 needs
+// no range handling).  The only loss against log1p is the rounding of
+// 1 + e^-|x|, at most 2^-24 absolute in softplus, so |dg| <= 2^-24 A plus a
+// few ulp of g: a relative change of the decay factor far below the fp32
+// state rounding of a call.  (The library log1pf costs over a hundred
+// instructions here, and 16 of them per lane and token made the one-token
+// decode twice as slow.)  Every body evaluates these two functions on the
+// same fp32 operands, so they agree bit for bit wherever the activation
+// happens.
+__device__ __forceinline__ float gate_log_decay(float raw, float bias, float A)
+{
+    constexpr float LN2 = 0.693147180559945309f;
+    const float x = raw + bias;
+    const float sp = fmaxf(x, 0.0f) + LN2 * __builtin_amdgcn_logf(1.0f + __expf(-fabsf(x)));
+    return -A * sp;
+}
+
+__device__ __forceinline__ float beta_from_raw(float r)
+{
+    return 1.0f / (1.0f + __expf(-r));
 }
 
 // The lane's 16 rows x 4 columns of a state tile in HBM.  fp32 state moves as
@@ -182,7 +220,13 @@ __device__ __forceinline__ float sum_col_groups(float x)
 }
 
 // One token's inputs as a lane needs them: q, k, g over its 16 key rows, v
-// over its 4 value columns, beta of the head.
+// over its 4 value columns, beta of the head.  With the fused gate
+// activation (RAWG) the lane activates only 2 of its row group's 16 key
+// rows (rows row0 + 2 cg and + 1, cg = the lane's column group) and the 8
+// lanes of the row group exchange the results: g0.x carries the two raw bf16
+// values and beta the raw beta's bits (zero-extended by the load; widened
+// where it is used, so that nothing waits for the load before the state
+// tile's loads are issued).
 struct TokenIn {
     uint4 k0, k1, q0, q1;
     float4 g0, g1, g2, g3;
@@ -190,22 +234,67 @@ struct TokenIn {
     float beta;
 };
 
+// What the fused gate activation needs besides the token: A_log of the head
+// and dt_bias of the lane's 2 key rows, loaded once per call.  A = exp(A_log)
+// is evaluated where it is used, so that no load of the state tile waits for
+// A_log to arrive.
+template <bool RAWG>
+struct HeadGate {
+    __device__ __forceinline__ void load(const DecodeParams &, int, int, int) {}
+};
+
+template <>
+struct HeadGate<true> {
+    float2 b;
+    float a_log;
+    __device__ __forceinline__ void load(const DecodeParams &p, int hv, int row0, int cg)
+    {
+        b = reinterpret_cast<const float2 *>(p.dt_bias + (int64_t)hv * KD + row0)[cg];
+        a_log = p.A_log[hv];
+    }
+};
+
+// x of lane 8 (lane / 8) + I: a broadcast within each group of 8 lanes, on
+// the VALU (no LDS-pipe round trip to wait for).  A quad_perm broadcast of
+// lane I % 4 serves the quad that holds lane I; the other quad of the group
+// takes it with a 4-lane row shift whose bank mask writes only that quad
+// (banks are the 4-lane quarters of a 16-lane row).
+template <int I>
+__device__ __forceinline__ float bcast8(float x)
+{
+    static_assert(I >= 0 && I < 8, "lane within a group of 8");
+    constexpr int DPP_ROW_SHL4 = 0x104;   // lane l <- l + 4 within its row
+    constexpr int DPP_ROW_SHR4 = 0x114;   // lane l <- l - 4 within its row
+    const int q = __builtin_amdgcn_update_dpp(0, __float_as_int(x), (I & 3) * 0x55, 0xF, 0xF, false);
+    const int r = I < 4 ? __builtin_amdgcn_update_dpp(q, q, DPP_ROW_SHR4, 0xF, 0xA, false)   // upper quads
+                        : __builtin_amdgcn_update_dpp(q, q, DPP_ROW_SHL4, 0xF, 0x5, false);  // lower quads
+    return __int_as_float(r);
+}
+
+template <bool RAWG>
 __device__ __forceinline__ void load_token(TokenIn &in, const DecodeParams &p, int64_t t, int h, int hv, int row0,
                                            int col)
 {
     const uint4 *kp = reinterpret_cast<const uint4 *>(p.k + t * p.k_stride + h * KD + row0);
     const uint4 *qp = reinterpret_cast<const uint4 *>(p.q + t * p.q_stride + h * KD + row0);
-    const float4 *gp = reinterpret_cast<const float4 *>(p.g + t * p.g_stride + (int64_t)hv * KD + row0);
     in.k0 = kp[0];
     in.k1 = kp[1];
     in.q0 = qp[0];
     in.q1 = qp[1];
-    in.g0 = gp[0];
-    in.g1 = gp[1];
-    in.g2 = gp[2];
-    in.g3 = gp[3];
+    if constexpr (RAWG) {
+        const int cg = (col >> 2) & 7;
+        const uint32_t *rp = reinterpret_cast<const uint32_t *>(p.raw_gate + t * p.raw_gate_stride + (int64_t)hv * KD + row0);
+        in.g0.x = __uint_as_float(rp[cg]);
+        in.beta = __uint_as_float((uint32_t)p.raw_beta[t * p.raw_beta_stride + hv]);
+    } else {
+        const float4 *gp = reinterpret_cast<const float4 *>(p.g + t * p.g_stride + (int64_t)hv * KD + row0);
+        in.g0 = gp[0];
+        in.g1 = gp[1];
+        in.g2 = gp[2];
+        in.g3 = gp[3];
+        in.beta = p.beta[t * p.beta_stride + hv];
+    }
     in.v = *reinterpret_cast<const uint2 *>(p.v + t * p.v_stride + (int64_t)hv * VD + col);
-    in.beta = p.beta[t * p.beta_stride + hv];
 }
 
 // Advance the lane's part of the state by one token and write its output.
@@ -213,17 +302,40 @@ __device__ __forceinline__ void load_token(TokenIn &in, const DecodeParams &p, i
 // contraction), so each inlined copy of this function rounds identically.
 // With PREFETCH the next token's inputs are loaded into `in` as soon as this
 // token's are unpacked, so they are in flight while this token computes.
-template <bool NORM, bool PREFETCH>
+template <bool NORM, bool PREFETCH, bool RAWG>
 __device__ __forceinline__ void advance_token(f32x4 (&s)[ROWS_PER_LANE], TokenIn &in, const DecodeParams &p,
-                                              int64_t t, int64_t eos, int h, int hv, int lane, int wave, int rg,
-                                              int row0, int col, float (&norm_partial)[2][4])
+                                              const HeadGate<RAWG> &hg, int64_t t, int64_t eos, int h, int hv,
+                                              int lane, int wave, int rg, int row0, int col,
+                                              float (&norm_partial)[2][4])
 {
     // unpack; the decay factors a_i = exp(g_i)
-    float kk[ROWS_PER_LANE], qq[ROWS_PER_LANE], a[ROWS_PER_LANE];
+    float kk[ROWS_PER_LANE], qq[ROWS_PER_LANE], a[ROWS_PER_LANE], gg[ROWS_PER_LANE];
     const uint32_t kw[8] = {in.k0.x, in.k0.y, in.k0.z, in.k0.w, in.k1.x, in.k1.y, in.k1.z, in.k1.w};
     const uint32_t qw[8] = {in.q0.x, in.q0.y, in.q0.z, in.q0.w, in.q1.x, in.q1.y, in.q1.z, in.q1.w};
-    const float gg[16] = {in.g0.x, in.g0.y, in.g0.z, in.g0.w, in.g1.x, in.g1.y, in.g1.z, in.g1.w,
-                          in.g2.x, in.g2.y, in.g2.z, in.g2.w, in.g3.x, in.g3.y, in.g3.z, in.g3.w};
+    float b;
+    if constexpr (RAWG) {
+        // this lane's 2 rows, then every row of the row group from its lanes
+        const uint32_t rw = __float_as_uint(in.g0.x);
+        const float A = expf(hg.a_log);
+        const float g_lo = gate_log_decay(bf16_lo(rw), hg.b.x, A);
+        const float g_hi = gate_log_decay(bf16_hi(rw), hg.b.y, A);
+        gg[0] = bcast8<0>(g_lo), gg[1] = bcast8<0>(g_hi);
+        gg[2] = bcast8<1>(g_lo), gg[3] = bcast8<1>(g_hi);
+        gg[4] = bcast8<2>(g_lo), gg[5] = bcast8<2>(g_hi);
+        gg[6] = bcast8<3>(g_lo), gg[7] = bcast8<3>(g_hi);
+        gg[8] = bcast8<4>(g_lo), gg[9] = bcast8<4>(g_hi);
+        gg[10] = bcast8<5>(g_lo), gg[11] = bcast8<5>(g_hi);
+        gg[12] = bcast8<6>(g_lo), gg[13] = bcast8<6>(g_hi);
+        gg[14] = bcast8<7>(g_lo), gg[15] = bcast8<7>(g_hi);
+        b = beta_from_raw(bf16_lo(__float_as_uint(in.beta)));
+    } else {
+        const float g16[16] = {in.g0.x, in.g0.y, in.g0.z, in.g0.w, in.g1.x, in.g1.y, in.g1.z, in.g1.w,
+                               in.g2.x, in.g2.y, in.g2.z, in.g2.w, in.g3.x, in.g3.y, in.g3.z, in.g3.w};
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            gg[i] = g16[i];
+        b = in.beta;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         kk[2 * i] = bf16_lo(kw[i]);
@@ -238,10 +350,9 @@ __device__ __forceinline__ void advance_token(f32x4 (&s)[ROWS_PER_LANE], TokenIn
         kq = fmaf(kk[i], qq[i], kq);
     }
     const float v0 = bf16_lo(in.v.x), v1 = bf16_hi(in.v.x), v2 = bf16_lo(in.v.y), v3 = bf16_hi(in.v.y);
-    const float b = in.beta;
     if constexpr (PREFETCH) {
         if (t + 1 < eos)
-            load_token(in, p, t + 1, h, hv, row0, col);
+            load_token<RAWG>(in, p, t + 1, h, hv, row0, col);
     }
 
     // one pass over the old state: both key-axis partial sums
@@ -329,23 +440,28 @@ struct TokenStage {
 
 // Cooperative global -> LDS copy of tokens t0 .. t0+nt-1 (nt <= STAGE_TOKENS),
 // in two halves so that the state tile's loads can be issued in between: the
-// loads into registers, then (after the tile's loads) the LDS writes.
-template <int NW>
+// loads into registers, then (after the tile's loads) the LDS writes.  With
+// the fused gate activation (RAWG) the raw gate arrives as bf16 pieces of 8
+// key channels with their 8 dt_bias values, and the activation runs once per
+// channel in stage_store, so LDS holds the activated g and beta either way.
+template <int NW, bool RAWG>
 struct StagePieces {
     static constexpr int THREADS = 64 * NW;
-    static constexpr int PIECES = KD / 8 + KD / 8 + KD / 4;   // 16-byte pieces of k, q, g per token
+    static constexpr int G_PIECES = RAWG ? KD / 8 : KD / 4;      // 16-byte pieces of g (or raw gate)
+    static constexpr int PIECES = KD / 8 + KD / 8 + G_PIECES;    // ... of k, q and g per token
     static constexpr int ITER = (STAGE_TOKENS * PIECES + THREADS - 1) / THREADS;
     static constexpr int VITER = (STAGE_TOKENS * NW * 8 + THREADS - 1) / THREADS;
     uint4 kqg[ITER];
+    float4 bias[RAWG ? ITER : 1][2];
     uint2 v[VITER];
     float beta;
 };
 
-template <int NW>
-__device__ __forceinline__ void stage_load(StagePieces<NW> &r, const DecodeParams &p, int64_t t0, int nt, int h,
-                                           int hv, int col0)
+template <int NW, bool RAWG>
+__device__ __forceinline__ void stage_load(StagePieces<NW, RAWG> &r, const DecodeParams &p, int64_t t0, int nt,
+                                           int h, int hv, int col0)
 {
-    using SP = StagePieces<NW>;
+    using SP = StagePieces<NW, RAWG>;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int it = 0; it < SP::ITER; ++it) {
@@ -353,11 +469,23 @@ __device__ __forceinline__ void stage_load(StagePieces<NW> &r, const DecodeParam
         if (idx < nt * SP::PIECES) {
             const int j = idx / SP::PIECES, e = idx - j * SP::PIECES;
             const int64_t t = t0 + j;
+            // one load per piece from a selected address (no divergent branches,
+            // whose loads into one register would have to wait for each other)
+            const uint4 *gsrc =
+                RAWG ? reinterpret_cast<const uint4 *>(p.raw_gate + t * p.raw_gate_stride + (int64_t)hv * KD)
+                     : reinterpret_cast<const uint4 *>(p.g + t * p.g_stride + (int64_t)hv * KD);
             const uint4 *src = e < KD / 8   ? reinterpret_cast<const uint4 *>(p.k + t * p.k_stride + h * KD) + e
                                : e < KD / 4 ? reinterpret_cast<const uint4 *>(p.q + t * p.q_stride + h * KD) + (e - KD / 8)
-                                            : reinterpret_cast<const uint4 *>(p.g + t * p.g_stride + (int64_t)hv * KD) +
-                                                  (e - KD / 4);
+                                            : gsrc + (e - KD / 4);
             r.kqg[it] = *src;
+            if constexpr (RAWG) {
+                // dt_bias of the piece's 8 key channels (k and q pieces read
+                // channels 0..7 and ignore them)
+                const int m = e < KD / 4 ? 0 : e - KD / 4;
+                const float4 *bp = reinterpret_cast<const float4 *>(p.dt_bias + (int64_t)hv * KD) + 2 * m;
+                r.bias[it][0] = bp[0];
+                r.bias[it][1] = bp[1];
+            }
         }
     }
 #pragma unroll
@@ -368,26 +496,40 @@ __device__ __forceinline__ void stage_load(StagePieces<NW> &r, const DecodeParam
             r.v[it] = reinterpret_cast<const uint2 *>(p.v + (t0 + j) * p.v_stride + (int64_t)hv * VD + col0)[e];
         }
     }
-    if (tid < nt)
-        r.beta = p.beta[(t0 + tid) * p.beta_stride + hv];
+    if (tid < nt) {
+        if constexpr (RAWG)   // the bits: widened in stage_store, after the tile's loads are issued
+            r.beta = __uint_as_float((uint32_t)p.raw_beta[(t0 + tid) * p.raw_beta_stride + hv]);
+        else
+            r.beta = p.beta[(t0 + tid) * p.beta_stride + hv];
+    }
 }
 
-template <int NW>
-__device__ __forceinline__ void stage_store(TokenStage<NW> &st, const StagePieces<NW> &r, int nt)
+template <int NW, bool RAWG>
+__device__ __forceinline__ void stage_store(TokenStage<NW> &st, const StagePieces<NW, RAWG> &r, int nt, float A)
 {
-    using SP = StagePieces<NW>;
+    using SP = StagePieces<NW, RAWG>;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int it = 0; it < SP::ITER; ++it) {
         const int idx = tid + it * SP::THREADS;
         if (idx < nt * SP::PIECES) {
             const int j = idx / SP::PIECES, e = idx - j * SP::PIECES;
-            if (e < KD / 8)
+            if (e < KD / 8) {
                 st.k[j][e] = r.kqg[it];
-            else if (e < KD / 4)
+            } else if (e < KD / 4) {
                 st.q[j][e - KD / 8] = r.kqg[it];
-            else
+            } else if constexpr (RAWG) {
+                const int m = e - KD / 4;
+                const uint4 w = r.kqg[it];
+                const float4 b0 = r.bias[it][0], b1 = r.bias[it][1];
+                st.g[j][2 * m] = float4{gate_log_decay(bf16_lo(w.x), b0.x, A), gate_log_decay(bf16_hi(w.x), b0.y, A),
+                                        gate_log_decay(bf16_lo(w.y), b0.z, A), gate_log_decay(bf16_hi(w.y), b0.w, A)};
+                st.g[j][2 * m + 1] =
+                    float4{gate_log_decay(bf16_lo(w.z), b1.x, A), gate_log_decay(bf16_hi(w.z), b1.y, A),
+                           gate_log_decay(bf16_lo(w.w), b1.z, A), gate_log_decay(bf16_hi(w.w), b1.w, A)};
+            } else {
                 st.g[j][e - KD / 4] = __builtin_bit_cast(float4, r.kqg[it]);
+            }
         }
     }
 #pragma unroll
@@ -399,7 +541,7 @@ __device__ __forceinline__ void stage_store(TokenStage<NW> &st, const StagePiece
         }
     }
     if (tid < nt)
-        st.beta[tid] = r.beta;
+        st.beta[tid] = RAWG ? beta_from_raw(bf16_lo(__float_as_uint(r.beta))) : r.beta;
 }
 
 __device__ __forceinline__ void read_staged(TokenIn &in, const uint4 (&k)[KD / 8], const uint4 (&q)[KD / 8],
@@ -417,15 +559,27 @@ __device__ __forceinline__ void read_staged(TokenIn &in, const uint4 (&k)[KD / 8
     in.beta = beta;
 }
 
+// hv / (HV / H), the q/k head that value head hv reads, as a multiply by
+// m = floor(2^32 / d) + 1 (d = HV / H; m = m_lo + 2^32 m_hi): for n d < 2^32,
+// floor(n m / 2^32) = floor(n / d) (the error term n (d - 2^32 mod d) / 2^32
+// stays below 1 - (n mod d) / d).  The host checks HV < 65536, so n < HV and
+// d <= HV keep n d < 2^32.  A scalar division would cost some thirty
+// dependent instructions at the start of every workgroup.
+__device__ __forceinline__ int qk_head(const DecodeParams &p, int hv)
+{
+    return (int)(__umulhi((uint32_t)hv, p.qk_magic) + (uint32_t)hv * p.qk_magic_hi);
+}
+
 // Three bodies share advance_token and round identically:
 //   BODY_LOOP: the token loop prefetches token t+1 while token t computes;
 //     the first token's inputs go out just before the state tile.  Fastest
-//     for one token per request from one tile per compute unit up.
+//     for one token per request from two tiles per compute unit up.
 //   BODY_PEELED: the first token is peeled off the loop and the tile's loads
 //     are issued around the first token's input loads (4 rows, the inputs,
 //     12 rows), pinned by scheduling fences; later tokens load at the top of
 //     their iteration.  Fastest for step calls with several tokens per
-//     request and for launches below one tile per compute unit.
+//     request, for launches below two tiles per compute unit and with the
+//     fused gate activation.
 //   BODY_STAGED: the workgroup copies the inputs of up to STAGE_TOKENS tokens
 //     into LDS while the tile is in flight, so the token loop reads no global
 //     memory.  Fastest for packed batches of mixed lengths.
@@ -436,7 +590,7 @@ constexpr int BODY_LOOP = 0, BODY_PEELED = 1, BODY_STAGED = 2;
 // with kernarg preloading, so they arrive in SGPRs at wave launch and the slot
 // index load issues without waiting for a kernel-argument fetch.  The rest
 // travels in DecodeParams.
-template <int NW, bool NORM, int BODY, bool BF16S>
+template <int NW, bool NORM, int BODY, bool BF16S, bool RAWG>
 __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot_idx, const int32_t *cu_seqlens,
                                                              void *state, int64_t slot_stride, int64_t num_slots,
                                                              int32_t HV, int32_t T, const int32_t *status,
@@ -471,7 +625,7 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot
     }
     if (eos <= bos)
         return;
-    const int h = hv / p.heads_per_qk;
+    const int h = qk_head(p, hv);
 
     const int cg = lane & 7;              // column group: 4 columns
     const int rg = lane >> 3;             // row group: 16 key rows
@@ -496,58 +650,66 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot
 
     if constexpr (BODY == BODY_LOOP) {
         // first token's inputs, then the whole tile
-        load_token(in, p, bos, h, hv, row0, col);
+        HeadGate<RAWG> hg;
+        hg.load(p, hv, row0, cg);
+        load_token<RAWG>(in, p, bos, h, hv, row0, col);
 #pragma unroll
         for (int i = 0; i < ROWS_PER_LANE; ++i)
             s[i] = tile.load(i);
         for (int64_t t = bos; t < eos; ++t) {
-            advance_token<NORM, true>(s, in, p, t, eos, h, hv, lane, wave, rg, row0, col, norm_partial);
+            advance_token<NORM, true, RAWG>(s, in, p, hg, t, eos, h, hv, lane, wave, rg, row0, col, norm_partial);
             keep_state(t);
         }
     } else if constexpr (BODY == BODY_PEELED) {
         constexpr int FIRST_ROWS = 4;
+        HeadGate<RAWG> hg;
 #pragma unroll
         for (int i = 0; i < FIRST_ROWS; ++i)
             s[i] = tile.load(i);
         __builtin_amdgcn_sched_barrier(0);
-        load_token(in, p, bos, h, hv, row0, col);
+        hg.load(p, hv, row0, cg);
+        load_token<RAWG>(in, p, bos, h, hv, row0, col);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = FIRST_ROWS; i < ROWS_PER_LANE; ++i)
             s[i] = tile.load(i);
         // all 16 loads of the tile are in flight before any math starts
         __builtin_amdgcn_sched_barrier(0);
-        advance_token<NORM, false>(s, in, p, bos, eos, h, hv, lane, wave, rg, row0, col, norm_partial);
+        advance_token<NORM, false, RAWG>(s, in, p, hg, bos, eos, h, hv, lane, wave, rg, row0, col, norm_partial);
         keep_state(bos);
         for (int64_t t = bos + 1; t < eos; ++t) {
-            load_token(in, p, t, h, hv, row0, col);
-            advance_token<NORM, false>(s, in, p, t, eos, h, hv, lane, wave, rg, row0, col, norm_partial);
+            load_token<RAWG>(in, p, t, h, hv, row0, col);
+            advance_token<NORM, false, RAWG>(s, in, p, hg, t, eos, h, hv, lane, wave, rg, row0, col, norm_partial);
             keep_state(t);
         }
     } else {
+        // LDS holds activated g and beta in both gate forms
         __shared__ TokenStage<NW> st;
+        const HeadGate<false> no_gate;
         const int col0 = vt * NW * 32;     // first column of the workgroup's tile
         int nt = (int)min<int64_t>(eos - bos, STAGE_TOKENS);
-        StagePieces<NW> pieces;
-        stage_load<NW>(pieces, p, bos, nt, h, hv, col0);
+        const float a_log = RAWG ? p.A_log[hv] : 0.0f;
+        StagePieces<NW, RAWG> pieces;
+        stage_load<NW, RAWG>(pieces, p, bos, nt, h, hv, col0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < ROWS_PER_LANE; ++i)
             s[i] = tile.load(i);
         __builtin_amdgcn_sched_barrier(0);
-        stage_store<NW>(st, pieces, nt);   // waits for the inputs only, not the tile
+        const float A = RAWG ? expf(a_log) : 0.0f;
+        stage_store<NW, RAWG>(st, pieces, nt, A);   // waits for the inputs only, not the tile
         for (int64_t t0 = bos; t0 < eos; t0 += STAGE_TOKENS) {
             if (t0 != bos) {
                 __syncthreads();           // every wave is done with the previous chunk
                 nt = (int)min<int64_t>(eos - t0, STAGE_TOKENS);
-                stage_load<NW>(pieces, p, t0, nt, h, hv, col0);
-                stage_store<NW>(st, pieces, nt);
+                stage_load<NW, RAWG>(pieces, p, t0, nt, h, hv, col0);
+                stage_store<NW, RAWG>(st, pieces, nt, A);
             }
             __syncthreads();
             for (int j = 0; j < nt; ++j) {
                 read_staged(in, st.k[j], st.q[j], st.g[j], st.v[j][wave * 8 + cg], st.beta[j], rg);
-                advance_token<NORM, false>(s, in, p, t0 + j, eos, h, hv, lane, wave, rg, row0, col,
-                                           norm_partial);
+                advance_token<NORM, false, false>(s, in, p, no_gate, t0 + j, eos, h, hv, lane, wave, rg, row0, col,
+                                                  norm_partial);
                 keep_state(t0 + j);
             }
         }
@@ -709,14 +871,20 @@ kda_status validate(const kda_decode_args *a, int64_t tokens, const int32_t *cu_
     if (flags & ~(KDA_FLAG_VTILE_MASK | KDA_FLAG_STATE_BF16 | KDA_FLAG_VALIDATE))
         return KDA_ERR_UNSUPPORTED;
     const int64_t state_elem = (flags & KDA_FLAG_STATE_BF16) ? 2 : 4;
-    if (a->N < 0 || a->H < 1 || a->HV < 1 || a->HV % a->H != 0 || tokens < 0)
+    if (a->N < 0 || a->H < 1 || a->HV < 1 || a->HV > 65535 || a->HV % a->H != 0 || tokens < 0)
         return KDA_ERR_SHAPE;
     if (a->K != KD || a->V != VD)
         return KDA_ERR_SHAPE;
+    // the gate inputs come in one form: activated (g, beta) or raw
+    const bool raw = a->raw_gate != nullptr;
+    if (raw ? (a->g || a->beta) : (a->raw_beta || a->A_log || a->dt_bias))
+        return KDA_ERR_UNSUPPORTED;
     if (a->N == 0)
         return KDA_OK;
     // per-token tensors may be NULL only when the call holds no token rows
-    if (tokens > 0 && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->out))
+    if (tokens > 0 && (!a->q || !a->k || !a->v || !a->out || (!raw && (!a->g || !a->beta))))
+        return KDA_ERR_NULL;
+    if (raw && (!a->raw_beta || !a->A_log || !a->dt_bias))
         return KDA_ERR_NULL;
     if (!a->state || !a->slot_idx)
         return KDA_ERR_NULL;
@@ -725,14 +893,20 @@ kda_status validate(const kda_decode_args *a, int64_t tokens, const int32_t *cu_
     const int64_t hk = (int64_t)a->H * a->K, hvk = (int64_t)a->HV * a->K, hvv = (int64_t)a->HV * a->V;
     if (a->num_slots < 0 || a->slot_stride < hvk * a->V)
         return KDA_ERR_SHAPE;
-    if (a->q_stride < hk || a->k_stride < hk || a->v_stride < hvv || a->g_stride < hvk ||
-        a->beta_stride < a->HV || a->out_stride < hvv || (a->gate && a->gate_stride < hvv))
+    if (a->q_stride < hk || a->k_stride < hk || a->v_stride < hvv || a->out_stride < hvv ||
+        (a->gate && a->gate_stride < hvv))
+        return KDA_ERR_SHAPE;
+    if (raw ? (a->raw_gate_stride < hvk || a->raw_beta_stride < a->HV)
+            : (a->g_stride < hvk || a->beta_stride < a->HV))
         return KDA_ERR_SHAPE;
     if (!(a->norm_eps >= 0.0f))
         return KDA_ERR_SHAPE;
     if (!aligned(a->q, 16) || !aligned(a->k, 16) || a->q_stride % 8 || a->k_stride % 8 ||
-        !aligned(a->v, 8) || a->v_stride % 4 || !aligned(a->g, 16) || a->g_stride % 4 ||
-        !aligned(a->beta, 4) || !aligned(a->state, 4 * state_elem) || a->slot_stride % 4 ||
+        !aligned(a->v, 8) || a->v_stride % 4 ||
+        (raw ? (!aligned(a->raw_gate, 16) || a->raw_gate_stride % 8 || !aligned(a->raw_beta, 2) ||
+                !aligned(a->A_log, 4) || !aligned(a->dt_bias, 16))
+             : (!aligned(a->g, 16) || a->g_stride % 4 || !aligned(a->beta, 4))) ||
+        !aligned(a->state, 4 * state_elem) || a->slot_stride % 4 ||
         !aligned(a->out, 8) || a->out_stride % 4 || !aligned(a->slot_idx, 4) ||
         (cu_seqlens && !aligned(cu_seqlens, 4)) ||
         (a->gate && (!aligned(a->gate, 8) || a->gate_stride % 4 || !aligned(a->norm_weight, 8))))
@@ -750,6 +924,10 @@ kda_status validate(const kda_decode_args *a, int64_t tokens, const int32_t *cu_
         span(cu_seqlens, 1, 0, (int64_t)a->N + 1, 4),
         span(a->gate, tokens, a->gate_stride, hvv, 2),
         span(a->norm_weight, 1, 0, a->V, 2),
+        span(a->raw_gate, tokens, a->raw_gate_stride, hvk, 2),
+        span(a->raw_beta, tokens, a->raw_beta_stride, a->HV, 2),
+        span(a->A_log, 1, 0, a->HV, 4),
+        span(a->dt_bias, 1, 0, hvk, 4),
     };
     if (overlaps(out, state))
         return KDA_ERR_ALIAS;
@@ -802,7 +980,7 @@ int32_t plan_vtile(int64_t units, int32_t T, bool norm)
     return 128;
 }
 
-template <int NW, bool NORM, bool BF16S>
+template <int NW, bool NORM, bool BF16S, bool RAWG>
 kda_status launch_decode(const DecodeParams &p, int64_t units, int body, hipStream_t stream)
 {
     const int64_t blocks = units * (4 / NW);
@@ -816,23 +994,31 @@ kda_status launch_decode(const DecodeParams &p, int64_t units, int body, hipStre
     void *args[] = {&slot_idx, &cu_seqlens, &state, &slot_stride, &num_slots, &HV, &T, &status,
                     const_cast<DecodeParams *>(&p)};
     const void *fn =
-        body == BODY_STAGED   ? reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_STAGED, BF16S>)
-        : body == BODY_PEELED ? reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_PEELED, BF16S>)
-                              : reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_LOOP, BF16S>);
+        body == BODY_STAGED   ? reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_STAGED, BF16S, RAWG>)
+        : body == BODY_PEELED ? reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_PEELED, BF16S, RAWG>)
+                              : reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_LOOP, BF16S, RAWG>);
     const hipError_t e = hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(64 * NW), args, 0, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
-template <bool BF16S>
+template <bool BF16S, bool RAWG>
 kda_status dispatch_width(const DecodeParams &p, int64_t units, int body, bool norm, int vtile, hipStream_t s)
 {
     if (norm)
-        return launch_decode<4, true, BF16S>(p, units, body, s);
+        return launch_decode<4, true, BF16S, RAWG>(p, units, body, s);
     switch (vtile) {
-    case 32: return launch_decode<1, false, BF16S>(p, units, body, s);
-    case 64: return launch_decode<2, false, BF16S>(p, units, body, s);
-    default: return launch_decode<4, false, BF16S>(p, units, body, s);
+    case 32: return launch_decode<1, false, BF16S, RAWG>(p, units, body, s);
+    case 64: return launch_decode<2, false, BF16S, RAWG>(p, units, body, s);
+    default: return launch_decode<4, false, BF16S, RAWG>(p, units, body, s);
     }
+}
+
+template <bool BF16S>
+kda_status dispatch_gate(const DecodeParams &p, int64_t units, int body, bool norm, int vtile, hipStream_t s)
+{
+    if (p.raw_gate)
+        return dispatch_width<BF16S, true>(p, units, body, norm, vtile, s);
+    return dispatch_width<BF16S, false>(p, units, body, norm, vtile, s);
 }
 
 kda_status run_decode(const kda_decode_args *a, int32_t T, const int32_t *cu_seqlens, int64_t tokens,
@@ -878,13 +1064,21 @@ kda_status run_decode(const kda_decode_args *a, int32_t T, const int32_t *cu_seq
     p.num_slots = a->num_slots;
     p.slot_stride = a->slot_stride;
     p.HV = a->HV;
-    p.heads_per_qk = a->HV / a->H;
     p.T = T;
+    const uint64_t qk_magic = (uint64_t(1) << 32) / (uint64_t)(a->HV / a->H) + 1;
+    p.qk_magic = (uint32_t)qk_magic;
+    p.qk_magic_hi = (uint32_t)(qk_magic >> 32);
     p.scale = a->scale;
     p.eps = a->norm_eps;
     p.status = nullptr;
     p.inter_state = a->inter_state;
     p.inter_stride = a->inter_stride;
+    p.raw_gate = static_cast<const uint16_t *>(a->raw_gate);
+    p.raw_beta = static_cast<const uint16_t *>(a->raw_beta);
+    p.A_log = a->A_log;
+    p.dt_bias = a->dt_bias;
+    p.raw_gate_stride = a->raw_gate_stride;
+    p.raw_beta_stride = a->raw_beta_stride;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (flags & KDA_FLAG_VALIDATE) {
@@ -899,13 +1093,15 @@ kda_status run_decode(const kda_decode_args *a, int32_t T, const int32_t *cu_seq
             return KDA_ERR_LAUNCH;
     }
     // packed batches: the staged body; step calls with several tokens per
-    // request or fewer tiles than compute units: the peeled body; otherwise
-    // the prefetching loop (all measured on MI355X, cold caches)
+    // request, fewer than 512 tiles (two per compute unit) or the fused gate
+    // activation: the peeled body (its straight-line first token also lets
+    // the activation run while the tile is in flight); otherwise the
+    // prefetching loop (all measured on MI355X, cold caches)
     const int body = cu_seqlens != nullptr ? BODY_STAGED
-                     : (T > 1 || units < 256) ? BODY_PEELED : BODY_LOOP;
+                     : (T > 1 || units < 512 || a->raw_gate) ? BODY_PEELED : BODY_LOOP;
     if (flags & KDA_FLAG_STATE_BF16)
-        return dispatch_width<true>(p, units, body, norm, vtile, s);
-    return dispatch_width<false>(p, units, body, norm, vtile, s);
+        return dispatch_gate<true>(p, units, body, norm, vtile, s);
+    return dispatch_gate<false>(p, units, body, norm, vtile, s);
 }
 
 }  // namespace

@@ -54,8 +54,8 @@ class DeviceProblem:
     q: torch.Tensor
     k: torch.Tensor
     v: torch.Tensor
-    g: torch.Tensor
-    beta: torch.Tensor
+    g: torch.Tensor | None
+    beta: torch.Tensor | None
     state: torch.Tensor
     slot_idx: torch.Tensor
     cu_seqlens: torch.Tensor
@@ -63,6 +63,17 @@ class DeviceProblem:
     gate: torch.Tensor | None
     norm_weight: torch.Tensor | None
     live_slots: np.ndarray        # the pool slots of live requests, in request order
+    raw_gate: torch.Tensor | None = None
+    raw_beta: torch.Tensor | None = None
+    A_log: torch.Tensor | None = None
+    dt_bias: torch.Tensor | None = None
+
+    def gate_kwargs(self) -> dict:
+        """The raw gate inputs as keyword arguments of the binding (empty for
+        activated problems)."""
+        if self.raw_gate is None:
+            return {}
+        return dict(raw_gate=self.raw_gate, raw_beta=self.raw_beta, A_log=self.A_log, dt_bias=self.dt_bias)
 
 
 def upload(p: ki.Problem, background_seed: int = 1234, state_dtype=torch.float32) -> DeviceProblem:
@@ -85,14 +96,18 @@ def upload(p: ki.Problem, background_seed: int = 1234, state_dtype=torch.float32
         state[torch.from_numpy(live_slots).to(DEV)] = live_t
     out = torch.empty((p.tokens, p.HV, p.V), device=DEV, dtype=torch.int16).fill_(
         np.int16(np.uint16(SENTINEL_BITS).view(np.int16))).view(torch.bfloat16)
+    raw = {}
+    if p.raw:
+        raw = dict(raw_gate=bf16_tensor(p.raw_gate), raw_beta=bf16_tensor(p.raw_beta), A_log=f32_tensor(p.A_log),
+                   dt_bias=f32_tensor(p.dt_bias))
     return DeviceProblem(
-        p=p, q=bf16_tensor(p.q), k=bf16_tensor(p.k), v=bf16_tensor(p.v), g=f32_tensor(p.g),
-        beta=f32_tensor(p.beta), state=state,
+        p=p, q=bf16_tensor(p.q), k=bf16_tensor(p.k), v=bf16_tensor(p.v),
+        g=None if p.g is None else f32_tensor(p.g), beta=None if p.beta is None else f32_tensor(p.beta), state=state,
         slot_idx=torch.from_numpy(p.slot_idx.astype(np.int32)).to(DEV),
         cu_seqlens=torch.from_numpy(p.cu_seqlens.astype(np.int32)).to(DEV), out=out,
         gate=None if p.gate is None else bf16_tensor(p.gate),
         norm_weight=None if p.norm_weight is None else bf16_tensor(p.norm_weight),
-        live_slots=live_slots)
+        live_slots=live_slots, **raw)
 
 
 def run_gpu(d: DeviceProblem, packed: bool | None = None, flags: int = 0, stream=None, device_status=None,
@@ -101,7 +116,7 @@ def run_gpu(d: DeviceProblem, packed: bool | None = None, flags: int = 0, stream
     if packed is None:
         packed = p.T is None
     kw = dict(scale=p.scale, gate=d.gate, norm_weight=d.norm_weight, eps=p.eps, flags=flags, stream=stream,
-              device_status=device_status, inter_state=inter_state)
+              device_status=device_status, inter_state=inter_state, **d.gate_kwargs())
     if packed:
         kda.kda_decode_packed(d.q, d.k, d.v, d.g, d.beta, d.state, d.slot_idx, d.cu_seqlens, d.out, **kw)
     else:
@@ -124,6 +139,8 @@ def run_oracle(p: ki.Problem, state_bf16: bool = False, inter_state=None):
     kw = {}
     if p.gate is not None:
         kw = dict(gate=p.gate, norm_weight=p.norm_weight, eps=p.eps)
+    if p.raw:
+        kw.update(raw_gate=p.raw_gate, raw_beta=p.raw_beta, A_log=p.A_log, dt_bias=p.dt_bias)
     out = oracle.decode_packed(p.q, p.k, p.v, p.g, p.beta, pool, remap, p.cu_seqlens, p.scale,
                                inter_state=inter_state, **kw)
     return out, pool

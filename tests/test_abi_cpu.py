@@ -113,7 +113,7 @@ def test_null_pointers():
 
 
 def test_shapes():
-    for field, value in (("K", 64), ("V", 256), ("H", 3), ("HV", 0), ("N", -1), ("num_slots", -1),
+    for field, value in (("K", 64), ("V", 256), ("H", 3), ("HV", 0), ("HV", 65536), ("N", -1), ("num_slots", -1),
                          ("slot_stride", 4 * 128 * 128 - 4), ("q_stride", 128), ("out_stride", 4),
                          ("beta_stride", 3), ("norm_eps", -1.0), ("norm_eps", float("nan"))):
         a, _ = _valid_args()
@@ -190,6 +190,59 @@ def test_intermediate_state_buffer():
     a, _ = _valid_args()
     a.inter_state, a.inter_stride = a.g, 4 * 128 * 128
     assert _step(a) == ALIAS
+
+
+def _raw_args():
+    """Valid fake arguments with the raw gate form (g and beta cleared)."""
+    a, spare = _valid_args()
+    a.raw_gate, a.raw_gate_stride = a.g, 4 * 128          # reuse g's region (bf16 needs less)
+    a.raw_beta, a.raw_beta_stride = a.beta, 4
+    a.A_log = spare
+    a.dt_bias = spare + 4096
+    a.g = a.beta = 0
+    return a
+
+
+def test_raw_gate_form():
+    a = _raw_args()
+    assert _step(a) == DEVICE                              # passes host validation
+    for f in ("raw_beta", "A_log", "dt_bias"):
+        a = _raw_args()
+        setattr(a, f, 0)
+        assert _step(a) == NULL, f
+    # mixed forms
+    a = _raw_args()
+    a.g = BASE + 50 * (1 << 26)
+    assert _step(a) == UNSUP
+    a = _raw_args()
+    a.beta = BASE + 50 * (1 << 26)
+    assert _step(a) == UNSUP
+    a, spare = _valid_args()
+    a.A_log = spare                                        # activated form plus a raw field
+    assert _step(a) == UNSUP
+    # strides and alignment
+    for field, value, status in (("raw_gate_stride", 4 * 128 - 8, SHAPE), ("raw_beta_stride", 3, SHAPE),
+                                 ("raw_gate_stride", 4 * 128 + 4, ALIGN)):
+        a = _raw_args()
+        setattr(a, field, value)
+        assert _step(a) == status, field
+    for field, offset in (("raw_gate", 8), ("raw_beta", 1), ("A_log", 2), ("dt_bias", 8)):
+        a = _raw_args()
+        setattr(a, field, getattr(a, field) + offset)
+        assert _step(a) == ALIGN, field
+    # written buffers may not overlap the raw inputs
+    a = _raw_args()
+    a.out = a.dt_bias + 1024
+    assert _step(a) == ALIAS
+    a = _raw_args()
+    a.state = a.A_log
+    assert _step(a) == ALIAS
+    # no requests: nothing is read, every pointer may be NULL
+    a = _raw_args()
+    a.N = 0
+    a.q = a.k = a.v = a.out = a.raw_gate = 0
+    a.raw_beta = a.A_log = a.dt_bias = 0
+    assert _step(a) == 0
 
 
 def test_aliasing():

@@ -152,6 +152,96 @@ def test_intermediate_states(name, dtype):
     _log(f"inter {name} {dtype}: max|d| {err.max():.3e}", "")
 
 
+# ------------------------------------------------------- fused gate activation
+RAW_SMALL = SMALL + [(16, 8, 8, 1, 40, 0, False)]   # 128 tiles, one token: the peeled body
+
+
+@pytest.mark.parametrize("case", RAW_SMALL)
+def test_fused_gate_small_cases(case):
+    N, H, HV, T, slots, n_pad, norm = case
+    p = ki.make_problem("raw", 91 + N, N=N, H=H, HV=HV, K=128, V=128, num_slots=slots, T=T, n_pad=n_pad,
+                        norm=norm, raw_gates=True)
+    _log(f"raw gate {case}", parity(p))
+
+
+@pytest.mark.parametrize("name,dtype", [("n32_t1_h8_rawgate", torch.bfloat16), ("n8_t4_h8", torch.float32),
+                                        ("n32_t1_h16_norm", torch.float32), ("n32_t1_h16_norm", torch.bfloat16)])
+def test_fused_gate_workload_variants(name, dtype):
+    if name.endswith("_rawgate"):
+        p = ki.workload(name)
+    else:
+        spec = dict(ki.WORKLOADS[name])
+        spec.pop("cid")
+        p = ki.make_problem(name, 123, K=128, V=128, raw_gates=True, **spec)
+    _log(f"{name} raw gate {dtype}", parity(p, state_dtype=dtype))
+
+
+def _run_fresh(p, **kw):
+    d = _fresh(p)
+    run_gpu(d, **kw)
+    torch.cuda.synchronize()
+    return d.out.view(torch.int16).clone(), d.state.clone()
+
+
+def test_fused_gate_bodies_bit_identical():
+    """The per-lane activation (loop and peeled bodies) and the cooperative
+    one (staged body, packed calls) round identically."""
+    for name, kw in (("loop", dict(N=32, HV=8, H=8, T=1, num_slots=64)),      # 256 tiles, T = 1
+                     ("peeled", dict(N=16, HV=8, H=8, T=1, num_slots=64)),    # 128 tiles
+                     ("peeled T=3", dict(N=9, HV=4, H=2, T=3, num_slots=16))):
+        p = ki.make_problem("raw", 5, K=128, V=128, raw_gates=True, **kw)
+        o1, s1 = _run_fresh(p, packed=False)
+        o2, s2 = _run_fresh(p, packed=True)
+        assert torch.equal(o1, o2) and torch.equal(s1, s2), name
+    p = ki.make_problem("raw", 6, N=32, H=8, HV=8, K=128, V=128, num_slots=64, T=1, raw_gates=True)
+    ref = _run_fresh(p)
+    for width in (32, 64, 128):
+        o, st = _run_fresh(p, flags=kda.KDA_FLAG_VTILE(width))
+        assert torch.equal(o, ref[0]) and torch.equal(st, ref[1]), width
+
+
+@pytest.mark.parametrize("N,T,packed", [(32, 1, False), (16, 1, False), (9, 3, False), (9, 3, True)])
+def test_fused_gate_exact_values_equal_activated_call(N, T, packed):
+    """Raw values whose activation is exact in fp32 (raw gate +inf or -inf:
+    g = -inf or 0; raw beta 0, +inf, -inf: beta = 1/2, 1, 0) decode bit for
+    bit like the activated call, in every body."""
+    p = ki.make_problem("exact", 17, N=N, H=4, HV=8, K=128, V=128, num_slots=2 * N, T=T, raw_gates=True)
+    pick = ki.draws(17, 50, np.arange(p.tokens * p.HV * p.K, dtype=np.uint64)).reshape(p.tokens, p.HV, p.K)
+    clear = (pick % np.uint64(4)) == 0
+    p.raw_gate[...] = np.where(clear, ki.to_bf16_bits(np.inf), ki.to_bf16_bits(-np.inf))
+    choice = (ki.draws(17, 51, np.arange(p.tokens * p.HV, dtype=np.uint64)) % np.uint64(3)).astype(np.int64)
+    choice = choice.reshape(p.tokens, p.HV)
+    p.raw_beta[...] = ki.to_bf16_bits(np.choose(choice, [0.0, np.inf, -np.inf]))
+    raw_out, raw_state = _run_fresh(p, packed=packed)
+    act = ki.make_problem("exact", 17, N=N, H=4, HV=8, K=128, V=128, num_slots=2 * N, T=T)
+    act.g[...] = np.where(clear, -np.inf, 0.0).astype(np.float32)
+    act.beta[...] = np.choose(choice, [0.5, 1.0, 0.0]).astype(np.float32)
+    act_out, act_state = _run_fresh(act, packed=packed)
+    assert torch.equal(raw_out, act_out) and torch.equal(raw_state, act_state)
+    # and both agree with the oracle
+    d = _fresh(p)
+    run_gpu(d, packed=packed)
+    torch.cuda.synchronize()
+    compare(d, *run_oracle(p))
+
+
+def test_fused_gate_intermediate_states():
+    p = ki.make_problem("ps", 62, N=40, H=4, HV=4, K=128, V=128, num_slots=64, T=None, t_max=6, n_pad=5,
+                        raw_gates=True)
+    d = upload(p)
+    inter = torch.full((p.tokens, p.HV, p.K, p.V), 1232.0, device=DEV)
+    run_gpu(d, inter_state=inter)
+    torch.cuda.synchronize()
+    ref_inter = np.full((p.tokens, p.HV, p.K, p.V), np.nan)
+    ref_out, ref_state = run_oracle(p, inter_state=ref_inter)
+    compare(d, ref_out, ref_state)
+    live_rows = np.isfinite(ref_inter[:, 0, 0, 0])
+    got = inter.cpu().numpy().astype(np.float64)
+    err = np.abs(got[live_rows] - ref_inter[live_rows])
+    assert np.all(err <= 1e-4 * np.abs(ref_inter[live_rows]) + 1e-6)
+    assert np.all(got[~live_rows] == 1232.0)
+
+
 # ------------------------------------------------------- transactional validation
 def _status_word():
     return torch.full((1,), -7, dtype=torch.int32, device=DEV)
