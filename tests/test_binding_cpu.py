@@ -1,0 +1,111 @@
+"""The Python binding's argument marshalling (no library call, no device):
+which gate-input forms it accepts, the shapes and dtypes it insists on, and
+the strides and pointers it writes into kda_decode_args."""
+import pytest
+import torch
+
+import linear_attention_recurrent_decode_amd as kda
+
+T, H, HV, K, V, SLOTS = 3, 2, 4, 128, 128, 5
+
+
+def _tensors():
+    bf = torch.bfloat16
+    return dict(
+        q=torch.zeros((T, H, K), dtype=bf), k=torch.zeros((T, H, K), dtype=bf), v=torch.zeros((T, HV, V), dtype=bf),
+        g=torch.zeros((T, HV, K)), beta=torch.zeros((T, HV)),
+        state=torch.zeros((SLOTS, HV, K, V)), slot_idx=torch.zeros(T, dtype=torch.int32),
+        out=torch.zeros((T, HV, V), dtype=bf),
+        raw_gate=torch.zeros((T, HV, K), dtype=bf), raw_beta=torch.zeros((T, HV), dtype=bf),
+        A_log=torch.zeros(HV), dt_bias=torch.zeros((HV, K)))
+
+
+def _args(t, **kw):
+    base = dict(q=t["q"], k=t["k"], v=t["v"], g=t["g"], beta=t["beta"], state=t["state"], slot_idx=t["slot_idx"],
+                out=t["out"], scale=0.088)
+    base.update(kw)
+    return kda.decode_args(**base)
+
+
+def test_activated_form():
+    t = _tensors()
+    a = _args(t)
+    assert a.g == t["g"].data_ptr() and a.beta == t["beta"].data_ptr()
+    assert not a.raw_gate and not a.raw_beta and not a.A_log and not a.dt_bias
+    assert (a.g_stride, a.beta_stride, a.q_stride, a.slot_stride) == (HV * K, HV, H * K, HV * K * V)
+
+
+def test_raw_form():
+    t = _tensors()
+    a = _args(t, g=None, beta=None, raw_gate=t["raw_gate"], raw_beta=t["raw_beta"], A_log=t["A_log"],
+              dt_bias=t["dt_bias"])
+    assert not a.g and not a.beta
+    assert a.raw_gate == t["raw_gate"].data_ptr() and a.raw_beta == t["raw_beta"].data_ptr()
+    assert a.A_log == t["A_log"].data_ptr() and a.dt_bias == t["dt_bias"].data_ptr()
+    assert (a.raw_gate_stride, a.raw_beta_stride) == (HV * K, HV)
+
+
+def test_raw_form_strided_rows():
+    t = _tensors()
+    wide = torch.zeros((T, HV * K + 64), dtype=torch.bfloat16)
+    a = _args(t, g=None, beta=None, raw_gate=wide[:, :HV * K].view(T, HV, K), raw_beta=wide[:, -HV:],
+              A_log=t["A_log"], dt_bias=t["dt_bias"])
+    assert a.raw_gate_stride == HV * K + 64 and a.raw_beta_stride == HV * K + 64
+
+
+@pytest.mark.parametrize("drop", ["raw_beta", "A_log", "dt_bias"])
+def test_raw_form_is_all_or_nothing(drop):
+    t = _tensors()
+    kw = dict(g=None, beta=None, raw_gate=t["raw_gate"], raw_beta=t["raw_beta"], A_log=t["A_log"],
+              dt_bias=t["dt_bias"])
+    kw[drop] = None
+    with pytest.raises(ValueError):
+        _args(t, **kw)
+
+
+def test_forms_do_not_mix():
+    t = _tensors()
+    with pytest.raises(ValueError):
+        _args(t, raw_gate=t["raw_gate"], raw_beta=t["raw_beta"], A_log=t["A_log"], dt_bias=t["dt_bias"])
+    with pytest.raises(ValueError):
+        _args(t, A_log=t["A_log"])
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("raw_gate", torch.zeros((T, HV, K))),                              # fp32, not bf16
+    ("raw_beta", torch.zeros((T, HV))),
+    ("A_log", torch.zeros(HV, dtype=torch.bfloat16)),
+    ("dt_bias", torch.zeros((HV, K), dtype=torch.bfloat16)),
+])
+def test_raw_dtypes(name, bad):
+    t = _tensors()
+    kw = dict(g=None, beta=None, raw_gate=t["raw_gate"], raw_beta=t["raw_beta"], A_log=t["A_log"],
+              dt_bias=t["dt_bias"])
+    kw[name] = bad
+    with pytest.raises(TypeError):
+        _args(t, **kw)
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("raw_gate", torch.zeros((T, HV, K // 2), dtype=torch.bfloat16)),
+    ("raw_beta", torch.zeros((T, HV + 1), dtype=torch.bfloat16)),
+    ("A_log", torch.zeros(HV + 1)),
+    ("dt_bias", torch.zeros((HV, K + 1))),
+])
+def test_raw_shapes(name, bad):
+    t = _tensors()
+    kw = dict(g=None, beta=None, raw_gate=t["raw_gate"], raw_beta=t["raw_beta"], A_log=t["A_log"],
+              dt_bias=t["dt_bias"])
+    kw[name] = bad
+    with pytest.raises(ValueError):
+        _args(t, **kw)
+
+
+def test_intermediate_state_shape_and_dtype():
+    t = _tensors()
+    a = _args(t, inter_state=torch.zeros((T, HV, K, V)))
+    assert a.inter_stride == HV * K * V
+    with pytest.raises(ValueError):
+        _args(t, inter_state=torch.zeros((T + 1, HV, K, V)))
+    with pytest.raises(TypeError):
+        _args(t, inter_state=torch.zeros((T, HV, K, V), dtype=torch.bfloat16))   # must match the pool

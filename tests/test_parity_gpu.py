@@ -242,6 +242,68 @@ def test_fused_gate_intermediate_states():
     assert np.all(got[~live_rows] == 1232.0)
 
 
+def test_fused_gate_strided_fused_projection():
+    """raw_gate and raw_beta as row-strided column blocks of one bf16
+    projection (with q, k, v), as a serving model's fused input projection
+    would hand them over."""
+    p = ki.make_problem("rawfused", 12, N=6, H=2, HV=4, K=128, V=128, num_slots=9, T=2, raw_gates=True)
+    d = upload(p)
+    T, HK, HVV, HVK = p.tokens, p.H * p.K, p.HV * p.V, p.HV * p.K
+    o_gate = 2 * HK + HVV
+    o_beta = o_gate + HVK + 8
+    width = (o_beta + p.HV + 7) // 8 * 8 + 8            # a multiple of 8: 16-byte rows for q, k and raw_gate
+    fused = torch.zeros((T, width), dtype=torch.bfloat16, device=DEV)
+    fused[:, :HK] = d.q.reshape(T, HK)
+    fused[:, HK:2 * HK] = d.k.reshape(T, HK)
+    fused[:, 2 * HK:2 * HK + HVV] = d.v.reshape(T, HVV)
+    fused[:, o_gate:o_gate + HVK] = d.raw_gate.reshape(T, HVK)
+    fused[:, o_beta:o_beta + p.HV] = d.raw_beta
+    d.q = fused[:, :HK].view(T, p.H, p.K)
+    d.k = fused[:, HK:2 * HK].view(T, p.H, p.K)
+    d.v = fused[:, 2 * HK:2 * HK + HVV].view(T, p.HV, p.V)
+    d.raw_gate = fused[:, o_gate:o_gate + HVK].view(T, p.HV, p.K)
+    d.raw_beta = fused[:, o_beta:o_beta + p.HV]
+    assert d.raw_gate.stride(0) == width and d.raw_beta.stride(0) == width
+    for packed in (False, True):
+        d2 = upload(p)
+        d2.q, d2.k, d2.v, d2.raw_gate, d2.raw_beta = d.q, d.k, d.v, d.raw_gate, d.raw_beta
+        run_gpu(d2, packed=packed)
+        torch.cuda.synchronize()
+        compare(d2, *run_oracle(p))
+
+
+def test_fused_gate_graph_validate_and_stream():
+    """The fused gate inside a HIP graph (replayed with eager work between),
+    with device-side validation, on a non-default stream: bit for bit the
+    eager call on the default stream."""
+    p = ki.make_problem("rawgraph", 13, N=24, H=4, HV=8, K=128, V=128, num_slots=40, T=None, n_pad=3,
+                        raw_gates=True)
+    eager = _fresh(p)
+    run_gpu(eager)
+    torch.cuda.synchronize()
+    d = _fresh(p)
+    init = d.state.clone()
+    status = _status_word()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            run_gpu(d, device_status=status, stream=s)
+    torch.cuda.synchronize()
+    live_rows = torch.from_numpy(np.isfinite(run_oracle(p)[0][:, 0, 0])).to(DEV)
+    for _ in range(3):
+        d.state.copy_(init)                  # eager work between replays
+        d.out.view(torch.int16).fill_(0)
+        status.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0       # KDA_DEVICE_OK
+        assert torch.equal(d.state, eager.state)
+        assert torch.equal(d.out.view(torch.int16)[live_rows], eager.out.view(torch.int16)[live_rows])
+
+
 # ------------------------------------------------------- transactional validation
 def _status_word():
     return torch.full((1,), -7, dtype=torch.int32, device=DEV)
