@@ -582,7 +582,9 @@ __device__ __forceinline__ int qk_head(const DecodeParams &p, int hv)
 //     fused gate activation.
 //   BODY_STAGED: the workgroup copies the inputs of up to STAGE_TOKENS tokens
 //     into LDS while the tile is in flight, so the token loop reads no global
-//     memory.  Fastest for packed batches of mixed lengths.
+//     memory (longer requests restage in chunks; with a bf16 pool they load
+//     the remaining tokens directly).  Fastest for packed batches of mixed
+//     lengths.
 constexpr int BODY_LOOP = 0, BODY_PEELED = 1, BODY_STAGED = 2;
 
 // The scalars on the critical path (slot lookup -> tile address, and the
@@ -698,19 +700,45 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot
         __builtin_amdgcn_sched_barrier(0);
         const float A = RAWG ? expf(a_log) : 0.0f;
         stage_store<NW, RAWG>(st, pieces, nt, A);   // waits for the inputs only, not the tile
-        for (int64_t t0 = bos; t0 < eos; t0 += STAGE_TOKENS) {
-            if (t0 != bos) {
-                __syncthreads();           // every wave is done with the previous chunk
-                nt = (int)min<int64_t>(eos - t0, STAGE_TOKENS);
-                stage_load<NW, RAWG>(pieces, p, t0, nt, h, hv, col0);
-                stage_store<NW, RAWG>(st, pieces, nt, A);
-            }
+        if constexpr (BF16S) {
+            // bf16 pool: tokens past the first chunk load their inputs directly
+            // (requests that long are rare).  Without the restaging loop the
+            // kernel fits in 168 VGPRs, three waves per SIMD, which the
+            // half-size tiles need to keep enough bytes in flight (53.0 vs
+            // 55.6 us on the packed H12 batch; the fp32 pool streams best at
+            // two waves per SIMD, 69.8 vs 72.5 us the other way round).
             __syncthreads();
             for (int j = 0; j < nt; ++j) {
                 read_staged(in, st.k[j], st.q[j], st.g[j], st.v[j][wave * 8 + cg], st.beta[j], rg);
-                advance_token<NORM, false, false>(s, in, p, no_gate, t0 + j, eos, h, hv, lane, wave, rg, row0, col,
+                advance_token<NORM, false, false>(s, in, p, no_gate, bos + j, eos, h, hv, lane, wave, rg, row0, col,
                                                   norm_partial);
-                keep_state(t0 + j);
+                keep_state(bos + j);
+            }
+            if (bos + STAGE_TOKENS < eos) {
+                HeadGate<RAWG> hg;
+                hg.load(p, hv, row0, cg);
+                for (int64_t t = bos + STAGE_TOKENS; t < eos; ++t) {
+                    load_token<RAWG>(in, p, t, h, hv, row0, col);
+                    advance_token<NORM, false, RAWG>(s, in, p, hg, t, eos, h, hv, lane, wave, rg, row0, col,
+                                                     norm_partial);
+                    keep_state(t);
+                }
+            }
+        } else {
+            for (int64_t t0 = bos; t0 < eos; t0 += STAGE_TOKENS) {
+                if (t0 != bos) {
+                    __syncthreads();           // every wave is done with the previous chunk
+                    nt = (int)min<int64_t>(eos - t0, STAGE_TOKENS);
+                    stage_load<NW, RAWG>(pieces, p, t0, nt, h, hv, col0);
+                    stage_store<NW, RAWG>(st, pieces, nt, A);
+                }
+                __syncthreads();
+                for (int j = 0; j < nt; ++j) {
+                    read_staged(in, st.k[j], st.q[j], st.g[j], st.v[j][wave * 8 + cg], st.beta[j], rg);
+                    advance_token<NORM, false, false>(s, in, p, no_gate, t0 + j, eos, h, hv, lane, wave, rg, row0,
+                                                      col, norm_partial);
+                    keep_state(t0 + j);
+                }
             }
         }
     }

@@ -55,13 +55,38 @@ def test_small_cases(case):
     _log(f"small {case}", parity(p))
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("t_max", [6, 9])
-def test_packed_long_requests(t_max):
-    """Requests longer than one staging chunk of tokens (up to 9 tokens)."""
+def test_packed_long_requests(t_max, dtype):
+    """Requests longer than one staging chunk of tokens (up to 9 tokens):
+    restaged with an fp32 pool, loaded token by token with a bf16 pool."""
     p = ki.make_problem("long", 40 + t_max, N=24, H=4, HV=8, K=128, V=128, num_slots=40, T=None,
                         t_max=t_max, n_pad=3)
     assert np.diff(p.cu_seqlens).max() > 4
-    _log(f"packed t_max={t_max}", parity(p))
+    _log(f"packed t_max={t_max} {dtype}", parity(p, state_dtype=dtype))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_packed_long_requests_fused_gate(dtype):
+    p = ki.make_problem("longraw", 49, N=24, H=4, HV=8, K=128, V=128, num_slots=40, T=None, t_max=9, n_pad=3,
+                        raw_gates=True)
+    assert np.diff(p.cu_seqlens).max() > 4
+    _log(f"packed raw t_max=9 {dtype}", parity(p, state_dtype=dtype))
+
+
+def test_packed_long_requests_match_step_bitwise():
+    """A uniform packed call with 6 tokens per request (past one staging
+    chunk) gives the step call's bits, fp32 and bf16 pool."""
+    p = ki.make_problem("long6", 50, N=12, H=2, HV=4, K=128, V=128, num_slots=20, T=6)
+    for dtype in (torch.float32, torch.bfloat16):
+        a = upload(p, state_dtype=dtype)
+        run_gpu(a, packed=False)
+        b = upload(p, state_dtype=dtype)
+        run_gpu(b, packed=True)
+        torch.cuda.synchronize()
+        assert torch.equal(a.state.view(torch.int16) if dtype == torch.bfloat16 else a.state,
+                           b.state.view(torch.int16) if dtype == torch.bfloat16 else b.state), dtype
+        assert torch.equal(a.out.view(torch.int16), b.out.view(torch.int16)), dtype
 
 
 def test_step_six_tokens():
