@@ -573,13 +573,14 @@ __device__ __forceinline__ int qk_head(const DecodeParams &p, int hv)
 // Three bodies share advance_token and round identically:
 //   BODY_LOOP: the token loop prefetches token t+1 while token t computes;
 //     the first token's inputs go out just before the state tile.  Fastest
-//     for one token per request from two tiles per compute unit up.
+//     for one token per request from two tiles per compute unit up with an
+//     fp32 pool.
 //   BODY_PEELED: the first token is peeled off the loop and the tile's loads
 //     are issued around the first token's input loads (4 rows, the inputs,
 //     12 rows), pinned by scheduling fences; later tokens load at the top of
 //     their iteration.  Fastest for step calls with several tokens per
-//     request, for launches below two tiles per compute unit and with the
-//     fused gate activation.
+//     request, for launches below two tiles per compute unit, with the fused
+//     gate activation and with a bf16 pool.
 //   BODY_STAGED: the workgroup copies the inputs of up to STAGE_TOKENS tokens
 //     into LDS while the tile is in flight, so the token loop reads no global
 //     memory (longer requests restage in chunks; with a bf16 pool they load
@@ -1121,12 +1122,15 @@ kda_status run_decode(const kda_decode_args *a, int32_t T, const int32_t *cu_seq
             return KDA_ERR_LAUNCH;
     }
     // packed batches: the staged body; step calls with several tokens per
-    // request, fewer than 512 tiles (two per compute unit) or the fused gate
-    // activation: the peeled body (its straight-line first token also lets
-    // the activation run while the tile is in flight); otherwise the
-    // prefetching loop (all measured on MI355X, cold caches)
+    // request, fewer than 512 tiles (two per compute unit), the fused gate
+    // activation or a bf16 pool: the peeled body (its straight-line first
+    // token also lets the activation run while the tile is in flight, and at
+    // 144 VGPRs it runs three waves per SIMD, which the half-size bf16 tiles
+    // need); otherwise the prefetching loop (all measured on MI355X, cold
+    // caches)
+    const bool bf16_pool = (flags & KDA_FLAG_STATE_BF16) != 0;
     const int body = cu_seqlens != nullptr ? BODY_STAGED
-                     : (T > 1 || units < 512 || a->raw_gate) ? BODY_PEELED : BODY_LOOP;
+                     : (T > 1 || units < 512 || a->raw_gate || bf16_pool) ? BODY_PEELED : BODY_LOOP;
     if (flags & KDA_FLAG_STATE_BF16)
         return dispatch_gate<true>(p, units, body, norm, vtile, s);
     return dispatch_gate<false>(p, units, body, norm, vtile, s);

@@ -94,6 +94,22 @@ def test_step_six_tokens():
     _log("step T=6", parity(p))
 
 
+@pytest.mark.parametrize("N", [64, 128])
+def test_loop_body_shapes(N):
+    """One token per request from 512 tiles up with an fp32 pool takes the
+    prefetching loop body (64- and 128-column tiles): parity with the oracle,
+    and bit for bit the staged body of the packed call over the same tokens."""
+    p = ki.make_problem("loop", 60 + N, N=N, H=8, HV=8, K=128, V=128, num_slots=2 * N + 8, T=1)
+    assert kda.kda_decode_plan(N * 8, 1, False) == (64 if N * 8 < 1024 else 128)
+    _log(f"loop body N={N}", parity(p))
+    a = _fresh(p)
+    run_gpu(a, packed=False)
+    b = _fresh(p)
+    run_gpu(b, packed=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a.state, b.state) and torch.equal(a.out.view(torch.int16), b.out.view(torch.int16))
+
+
 def test_packed_and_step_bodies_bit_identical():
     """A uniform packed call and the step call over the same tokens give the
     same bits (different kernel bodies, same arithmetic)."""
