@@ -1022,10 +1022,15 @@ kda_status launch_decode(const DecodeParams &p, int64_t units, int body, hipStre
     const int32_t *status = p.status;
     void *args[] = {&slot_idx, &cu_seqlens, &state, &slot_stride, &num_slots, &HV, &T, &status,
                     const_cast<DecodeParams *>(&p)};
-    const void *fn =
-        body == BODY_STAGED   ? reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_STAGED, BF16S, RAWG>)
-        : body == BODY_PEELED ? reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_PEELED, BF16S, RAWG>)
-                              : reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_LOOP, BF16S, RAWG>);
+    // the loop body serves only fp32 pools with activated gates (run_decode's
+    // plan); it is not instantiated for the other forms
+    const void *fn = body == BODY_STAGED
+                         ? reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_STAGED, BF16S, RAWG>)
+                         : reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_PEELED, BF16S, RAWG>);
+    if constexpr (!BF16S && !RAWG) {
+        if (body == BODY_LOOP)
+            fn = reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_LOOP, BF16S, RAWG>);
+    }
     const hipError_t e = hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(64 * NW), args, 0, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
