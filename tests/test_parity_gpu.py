@@ -345,6 +345,80 @@ def test_fused_gate_graph_validate_and_stream():
         assert torch.equal(d.out.view(torch.int16)[live_rows], eager.out.view(torch.int16)[live_rows])
 
 
+# ------------------------------------------------------- seeded random configurations
+def _random_case(i):
+    """A seeded draw over the option space: request count, head counts and
+    ratio, step or packed lengths, padding, norm, raw gates, pool dtype,
+    per-token states, forced tile width."""
+    d = ki.draws(0x5EED, 70 + i, np.arange(16, dtype=np.uint64))
+    pick = lambda j, n: int(d[j] % np.uint64(n))
+    H = 1 + pick(0, 4)
+    HV = H * (1 + pick(1, 3))
+    N = 1 + pick(2, 40)
+    packed = pick(3, 2) == 1
+    T = None if packed else 1 + pick(4, 5)
+    n_pad = min(pick(5, 4), N - 1) if N > 1 else 0
+    norm = pick(6, 3) == 0
+    raw = pick(7, 2) == 1
+    bf16 = pick(8, 2) == 1
+    inter = pick(9, 3) == 0
+    width = [0, 32, 64, 128][pick(10, 4)] if not norm else 0
+    return dict(N=N, H=H, HV=HV, T=T, t_max=1 + pick(11, 6), n_pad=n_pad, norm=norm, raw=raw, bf16=bf16,
+                inter=inter, width=width)
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_configurations(i):
+    c = _random_case(i)
+    p = ki.make_problem("rand", 900 + i, N=c["N"], H=c["H"], HV=c["HV"], K=128, V=128, num_slots=c["N"] + 7,
+                        T=c["T"], t_max=c["t_max"], n_pad=c["n_pad"], norm=c["norm"], raw_gates=c["raw"])
+    dtype = torch.bfloat16 if c["bf16"] else torch.float32
+    flags = kda.KDA_FLAG_VTILE(c["width"]) if c["width"] else 0
+    print(f"[parity] random case {i}: {c}", flush=True)
+    d = upload(p, state_dtype=dtype)
+    before = d.state.clone()
+    inter = None
+    if c["inter"]:
+        inter = torch.full((p.tokens, p.HV, p.K, p.V), 1232.0, dtype=dtype, device=DEV)
+    run_gpu(d, flags=flags, inter_state=inter)
+    torch.cuda.synchronize()
+    ref_inter = np.full((p.tokens, p.HV, p.K, p.V), np.nan) if c["inter"] else None
+    ref_out, ref_state = run_oracle(p, state_bf16=c["bf16"], inter_state=ref_inter)
+    compare(d, ref_out, ref_state)
+    untouched = torch.ones(p.num_slots, dtype=torch.bool, device=DEV)
+    if len(d.live_slots):
+        untouched[torch.from_numpy(d.live_slots).to(DEV)] = False
+    assert torch.equal(d.state[untouched], before[untouched])
+    if c["inter"]:
+        got = inter.float().cpu().numpy().astype(np.float64)
+        rows = np.isfinite(ref_inter[:, 0, 0, 0])
+        tol = (2.0 ** -8 if c["bf16"] else 1e-4) * np.abs(ref_inter[rows]) + 1e-6
+        assert np.all(np.abs(got[rows] - ref_inter[rows]) <= tol)
+        assert np.all(got[~rows] == 1232.0)
+
+
+def test_concurrent_streams_on_disjoint_slots():
+    """Two halves of a batch on two streams at once give the bits of one
+    call over the whole batch (every (request, head) is independent)."""
+    p = ki.make_problem("streams", 31, N=40, H=4, HV=8, K=128, V=128, num_slots=64, T=2)
+    whole = _fresh(p)
+    run_gpu(whole)
+    torch.cuda.synchronize()
+    d = _fresh(p)
+    half = p.N // 2
+    rows = half * p.T
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    for lo, s in ((0, s1), (half, s2)):
+        r = slice(lo * p.T, lo * p.T + rows)
+        kda.kda_decode_step(d.q[r], d.k[r], d.v[r], d.g[r], d.beta[r], d.state, d.slot_idx[lo:lo + half], d.out[r],
+                            T=p.T, scale=p.scale, stream=s)
+    torch.cuda.synchronize()
+    assert torch.equal(d.state, whole.state)
+    assert torch.equal(d.out.view(torch.int16), whole.out.view(torch.int16))
+
+
 # ------------------------------------------------------- transactional validation
 def _status_word():
     return torch.full((1,), -7, dtype=torch.int32, device=DEV)
