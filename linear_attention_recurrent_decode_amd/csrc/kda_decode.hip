@@ -29,10 +29,16 @@
 //   S'_ij = a_i S_ij + k_i v'_j
 // so both key-axis reductions come from one pass over the old state, and the
 // only cross-lane step per token is one 3-level reduction (DPP and permlane
-// swaps, no LDS) over the 8 lanes that share a column group.  The gated RMSNorm epilogue (b12x PR 249,
-// walkthrough: normalise and gate the decoded output) needs the sum of o^2
-// over all 128 columns, which forces the 4-wave tile and adds one LDS
-// exchange per token.
+// swaps, no LDS) over the 8 lanes that share a column group.  The gated
+// RMSNorm epilogue (b12x PR 249, walkthrough: normalise and gate the decoded
+// output) needs the sum of o^2 over all 128 columns, which forces the 4-wave
+// tile and adds one LDS exchange per token.
+//
+// Options of the same kernels: a bf16 state pool (widened exactly on load,
+// rounded once on write-back), the gate activation fused from raw
+// projections (FlashInfer PR 4562's binding passes raw_gate, raw_beta, A_log
+// and dt_bias), the state after every token for speculative decoding, and a
+// one-workgroup metadata check that makes a call all or nothing.
 
 #include <hip/hip_runtime.h>
 
@@ -117,11 +123,10 @@ __device__ __forceinline__ float silu(float z)
 // no range handling).  The only loss against log1p is the rounding of
 // 1 + e^-|x|, at most 2^-24 absolute in softplus, so |dg| <= 2^-24 A plus a
 // few ulp of g: a relative change of the decay factor far below the fp32
-// state rounding of a call.  (The library log1pf costs over a hundred
-// instructions here, and 16 of them per lane and token made the one-token
-// decode twice as slow.)  Every body evaluates these two functions on the
-// same fp32 operands, so they agree bit for bit wherever the activation
-// happens.
+// state rounding of a call.  (The device library's log1pf expands to over a
+// hundred instructions, f64 steps included.)  Every body evaluates these two
+// functions on the same fp32 operands, so they agree bit for bit wherever
+// the activation happens.
 __device__ __forceinline__ float gate_log_decay(float raw, float bias, float A)
 {
     constexpr float LN2 = 0.693147180559945309f;
