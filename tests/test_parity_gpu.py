@@ -7,7 +7,8 @@ import torch
 
 import kda_inputs as ki
 import linear_attention_recurrent_decode_amd as kda
-from kda_harness import (DEV, bf16_tensor, compare, f32_tensor, parity, run_gpu, run_oracle, upload)
+import oracle
+from kda_harness import (DEV, bf16_tensor, bf16_to_f64, compare, f32_tensor, parity, run_gpu, run_oracle, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -343,6 +344,45 @@ def test_fused_gate_graph_validate_and_stream():
         assert int(status.item()) == 0       # KDA_DEVICE_OK
         assert torch.equal(d.state, eager.state)
         assert torch.equal(d.out.view(torch.int16)[live_rows], eager.out.view(torch.int16)[live_rows])
+
+
+# ------------------------------------------------------- a large batch, sampled
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_large_batch_sampled(dtype):
+    """2048 requests x 16 value heads (32768 tiles of 128 columns) in a
+    2112-slot pool (2.1 GiB fp32): the oracle checks a seeded sample of 24
+    requests (outputs and final states); the 64 slots no request owns stay
+    bitwise untouched.  The pool is drawn on the device, the sampled slots
+    are copied back for the oracle."""
+    N, H, HV, slots = 2048, 16, 16, 2112
+    p = ki.make_problem("large", 77, N=N, H=H, HV=HV, K=128, V=128, num_slots=slots, T=1)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(4321)
+    state = (torch.randn((slots, HV, 128, 128), generator=gen, device=DEV) * 0.05).to(dtype)
+    before = state.clone()
+    out = torch.empty((N, HV, 128), dtype=torch.bfloat16, device=DEV)
+    kda.kda_decode_step(bf16_tensor(p.q), bf16_tensor(p.k), bf16_tensor(p.v), f32_tensor(p.g), f32_tensor(p.beta),
+                        state, torch.from_numpy(p.slot_idx).to(DEV), out, T=1, scale=p.scale)
+    torch.cuda.synchronize()
+    sample = np.sort(ki.permutation(77, 5, N)[:24])
+    sslots = p.slot_idx[sample].astype(np.int64)
+    pool = before[torch.from_numpy(sslots).to(DEV)].float().cpu().numpy().astype(np.float64)
+    ref_out = oracle.decode_step(p.q[sample], p.k[sample], p.v[sample], p.g[sample], p.beta[sample], pool,
+                                 np.arange(len(sample), dtype=np.int32), 1, p.scale)
+    got_out = bf16_to_f64(out[torch.from_numpy(sample).to(DEV)])
+    err = np.abs(got_out - ref_out)
+    assert np.all(err <= 2e-3 + 2.0 ** -8 * np.abs(ref_out)), err.max()
+    got_state = state[torch.from_numpy(sslots).to(DEV)].float().cpu().numpy().astype(np.float64)
+    serr = np.abs(got_state - pool)
+    if dtype == torch.bfloat16:
+        assert np.all(serr <= 2.0 ** -8 * np.abs(pool) + 1e-6), serr.max()
+    else:
+        assert np.all(serr <= 1e-4 * np.abs(pool) + 1e-6), serr.max()
+    spare = np.setdiff1d(np.arange(slots), p.slot_idx)
+    assert len(spare) == 64
+    idx = torch.from_numpy(spare).to(DEV)
+    assert torch.equal(state[idx], before[idx])
+    _log(f"large batch {dtype}", f"out max|d| {err.max():.3e}, state max|d| {serr.max():.3e}")
 
 
 # ------------------------------------------------------- seeded random configurations
