@@ -433,6 +433,13 @@ __device__ __forceinline__ void advance_token(f32x4 (&s)[ROWS_PER_LANE], TokenIn
 // the workgroup's columns, beta.
 constexpr int STAGE_TOKENS = 4;
 
+// Tokens of the next chunk to stage: min(remaining, STAGE_TOKENS), in integers
+// (the device library's 64-bit min goes through doubles).
+__device__ __forceinline__ int chunk_tokens(int64_t remaining)
+{
+    return remaining < STAGE_TOKENS ? (int)remaining : STAGE_TOKENS;
+}
+
 template <int NW>
 struct TokenStage {
     uint4 k[STAGE_TOKENS][KD / 8];
@@ -694,7 +701,7 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot
         __shared__ TokenStage<NW> st;
         const HeadGate<false> no_gate;
         const int col0 = vt * NW * 32;     // first column of the workgroup's tile
-        int nt = (int)min<int64_t>(eos - bos, STAGE_TOKENS);
+        int nt = chunk_tokens(eos - bos);
         const float a_log = RAWG ? p.A_log[hv] : 0.0f;
         StagePieces<NW, RAWG> pieces;
         stage_load<NW, RAWG>(pieces, p, bos, nt, h, hv, col0);
@@ -733,7 +740,7 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot
             for (int64_t t0 = bos; t0 < eos; t0 += STAGE_TOKENS) {
                 if (t0 != bos) {
                     __syncthreads();           // every wave is done with the previous chunk
-                    nt = (int)min<int64_t>(eos - t0, STAGE_TOKENS);
+                    nt = chunk_tokens(eos - t0);
                     stage_load<NW, RAWG>(pieces, p, t0, nt, h, hv, col0);
                     stage_store<NW, RAWG>(st, pieces, nt, A);
                 }
