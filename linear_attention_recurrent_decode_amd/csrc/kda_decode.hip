@@ -223,17 +223,18 @@ __device__ __forceinline__ float sum_col_groups(float x)
     return x;
 }
 
-// One token's inputs as a lane needs them: q, k, g over its 16 key rows, v
-// over its 4 value columns, beta of the head.  With the fused gate
-// activation (RAWG) the lane activates only 2 of its row group's 16 key
-// rows (rows row0 + 2 cg and + 1, cg = the lane's column group) and the 8
-// lanes of the row group exchange the results: g0.x carries the two raw bf16
-// values and beta the raw beta's bits (zero-extended by the load; widened
-// where it is used, so that nothing waits for the load before the state
-// tile's loads are issued).
+// One token's inputs as a lane needs them: q, k over its 16 key rows, v over
+// its 4 value columns, beta of the head, and g of only 2 of its 16 key rows
+// (rows row0 + 2 cg and + 1, cg = the lane's column group): each lane takes
+// the exponential of its 2 rows and the 8 lanes of the row group exchange
+// the decay factors (bcast8), instead of all 8 computing all 16.  With the
+// fused gate activation (RAWG) g.x carries the 2 rows' raw bf16 values, which
+// the lane activates first, and beta the raw beta's bits (zero-extended by
+// the load; widened where it is used, so that nothing waits for the load
+// before the state tile's loads are issued).
 struct TokenIn {
     uint4 k0, k1, q0, q1;
-    float4 g0, g1, g2, g3;
+    float2 g;
     uint2 v;
     float beta;
 };
@@ -285,17 +286,13 @@ __device__ __forceinline__ void load_token(TokenIn &in, const DecodeParams &p, i
     in.k1 = kp[1];
     in.q0 = qp[0];
     in.q1 = qp[1];
+    const int cg = (col >> 2) & 7;
     if constexpr (RAWG) {
-        const int cg = (col >> 2) & 7;
         const uint32_t *rp = reinterpret_cast<const uint32_t *>(p.raw_gate + t * p.raw_gate_stride + (int64_t)hv * KD + row0);
-        in.g0.x = __uint_as_float(rp[cg]);
+        in.g.x = __uint_as_float(rp[cg]);
         in.beta = __uint_as_float((uint32_t)p.raw_beta[t * p.raw_beta_stride + hv]);
     } else {
-        const float4 *gp = reinterpret_cast<const float4 *>(p.g + t * p.g_stride + (int64_t)hv * KD + row0);
-        in.g0 = gp[0];
-        in.g1 = gp[1];
-        in.g2 = gp[2];
-        in.g3 = gp[3];
+        in.g = reinterpret_cast<const float2 *>(p.g + t * p.g_stride + (int64_t)hv * KD + row0)[cg];
         in.beta = p.beta[t * p.beta_stride + hv];
     }
     in.v = *reinterpret_cast<const uint2 *>(p.v + t * p.v_stride + (int64_t)hv * VD + col);
@@ -312,34 +309,32 @@ __device__ __forceinline__ void advance_token(f32x4 (&s)[ROWS_PER_LANE], TokenIn
                                               int lane, int wave, int rg, int row0, int col,
                                               float (&norm_partial)[2][4])
 {
-    // unpack; the decay factors a_i = exp(g_i)
-    float kk[ROWS_PER_LANE], qq[ROWS_PER_LANE], a[ROWS_PER_LANE], gg[ROWS_PER_LANE];
+    // unpack; the decay factors a_i = exp(g_i): this lane's 2 rows, then all
+    // 16 rows of the row group from its 8 lanes
+    float kk[ROWS_PER_LANE], qq[ROWS_PER_LANE], a[ROWS_PER_LANE];
     const uint32_t kw[8] = {in.k0.x, in.k0.y, in.k0.z, in.k0.w, in.k1.x, in.k1.y, in.k1.z, in.k1.w};
     const uint32_t qw[8] = {in.q0.x, in.q0.y, in.q0.z, in.q0.w, in.q1.x, in.q1.y, in.q1.z, in.q1.w};
-    float b;
+    float b, g_lo, g_hi;
     if constexpr (RAWG) {
-        // this lane's 2 rows, then every row of the row group from its lanes
-        const uint32_t rw = __float_as_uint(in.g0.x);
+        const uint32_t rw = __float_as_uint(in.g.x);
         const float A = expf(hg.a_log);
-        const float g_lo = gate_log_decay(bf16_lo(rw), hg.b.x, A);
-        const float g_hi = gate_log_decay(bf16_hi(rw), hg.b.y, A);
-        gg[0] = bcast8<0>(g_lo), gg[1] = bcast8<0>(g_hi);
-        gg[2] = bcast8<1>(g_lo), gg[3] = bcast8<1>(g_hi);
-        gg[4] = bcast8<2>(g_lo), gg[5] = bcast8<2>(g_hi);
-        gg[6] = bcast8<3>(g_lo), gg[7] = bcast8<3>(g_hi);
-        gg[8] = bcast8<4>(g_lo), gg[9] = bcast8<4>(g_hi);
-        gg[10] = bcast8<5>(g_lo), gg[11] = bcast8<5>(g_hi);
-        gg[12] = bcast8<6>(g_lo), gg[13] = bcast8<6>(g_hi);
-        gg[14] = bcast8<7>(g_lo), gg[15] = bcast8<7>(g_hi);
+        g_lo = gate_log_decay(bf16_lo(rw), hg.b.x, A);
+        g_hi = gate_log_decay(bf16_hi(rw), hg.b.y, A);
         b = beta_from_raw(bf16_lo(__float_as_uint(in.beta)));
     } else {
-        const float g16[16] = {in.g0.x, in.g0.y, in.g0.z, in.g0.w, in.g1.x, in.g1.y, in.g1.z, in.g1.w,
-                               in.g2.x, in.g2.y, in.g2.z, in.g2.w, in.g3.x, in.g3.y, in.g3.z, in.g3.w};
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            gg[i] = g16[i];
+        g_lo = in.g.x;
+        g_hi = in.g.y;
         b = in.beta;
     }
+    const float a_lo = __expf(g_lo), a_hi = __expf(g_hi);
+    a[0] = bcast8<0>(a_lo), a[1] = bcast8<0>(a_hi);
+    a[2] = bcast8<1>(a_lo), a[3] = bcast8<1>(a_hi);
+    a[4] = bcast8<2>(a_lo), a[5] = bcast8<2>(a_hi);
+    a[6] = bcast8<3>(a_lo), a[7] = bcast8<3>(a_hi);
+    a[8] = bcast8<4>(a_lo), a[9] = bcast8<4>(a_hi);
+    a[10] = bcast8<5>(a_lo), a[11] = bcast8<5>(a_hi);
+    a[12] = bcast8<6>(a_lo), a[13] = bcast8<6>(a_hi);
+    a[14] = bcast8<7>(a_lo), a[15] = bcast8<7>(a_hi);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         kk[2 * i] = bf16_lo(kw[i]);
@@ -349,10 +344,8 @@ __device__ __forceinline__ void advance_token(f32x4 (&s)[ROWS_PER_LANE], TokenIn
     }
     float kq = 0.f;
 #pragma unroll
-    for (int i = 0; i < ROWS_PER_LANE; ++i) {
-        a[i] = __expf(gg[i]);
+    for (int i = 0; i < ROWS_PER_LANE; ++i)
         kq = fmaf(kk[i], qq[i], kq);
-    }
     const float v0 = bf16_lo(in.v.x), v1 = bf16_hi(in.v.x), v2 = bf16_lo(in.v.y), v3 = bf16_hi(in.v.y);
     if constexpr (PREFETCH) {
         if (t + 1 < eos)
@@ -556,16 +549,13 @@ __device__ __forceinline__ void stage_store(TokenStage<NW> &st, const StagePiece
 }
 
 __device__ __forceinline__ void read_staged(TokenIn &in, const uint4 (&k)[KD / 8], const uint4 (&q)[KD / 8],
-                                            const float4 (&g)[KD / 4], uint2 v, float beta, int rg)
+                                            const float4 (&g)[KD / 4], uint2 v, float beta, int rg, int cg)
 {
     in.k0 = k[2 * rg];
     in.k1 = k[2 * rg + 1];
     in.q0 = q[2 * rg];
     in.q1 = q[2 * rg + 1];
-    in.g0 = g[4 * rg];
-    in.g1 = g[4 * rg + 1];
-    in.g2 = g[4 * rg + 2];
-    in.g3 = g[4 * rg + 3];
+    in.g = reinterpret_cast<const float2 *>(g)[8 * rg + cg];   // key rows 16 rg + 2 cg, + 1
     in.v = v;
     in.beta = beta;
 }
@@ -721,7 +711,7 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot
             // two waves per SIMD, 69.8 vs 72.5 us the other way round).
             __syncthreads();
             for (int j = 0; j < nt; ++j) {
-                read_staged(in, st.k[j], st.q[j], st.g[j], st.v[j][wave * 8 + cg], st.beta[j], rg);
+                read_staged(in, st.k[j], st.q[j], st.g[j], st.v[j][wave * 8 + cg], st.beta[j], rg, cg);
                 advance_token<NORM, false, false>(s, in, p, no_gate, bos + j, eos, h, hv, lane, wave, rg, row0, col,
                                                   norm_partial);
                 keep_state(bos + j);
@@ -746,7 +736,7 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot
                 }
                 __syncthreads();
                 for (int j = 0; j < nt; ++j) {
-                    read_staged(in, st.k[j], st.q[j], st.g[j], st.v[j][wave * 8 + cg], st.beta[j], rg);
+                    read_staged(in, st.k[j], st.q[j], st.g[j], st.v[j][wave * 8 + cg], st.beta[j], rg, cg);
                     advance_token<NORM, false, false>(s, in, p, no_gate, t0 + j, eos, h, hv, lane, wave, rg, row0,
                                                       col, norm_partial);
                     keep_state(t0 + j);
