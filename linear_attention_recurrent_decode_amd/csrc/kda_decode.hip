@@ -179,6 +179,7 @@ struct TileIO {
                                                           false))
 constexpr int DPP_ROW_ROR8 = 0x128;          // lane l <- l^8 within its 16-lane row
 constexpr int DPP_ROW_HALF_MIRROR = 0x141;   // lane l <- 7 - l within its 8-lane half row
+constexpr int DPP_ROW_MIRROR = 0x140;        // lane l <- 15 - l within its 16-lane row
 constexpr int DPP_QUAD_XOR1 = 0xB1;          // quad_perm [1,0,3,2]
 constexpr int DPP_QUAD_XOR2 = 0x4E;          // quad_perm [2,3,0,1]
 
@@ -342,10 +343,14 @@ __device__ __forceinline__ void advance_token(f32x4 (&s)[ROWS_PER_LANE], TokenIn
         qq[2 * i] = bf16_lo(qw[i]);
         qq[2 * i + 1] = bf16_hi(qw[i]);
     }
-    float kq = 0.f;
+    // k.q over the lane's 16 rows as a pairwise tree (row pairs 2m, 2m + 1,
+    // then pairs of pairs): the order in which the 16-column-wave kernel,
+    // whose lanes own one row pair each, adds them across lanes
+    float kp[ROWS_PER_LANE / 2];
 #pragma unroll
-    for (int i = 0; i < ROWS_PER_LANE; ++i)
-        kq = fmaf(kk[i], qq[i], kq);
+    for (int m = 0; m < ROWS_PER_LANE / 2; ++m)
+        kp[m] = fmaf(kk[2 * m + 1], qq[2 * m + 1], kk[2 * m] * qq[2 * m]);
+    float kq = ((kp[0] + kp[1]) + (kp[2] + kp[3])) + ((kp[4] + kp[5]) + (kp[6] + kp[7]));
     const float v0 = bf16_lo(in.v.x), v1 = bf16_hi(in.v.x), v2 = bf16_lo(in.v.y), v3 = bf16_hi(in.v.y);
     if constexpr (PREFETCH) {
         if (t + 1 < eos)
@@ -755,6 +760,233 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot
         tile.store(i, s[i]);
 }
 
+// ------------------------------------------------- 16-column waves (calls with few tiles or several tokens)
+//
+// A second decomposition of the same arithmetic, for calls whose time goes
+// into the per-token chain rather than into streaming the tile: several
+// tokens per request, or few (request, value head) tiles.  A wave owns 16
+// value columns x all 128 key rows; lane l holds column l % 16 of the 32 key
+// rows 32 (l / 16) .. +31 (its row quarter).  The 16 lanes of a DPP row then
+// share their key rows, so every per-row factor (a_i k_i, a_i q_i, a_i, k_i)
+// is computed once, by the lane that owns the row pair (rows 2 (l % 16), + 1
+// of the quarter), and reaches the other 15 lanes as a DPP row_newbcast
+// operand of the very multiply-add that uses it: no unpacking, broadcasting
+// or scaling instructions per lane and row.  Per token a lane issues 64
+// fused partial-sum and 64 fused update instructions plus about 50 others
+// (the 32-column layout: about 470), and twice as many waves share the work
+// of a tile, which the compute unit's dual-issue VALU absorbs.  The cost is
+// the tile stream: one 4-byte element per lane and row, 64-byte row pieces.
+//
+// Every result bit equals the 32-column kernel's: the lane's two 16-row
+// halves are summed separately in row order and then added (the 32-column
+// kernel's first reduction level), the row quarters are added by the same
+// two swaps, k.q uses the same pairwise tree, and the update and readout
+// are the same fused operations on the same operands.
+
+constexpr int Q_ROWS = 32;   // key rows per lane: 128 rows over 4 row quarters
+
+// One token's inputs as a 16-column-wave lane needs them: k, q and g of its
+// row pair, v of its column, beta of the head.  With the fused gate (RAWG)
+// g.x carries the row pair's raw bf16 values and beta the raw beta's bits.
+struct PairIn {
+    uint32_t k, q;
+    float2 g;
+    uint32_t v;
+    float beta;
+};
+
+template <bool RAWG>
+__device__ __forceinline__ void load_pair(PairIn &in, const DecodeParams &p, int64_t t, int h, int hv, int row0,
+                                          int cp, int col)
+{
+    in.k = reinterpret_cast<const uint32_t *>(p.k + t * p.k_stride + h * KD + row0)[cp];
+    in.q = reinterpret_cast<const uint32_t *>(p.q + t * p.q_stride + h * KD + row0)[cp];
+    if constexpr (RAWG) {
+        in.g.x = __uint_as_float(
+            reinterpret_cast<const uint32_t *>(p.raw_gate + t * p.raw_gate_stride + (int64_t)hv * KD + row0)[cp]);
+        in.beta = __uint_as_float((uint32_t)p.raw_beta[t * p.raw_beta_stride + hv]);
+    } else {
+        in.g = reinterpret_cast<const float2 *>(p.g + t * p.g_stride + (int64_t)hv * KD + row0)[cp];
+        in.beta = p.beta[t * p.beta_stride + hv];
+    }
+    in.v = p.v[t * p.v_stride + (int64_t)hv * VD + col];
+}
+
+// Partial sums over rows 8B .. 8B+7 of the lane's quarter, whose owners are
+// lanes 4B .. 4B+3 of the DPP row (lo values for even rows, hi for odd):
+// u += s_i (a_i k_i), w += s_i (a_i q_i), the factor taken from its owner by
+// row_newbcast.  A DPP operand must not be written by the two VALU
+// instructions before it; nothing in the block writes one, and the leading
+// s_nop covers whatever the compiler placed before the block.
+#define Q_ROW_UW(AK, AQ, S, IMM)                                                                \
+    "v_fmac_f32_dpp %0, %" AK ", %" S " row_newbcast:%c" IMM " row_mask:0xf bank_mask:0xf\n\t" \
+    "v_fmac_f32_dpp %1, %" AQ ", %" S " row_newbcast:%c" IMM " row_mask:0xf bank_mask:0xf\n\t"
+
+template <int B>
+__device__ __forceinline__ void quarter_sums8(const float (&s)[Q_ROWS], float ak_lo, float ak_hi, float aq_lo,
+                                              float aq_hi, float &u, float &w)
+{
+    asm volatile("s_nop 1\n\t"
+                 Q_ROW_UW("2", "4", "6", "14") Q_ROW_UW("3", "5", "7", "14")
+                 Q_ROW_UW("2", "4", "8", "15") Q_ROW_UW("3", "5", "9", "15")
+                 Q_ROW_UW("2", "4", "10", "16") Q_ROW_UW("3", "5", "11", "16")
+                 Q_ROW_UW("2", "4", "12", "17") Q_ROW_UW("3", "5", "13", "17")
+                 : "+v"(u), "+v"(w)
+                 : "v"(ak_lo), "v"(ak_hi), "v"(aq_lo), "v"(aq_hi),
+                   "v"(s[8 * B + 0]), "v"(s[8 * B + 1]), "v"(s[8 * B + 2]), "v"(s[8 * B + 3]),
+                   "v"(s[8 * B + 4]), "v"(s[8 * B + 5]), "v"(s[8 * B + 6]), "v"(s[8 * B + 7]),
+                   "i"(4 * B), "i"(4 * B + 1), "i"(4 * B + 2), "i"(4 * B + 3));
+}
+
+// The update of rows 8B .. 8B+7: s_i = k_i v' + (a_i s_i), one rounding for
+// the multiply-add as in fmaf(k_i, v', a_i s_i).
+#define Q_ROW_UPD(A, K, S, IMM)                                                                  \
+    "v_mul_f32_dpp %" S ", %" A ", %" S " row_newbcast:%c" IMM " row_mask:0xf bank_mask:0xf\n\t" \
+    "v_fmac_f32_dpp %" S ", %" K ", %12 row_newbcast:%c" IMM " row_mask:0xf bank_mask:0xf\n\t"
+
+template <int B>
+__device__ __forceinline__ void quarter_update8(float (&s)[Q_ROWS], float a_lo, float a_hi, float k_lo, float k_hi,
+                                                float vp)
+{
+    asm volatile("s_nop 1\n\t"
+                 Q_ROW_UPD("8", "10", "0", "13") Q_ROW_UPD("9", "11", "1", "13")
+                 Q_ROW_UPD("8", "10", "2", "14") Q_ROW_UPD("9", "11", "3", "14")
+                 Q_ROW_UPD("8", "10", "4", "15") Q_ROW_UPD("9", "11", "5", "15")
+                 Q_ROW_UPD("8", "10", "6", "16") Q_ROW_UPD("9", "11", "7", "16")
+                 : "+v"(s[8 * B + 0]), "+v"(s[8 * B + 1]), "+v"(s[8 * B + 2]), "+v"(s[8 * B + 3]),
+                   "+v"(s[8 * B + 4]), "+v"(s[8 * B + 5]), "+v"(s[8 * B + 6]), "+v"(s[8 * B + 7])
+                 : "v"(a_lo), "v"(a_hi), "v"(k_lo), "v"(k_hi), "v"(vp),
+                   "i"(4 * B), "i"(4 * B + 1), "i"(4 * B + 2), "i"(4 * B + 3));
+}
+
+// Advance the lane's column of its row quarter by one token and write its
+// output (the same recurrence as advance_token).
+template <bool RAWG>
+__device__ __forceinline__ void advance_pair(float (&s)[Q_ROWS], const PairIn &in, const DecodeParams &p,
+                                             const HeadGate<RAWG> &hg, int64_t t, int hv, int rq, int col)
+{
+    const float k_lo = bf16_lo(in.k), k_hi = bf16_hi(in.k), q_lo = bf16_lo(in.q), q_hi = bf16_hi(in.q);
+    float b, g_lo, g_hi;
+    if constexpr (RAWG) {
+        const uint32_t rw = __float_as_uint(in.g.x);
+        const float A = expf(hg.a_log);
+        g_lo = gate_log_decay(bf16_lo(rw), hg.b.x, A);
+        g_hi = gate_log_decay(bf16_hi(rw), hg.b.y, A);
+        b = beta_from_raw(bf16_lo(__float_as_uint(in.beta)));
+    } else {
+        g_lo = in.g.x;
+        g_hi = in.g.y;
+        b = in.beta;
+    }
+    const float a_lo = __expf(g_lo), a_hi = __expf(g_hi);
+    const float ak_lo = a_lo * k_lo, ak_hi = a_hi * k_hi, aq_lo = a_lo * q_lo, aq_hi = a_hi * q_hi;
+
+    // both key-axis partial sums, each 16-row half in row order
+    float u_lo = 0.f, w_lo = 0.f, u_hi = 0.f, w_hi = 0.f;
+    quarter_sums8<0>(s, ak_lo, ak_hi, aq_lo, aq_hi, u_lo, w_lo);
+    quarter_sums8<2>(s, ak_lo, ak_hi, aq_lo, aq_hi, u_hi, w_hi);
+    quarter_sums8<1>(s, ak_lo, ak_hi, aq_lo, aq_hi, u_lo, w_lo);
+    quarter_sums8<3>(s, ak_lo, ak_hi, aq_lo, aq_hi, u_hi, w_hi);
+
+    // k.q: the row pair, then pairs of pairs across the DPP row, then the quarters
+    float kq = fmaf(k_hi, q_hi, k_lo * q_lo);
+    kq += KDA_DPP(kq, DPP_QUAD_XOR1);
+    kq += KDA_DPP(kq, DPP_QUAD_XOR2);
+    kq += KDA_DPP(kq, DPP_ROW_HALF_MIRROR);
+    kq += KDA_DPP(kq, DPP_ROW_MIRROR);
+    kq = add_permlane32_swap(add_permlane16_swap(kq));
+    const float u = add_permlane32_swap(add_permlane16_swap(u_lo + u_hi));
+    const float w = add_permlane32_swap(add_permlane16_swap(w_lo + w_hi));
+
+    const float vp = b * (bf16_lo(in.v) - u);
+    const float o = p.scale * fmaf(vp, kq, w);
+    quarter_update8<0>(s, a_lo, a_hi, k_lo, k_hi, vp);
+    quarter_update8<1>(s, a_lo, a_hi, k_lo, k_hi, vp);
+    quarter_update8<2>(s, a_lo, a_hi, k_lo, k_hi, vp);
+    quarter_update8<3>(s, a_lo, a_hi, k_lo, k_hi, vp);
+    if (rq == 0)
+        p.out[t * p.out_stride + (int64_t)hv * VD + col] = (uint16_t)pack_bf16x2(o, 0.0f);
+}
+
+// fp32 pool, no norm epilogue; NQ waves of 16 columns per workgroup.  The
+// inputs of the first PF tokens are loaded with the tile (later tokens, if
+// any, load at the top of their iteration).
+template <int NQ, int PF, bool RAWG>
+__global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *slot_idx, const int32_t *cu_seqlens,
+                                                               void *state, int64_t slot_stride, int64_t num_slots,
+                                                               int32_t HV, int32_t T, const int32_t *status,
+                                                               DecodeParams p)
+{
+    static_assert(NQ == 2 || NQ == 4, "a workgroup is 2 or 4 waves of 16 columns");
+    static_assert(PF >= 1 && PF <= 4, "up to 4 tokens' inputs ahead");
+    constexpr int NVT = 8 / NQ;   // value tiles per head
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t block = blockIdx.x;
+    const int vt = (int)(block % NVT);
+    const int64_t unit = block / NVT;
+    const int64_t req = unit / HV;
+    const int hv = (int)(unit - req * HV);
+
+    const int64_t slot = slot_idx[req];
+    if (status && *status != KDA_DEVICE_OK)
+        return;
+    if (slot < 0 || slot >= num_slots)
+        return;
+    const int64_t bos = req * T, eos = bos + T;
+    const int h = qk_head(p, hv);
+
+    const int cp = lane & 15;             // column within the wave; owner of row pair cp
+    const int rq = lane >> 4;             // row quarter
+    const int col = (vt * NQ + wave) * 16 + cp;
+    const int row0 = rq * Q_ROWS;
+
+    float *tile = static_cast<float *>(state) + slot * slot_stride + (int64_t)hv * (KD * VD) + (int64_t)row0 * VD + col;
+    float s[Q_ROWS];
+    auto keep_state = [&](int64_t t) {
+        if (p.inter_state) {
+            float *it = static_cast<float *>(p.inter_state) + t * p.inter_stride + (int64_t)hv * (KD * VD) +
+                        (int64_t)row0 * VD + col;
+#pragma unroll
+            for (int i = 0; i < Q_ROWS; ++i)
+                __builtin_nontemporal_store(s[i], it + i * VD);
+        }
+    };
+    HeadGate<RAWG> hg;
+    PairIn in[PF];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        s[i] = __builtin_nontemporal_load(tile + i * VD);
+    __builtin_amdgcn_sched_barrier(0);
+    hg.load(p, hv, row0, cp);
+    // token j < PF, or the last token again for j >= T (a harmless repeat
+    // that keeps the loads unconditional)
+#pragma unroll
+    for (int j = 0; j < PF; ++j)
+        load_pair<RAWG>(in[j], p, j < T ? bos + j : eos - 1, h, hv, row0, cp, col);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 8; i < Q_ROWS; ++i)
+        s[i] = __builtin_nontemporal_load(tile + i * VD);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+        if (j < T) {
+            advance_pair<RAWG>(s, in[j], p, hg, bos + j, hv, rq, col);
+            keep_state(bos + j);
+        }
+    }
+    for (int64_t t = bos + PF; t < eos; ++t) {
+        load_pair<RAWG>(in[0], p, t, h, hv, row0, cp, col);
+        advance_pair<RAWG>(s, in[0], p, hg, t, hv, rq, col);
+        keep_state(t);
+    }
+#pragma unroll
+    for (int i = 0; i < Q_ROWS; ++i)
+        __builtin_nontemporal_store(s[i], tile + i * VD);
+}
+
 // Metadata check for KDA_FLAG_VALIDATE: one workgroup, lowest error code wins.
 constexpr int VALIDATE_THREADS = 1024;
 constexpr int VALIDATE_LDS_SLOTS = 8192;
@@ -1010,6 +1242,55 @@ int32_t plan_vtile(int64_t units, int32_t T, bool norm)
     return 128;
 }
 
+// 16-column waves (kda_decode_q_kernel) for an fp32 pool without the norm:
+// 0 = not used, else waves per workgroup.  They pay off where the per-token
+// chain, not the tile stream, sets the time; measured on MI355X with cold
+// caches against the 32-column kernel, they win up to 64 tiles with one
+// token per request, up to 384 with four (N48/H8: 12.9 vs 13.6 us; N64:
+// 17.0 vs 16.0), and cross over in between for two and three.
+int32_t plan_quarter_waves(int64_t units, int32_t T)
+{
+    const int64_t limit = T == 1 ? 64 : T == 2 ? 128 : T == 3 ? 192 : 384;
+    if (units > limit)
+        return 0;
+    return units < 128 ? 2 : 4;
+}
+
+template <int NQ, int PF, bool RAWG>
+kda_status launch_q(const DecodeParams &p, int64_t units, hipStream_t stream)
+{
+    const int64_t blocks = units * (8 / NQ);
+    if (blocks > 0x7FFFFFFF)
+        return KDA_ERR_SHAPE;
+    const int32_t *slot_idx = p.slot_idx, *cu_seqlens = p.cu_seqlens;
+    void *state = p.state;
+    int64_t slot_stride = p.slot_stride, num_slots = p.num_slots;
+    int32_t HV = p.HV, T = p.T;
+    const int32_t *status = p.status;
+    void *args[] = {&slot_idx, &cu_seqlens, &state, &slot_stride, &num_slots, &HV, &T, &status,
+                    const_cast<DecodeParams *>(&p)};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&kda_decode_q_kernel<NQ, PF, RAWG>),
+                                         dim3((uint32_t)blocks), dim3(64 * NQ), args, 0, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+template <int NQ, bool RAWG>
+kda_status dispatch_q_tokens(const DecodeParams &p, int64_t units, hipStream_t s)
+{
+    switch (p.T) {
+    case 1: return launch_q<NQ, 1, RAWG>(p, units, s);
+    case 2: return launch_q<NQ, 2, RAWG>(p, units, s);
+    case 3: return launch_q<NQ, 3, RAWG>(p, units, s);
+    default: return launch_q<NQ, 4, RAWG>(p, units, s);
+    }
+}
+
+template <bool RAWG>
+kda_status dispatch_q(const DecodeParams &p, int64_t units, int nq, hipStream_t s)
+{
+    return nq == 2 ? dispatch_q_tokens<2, RAWG>(p, units, s) : dispatch_q_tokens<4, RAWG>(p, units, s);
+}
+
 template <int NW, bool NORM, bool BF16S, bool RAWG>
 kda_status launch_decode(const DecodeParams &p, int64_t units, int body, hipStream_t stream)
 {
@@ -1067,8 +1348,12 @@ kda_status run_decode(const kda_decode_args *a, int32_t T, const int32_t *cu_seq
     if (a->N == 0)
         return KDA_OK;
     const bool norm = a->gate != nullptr;
+    const bool bf16_pool = (flags & KDA_FLAG_STATE_BF16) != 0;
     const int64_t units = (int64_t)a->N * a->HV;
     int vtile = vtile_from_flags(flags);
+    // a forced width keeps the 32-column waves; otherwise step calls on an
+    // fp32 pool without the norm may take the 16-column waves
+    const int nq = (vtile == 0 && !cu_seqlens && !norm && !bf16_pool) ? plan_quarter_waves(units, T) : 0;
     if (vtile == 0)
         vtile = plan_vtile(units, cu_seqlens ? 1 : T, norm);
     if (norm && vtile != 128)
@@ -1127,14 +1412,15 @@ kda_status run_decode(const kda_decode_args *a, int32_t T, const int32_t *cu_seq
                             vargs, 0, s) != hipSuccess)
             return KDA_ERR_LAUNCH;
     }
-    // packed batches: the staged body; step calls with several tokens per
-    // request, fewer than 512 tiles (two per compute unit), the fused gate
-    // activation or a bf16 pool: the peeled body (its straight-line first
-    // token also lets the activation run while the tile is in flight, and at
-    // 144 VGPRs it runs three waves per SIMD, which the half-size bf16 tiles
-    // need); otherwise the prefetching loop (all measured on MI355X, cold
-    // caches)
-    const bool bf16_pool = (flags & KDA_FLAG_STATE_BF16) != 0;
+    if (nq)
+        return a->raw_gate ? dispatch_q<true>(p, units, nq, s) : dispatch_q<false>(p, units, nq, s);
+    // 32-column waves.  Packed batches: the staged body; step calls with
+    // several tokens per request, fewer than 512 tiles (two per compute
+    // unit), the fused gate activation or a bf16 pool: the peeled body (its
+    // straight-line first token also lets the activation run while the tile
+    // is in flight, and at 144 VGPRs it runs three waves per SIMD, which the
+    // half-size bf16 tiles need); otherwise the prefetching loop (all
+    // measured on MI355X, cold caches)
     const int body = cu_seqlens != nullptr ? BODY_STAGED
                      : (T > 1 || units < 512 || a->raw_gate || bf16_pool) ? BODY_PEELED : BODY_LOOP;
     if (flags & KDA_FLAG_STATE_BF16)
@@ -1199,7 +1485,8 @@ kda_status kda_gated_rmsnorm(const void *x, const void *gate, const void *weight
 
 int32_t kda_decode_plan(int64_t units, int32_t T, int32_t has_norm)
 {
-    return plan_vtile(units, T, has_norm != 0);
+    const int32_t nq = has_norm ? 0 : plan_quarter_waves(units, T);
+    return nq ? 16 * nq : plan_vtile(units, T, has_norm != 0);
 }
 
 const char *kda_status_string(kda_status status)

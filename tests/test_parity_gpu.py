@@ -672,6 +672,59 @@ def test_tile_widths_bit_identical():
             assert torch.equal(o, results[0][0]) and torch.equal(s, results[0][1]), name
 
 
+# ------------------------------------------------------- 16-column waves
+QUARTER_CASES = [
+    # (N, H, HV, T, raw gates): the library picks the 16-column waves at all of these
+    (1, 8, 8, 4, False),      # 8 tiles, two waves per workgroup
+    (5, 1, 3, 2, False),      # three value heads per q/k head
+    (9, 4, 8, 3, True),       # fused gate activation
+    (20, 4, 8, 4, False),     # 160 tiles: four waves per workgroup
+    (7, 2, 4, 6, True),       # tokens past the four whose inputs load with the tile
+    (8, 8, 8, 1, False),      # one token, 64 tiles
+]
+
+
+@pytest.mark.parametrize("case", QUARTER_CASES)
+def test_quarter_waves_match_wide_waves_bitwise(case):
+    """The 16-column-wave kernel (the library's choice at these shapes) and
+    the 32-column kernel (every forced tile width) give the same bits:
+    outputs, final states and per-token states; and they match the oracle."""
+    N, H, HV, T, raw = case
+    p = ki.make_problem("quarter", 300 + N, N=N, H=H, HV=HV, K=128, V=128, num_slots=2 * N + 3, T=T,
+                        n_pad=N // 4, raw_gates=raw)
+    assert kda.kda_decode_plan(N * HV, T, False) == (32 if N * HV < 128 else 64)
+    results = []
+    for flags in (0, kda.KDA_FLAG_VTILE(32), kda.KDA_FLAG_VTILE(64), kda.KDA_FLAG_VTILE(128)):
+        d = _fresh(p)
+        inter = torch.full((p.tokens, p.HV, p.K, p.V), 1232.0, device=DEV)
+        run_gpu(d, flags=flags, inter_state=inter)
+        torch.cuda.synchronize()
+        if flags == 0:
+            ref_inter = np.full((p.tokens, p.HV, p.K, p.V), np.nan)
+            ref_out, ref_state = run_oracle(p, inter_state=ref_inter)
+            _log(f"quarter waves {case}", compare(d, ref_out, ref_state))
+            live_rows = np.isfinite(ref_inter[:, 0, 0, 0])
+            got = inter.cpu().numpy().astype(np.float64)
+            assert np.all(np.abs(got[live_rows] - ref_inter[live_rows]) <= 1e-4 * np.abs(ref_inter[live_rows]) + 1e-6)
+            assert np.all(got[~live_rows] == 1232.0)
+        results.append((d.out.view(torch.int16).clone(), d.state.clone(), inter))
+    for o, st, it in results[1:]:
+        assert torch.equal(o, results[0][0]) and torch.equal(st, results[0][1]) and torch.equal(it, results[0][2])
+
+
+def test_quarter_waves_full_t4_sweep_match_wide_waves():
+    """The T = 4 serving sweep: the library's choice against the forced
+    32-column kernel, bit for bit."""
+    for n in (1, 8, 16, 24, 32):
+        p = ki.workload(f"n{n}_t4_h8")
+        a = _fresh(p)
+        run_gpu(a)
+        b = _fresh(p)
+        run_gpu(b, flags=kda.KDA_FLAG_VTILE(128))
+        torch.cuda.synchronize()
+        assert torch.equal(a.state, b.state) and torch.equal(a.out.view(torch.int16), b.out.view(torch.int16)), n
+
+
 def test_chained_single_tokens_bit_identical():
     p = ki.workload("n32_t4_h8")
     d_multi = _fresh(p)
