@@ -17,6 +17,9 @@
 // (request, value head, value tile).  Columns never interact in the
 // recurrence, so the tiling cannot change a single result bit: every wave runs
 // the same per-column arithmetic in the same order whatever the tile width.
+// Calls with several tokens per request or few tiles take a second layout
+// of the same arithmetic, with the same result bits (16-column waves, one
+// column of 32 key rows per lane; see kda_decode_q_kernel).
 //
 // Per token (vLLM PR 57585 names the op; the gated delta rule of Kimi Delta
 // Attention is the recurrence):
