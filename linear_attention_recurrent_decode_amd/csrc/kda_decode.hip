@@ -777,8 +777,10 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot
 // or scaling instructions per lane and row.  Per token a lane issues 64
 // fused partial-sum and 64 fused update instructions plus about 50 others
 // (the 32-column layout: about 470), and twice as many waves share the work
-// of a tile, which the compute unit's dual-issue VALU absorbs.  The cost is
-// the tile stream: one 4-byte element per lane and row, 64-byte row pieces.
+// of a tile.  A lane's column is a 4-byte element per row, so the tile moves
+// between HBM and the lanes through LDS: 16-byte accesses over full row
+// pieces of the workgroup's 32 or 64 columns, then one LDS read (or write)
+// per row and lane.
 //
 // Every result bit equals the 32-column kernel's: the lane's two 16-row
 // halves are summed separately in row order and then added (the 32-column
@@ -945,7 +947,6 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
     const int col = (vt * NQ + wave) * 16 + cp;
     const int row0 = rq * Q_ROWS;
 
-    float *tile = static_cast<float *>(state) + slot * slot_stride + (int64_t)hv * (KD * VD) + (int64_t)row0 * VD + col;
     float s[Q_ROWS];
     auto keep_state = [&](int64_t t) {
         if (p.inter_state) {
@@ -956,23 +957,42 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
                 __builtin_nontemporal_store(s[i], it + i * VD);
         }
     };
+    // The tile streams through LDS: the workgroup reads and writes its
+    // 128 rows x C columns with 16-byte accesses (C/4 lanes per row, full
+    // 128- or 256-byte row pieces, 8 per lane), and each lane takes its
+    // column of 32 rows from LDS.  Row r of the staged tile starts at dword
+    // r C + 16 (r / 32): the pad puts the 4 row quarters read by one
+    // instruction on disjoint 16-bank groups.
+    constexpr int C = 16 * NQ;
+    __shared__ float stage[KD * C + 4 * 16];
+    auto lds_at = [](int r, int c) { return r * C + (r >> 5) * 16 + c; };
+    const int c4 = 4 * ((int)threadIdx.x % (C / 4));
+    const int r16 = (int)threadIdx.x / (C / 4);   // 0 .. 15: row within each 16-row slab
+    f32x4 *slab = reinterpret_cast<f32x4 *>(static_cast<float *>(state) + slot * slot_stride +
+                                            (int64_t)hv * (KD * VD) + vt * C + (int64_t)r16 * VD + c4);
     HeadGate<RAWG> hg;
     PairIn in[PF];
+    {
+        f32x4 piece[KD / 16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        s[i] = __builtin_nontemporal_load(tile + i * VD);
-    __builtin_amdgcn_sched_barrier(0);
-    hg.load(p, hv, row0, cp);
-    // token j < PF, or the last token again for j >= T (a harmless repeat
-    // that keeps the loads unconditional)
+        for (int j = 0; j < KD / 16; ++j)
+            piece[j] = __builtin_nontemporal_load(slab + j * 16 * (VD / 4));
+        __builtin_amdgcn_sched_barrier(0);
+        hg.load(p, hv, row0, cp);
+        // token j < PF, or the last token again for j >= T (a harmless repeat
+        // that keeps the loads unconditional)
 #pragma unroll
-    for (int j = 0; j < PF; ++j)
-        load_pair<RAWG>(in[j], p, j < T ? bos + j : eos - 1, h, hv, row0, cp, col);
-    __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < PF; ++j)
+            load_pair<RAWG>(in[j], p, j < T ? bos + j : eos - 1, h, hv, row0, cp, col);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 8; i < Q_ROWS; ++i)
-        s[i] = __builtin_nontemporal_load(tile + i * VD);
-    __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < KD / 16; ++j)
+            *reinterpret_cast<f32x4 *>(&stage[lds_at(16 * j + r16, c4)]) = piece[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < Q_ROWS; ++i)
+        s[i] = stage[lds_at(row0 + i, 16 * wave + cp)];
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
         if (j < T) {
@@ -985,9 +1005,16 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
         advance_pair<RAWG>(s, in[0], p, hg, t, hv, rq, col);
         keep_state(t);
     }
+    // back through LDS (every wave is done reading its column first)
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < Q_ROWS; ++i)
-        __builtin_nontemporal_store(s[i], tile + i * VD);
+        stage[lds_at(row0 + i, 16 * wave + cp)] = s[i];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KD / 16; ++j)
+        __builtin_nontemporal_store(*reinterpret_cast<const f32x4 *>(&stage[lds_at(16 * j + r16, c4)]),
+                                    slab + j * 16 * (VD / 4));
 }
 
 // Metadata check for KDA_FLAG_VALIDATE: one workgroup, lowest error code wins.
@@ -1247,13 +1274,16 @@ int32_t plan_vtile(int64_t units, int32_t T, bool norm)
 
 // 16-column waves (kda_decode_q_kernel) for an fp32 pool without the norm:
 // 0 = not used, else waves per workgroup.  They pay off where the per-token
-// chain, not the tile stream, sets the time; measured on MI355X with cold
-// caches against the 32-column kernel, they win up to 64 tiles with one
-// token per request, up to 384 with four (N48/H8: 12.9 vs 13.6 us; N64:
-// 17.0 vs 16.0), and cross over in between for two and three.
+// chain, not the tile stream, sets the time.  Measured on MI355X with cold
+// caches against the 32-column kernel (H = 8): with one token per request
+// they win up to 64 tiles (N8: 3.88 vs 3.99 us) and lose from 128 (N16: 4.95
+// vs 4.75); with two or more tokens they win or tie up to 512 tiles (T = 2:
+// N16 5.52 vs 6.07, N32 7.78 vs 7.86, N64 12.54 vs 14.19; T = 4: N32 9.50
+// vs 10.17, N64 14.29 vs 16.38) and lose at 1024 (N128/T4: 30.6 vs 29.7).
+// Two waves per workgroup below 128 tiles, four from 128.
 int32_t plan_quarter_waves(int64_t units, int32_t T)
 {
-    const int64_t limit = T == 1 ? 64 : T == 2 ? 128 : T == 3 ? 192 : 384;
+    const int64_t limit = T == 1 ? 64 : 512;
     if (units > limit)
         return 0;
     return units < 128 ? 2 : 4;

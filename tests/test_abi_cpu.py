@@ -67,11 +67,11 @@ def test_status_strings_and_plan():
             assert kda.kda_decode_plan(units, T, False) in (32, 64, 128)
             assert kda.kda_decode_plan(units, T, True) == 128
     # the launch table: 16-column waves (2 or 4 per workgroup) up to 64 tiles
-    # with one token, 128 with two, 192 with three, 384 with four or more;
-    # 32-column waves (32, 64 or 128 columns per workgroup) above
+    # with one token and up to 512 with two or more; 32-column waves (32, 64
+    # or 128 columns per workgroup) above
     expect = {(8, 1): 32, (64, 1): 32, (65, 1): 32, (256, 1): 64, (1024, 1): 128,
-              (128, 2): 64, (129, 2): 32, (192, 3): 64, (193, 3): 32, (256, 3): 128,
-              (8, 4): 32, (127, 4): 32, (128, 4): 64, (384, 4): 64, (385, 4): 128, (384, 9): 64}
+              (128, 2): 64, (512, 2): 64, (513, 2): 128, (192, 3): 64,
+              (8, 4): 32, (127, 4): 32, (128, 4): 64, (512, 4): 64, (513, 4): 128, (384, 9): 64}
     for (units, T), width in expect.items():
         assert kda.kda_decode_plan(units, T, False) == width, (units, T)
 

@@ -681,6 +681,7 @@ QUARTER_CASES = [
     (20, 4, 8, 4, False),     # 160 tiles: four waves per workgroup
     (7, 2, 4, 6, True),       # tokens past the four whose inputs load with the tile
     (8, 8, 8, 1, False),      # one token, 64 tiles
+    (60, 8, 8, 2, False),     # 480 tiles, two tokens
 ]
 
 
