@@ -80,8 +80,10 @@ typedef enum kda_status {
 #define KDA_DEVICE_ERR_CU_SEQLENS 3   /* cu_seqlens negative, decreasing, or past total_tokens */
 
 /* flags: bits 8..9 force the value-tile width of one workgroup
- * (1 = 32 columns, 2 = 64, 3 = 128; 0 = the library's choice).  Results are
- * bit-identical for every width; the knob exists for tests and tuning. */
+ * (1 = 32 columns, 2 = 64, 3 = 128; 0 = the library's choice) of 32-column
+ * waves; the library's choice may instead use 16-column waves (step calls
+ * without the norm).  Results are bit-identical for every width and wave
+ * layout; the knob exists for tests and tuning. */
 #define KDA_FLAG_VTILE_SHIFT 8u
 #define KDA_FLAG_VTILE_MASK (3u << KDA_FLAG_VTILE_SHIFT)
 #define KDA_FLAG_VTILE(code) (((uint32_t)(code) & 3u) << KDA_FLAG_VTILE_SHIFT)
@@ -210,8 +212,11 @@ kda_status kda_gated_rmsnorm(const void *x, const void *gate, const void *weight
                              int64_t rows, int32_t V, float eps, void *stream);
 
 /* The value-tile width (32, 64 or 128 columns per workgroup) the library
- * picks for `units` = N*HV (request, value head) pairs, T tokens and with or
- * without the norm epilogue.  Host-only, no device access. */
+ * picks for a step call on an fp32 pool with `units` = N*HV (request, value
+ * head) pairs, T tokens and with or without the norm epilogue.  Host-only,
+ * no device access.  (Packed calls plan as T = 1; with a bf16 pool step
+ * calls without the norm take 64-column workgroups of 16-column waves up to
+ * 512 units.) */
 int32_t kda_decode_plan(int64_t units, int32_t T, int32_t has_norm);
 
 /* Static description of a status code. */

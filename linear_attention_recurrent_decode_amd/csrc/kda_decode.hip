@@ -91,6 +91,7 @@ struct DecodeParams {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -913,10 +914,62 @@ __device__ __forceinline__ void advance_pair(float (&s)[Q_ROWS], const PairIn &i
         p.out[t * p.out_stride + (int64_t)hv * VD + col] = (uint16_t)pack_bf16x2(o, 0.0f);
 }
 
-// fp32 pool, no norm epilogue; NQ waves of 16 columns per workgroup.  The
-// inputs of the first PF tokens are loaded with the tile (later tokens, if
-// any, load at the top of their iteration).
-template <int NQ, int PF, bool RAWG>
+// The workgroup's 128 rows x C columns of a state tile in HBM, moved with
+// 16-byte non-temporal accesses over full row pieces: 4 fp32 or 8 bf16
+// elements per lane and access, so 16 (fp32) or 32 (bf16) rows per
+// instruction across the workgroup's 4C lanes, N pieces per lane.  In LDS
+// the tile is fp32 either way (bf16 widened exactly on the way in, rounded
+// to nearest even on the way out), row r at dword r C + 16 (r / 32): the
+// pad puts the 4 row quarters that one column read touches on disjoint
+// 16-bank groups.
+template <int C, bool BF16S>
+struct SlabIO {
+    static constexpr int ELEMS = BF16S ? 8 : 4;            // elements per 16-byte piece
+    static constexpr int ROWS = 4 * C / (C / ELEMS);       // rows per instruction
+    static constexpr int N = KD / ROWS;                    // pieces per lane
+    u32x4 *ptr;
+    int r0, c0;
+
+    __device__ __forceinline__ SlabIO(void *state, int64_t elem_offset, int tid)
+        : r0(tid / (C / ELEMS)), c0(ELEMS * (tid % (C / ELEMS)))
+    {
+        ptr = reinterpret_cast<u32x4 *>(static_cast<char *>(state) +
+                                        (elem_offset + (int64_t)r0 * VD + c0) * (BF16S ? 2 : 4));
+    }
+    static __device__ __forceinline__ int lds_at(int r, int c) { return r * C + (r >> 5) * 16 + c; }
+
+    __device__ __forceinline__ u32x4 load(int j) const
+    {
+        return __builtin_nontemporal_load(ptr + j * ROWS * VD / ELEMS);
+    }
+    __device__ __forceinline__ void to_lds(float *stage, int j, u32x4 w) const
+    {
+        float *d = stage + lds_at(j * ROWS + r0, c0);
+        if constexpr (BF16S) {
+            *reinterpret_cast<f32x4 *>(d) = f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+            *reinterpret_cast<f32x4 *>(d + 4) = f32x4{bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+        } else {
+            *reinterpret_cast<f32x4 *>(d) = __builtin_bit_cast(f32x4, w);
+        }
+    }
+    __device__ __forceinline__ void store_from_lds(const float *stage, int j) const
+    {
+        const float *d = stage + lds_at(j * ROWS + r0, c0);
+        u32x4 w;
+        if constexpr (BF16S) {
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(d), b = *reinterpret_cast<const f32x4 *>(d + 4);
+            w = u32x4{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w)};
+        } else {
+            w = __builtin_bit_cast(u32x4, *reinterpret_cast<const f32x4 *>(d));
+        }
+        __builtin_nontemporal_store(w, ptr + j * ROWS * VD / ELEMS);
+    }
+};
+
+// No norm epilogue; NQ waves of 16 columns per workgroup; fp32 or bf16
+// pool (BF16S).  The inputs of the first PF tokens are loaded with the tile
+// (later tokens, if any, load at the top of their iteration).
+template <int NQ, int PF, bool RAWG, bool BF16S>
 __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *slot_idx, const int32_t *cu_seqlens,
                                                                void *state, int64_t slot_stride, int64_t num_slots,
                                                                int32_t HV, int32_t T, const int32_t *status,
@@ -948,35 +1001,33 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
     const int row0 = rq * Q_ROWS;
 
     float s[Q_ROWS];
+    // per-token states: each lane writes its column (one element per row)
     auto keep_state = [&](int64_t t) {
         if (p.inter_state) {
-            float *it = static_cast<float *>(p.inter_state) + t * p.inter_stride + (int64_t)hv * (KD * VD) +
-                        (int64_t)row0 * VD + col;
+            const int64_t at = t * p.inter_stride + (int64_t)hv * (KD * VD) + (int64_t)row0 * VD + col;
 #pragma unroll
-            for (int i = 0; i < Q_ROWS; ++i)
-                __builtin_nontemporal_store(s[i], it + i * VD);
+            for (int i = 0; i < Q_ROWS; ++i) {
+                if constexpr (BF16S)
+                    __builtin_nontemporal_store((uint16_t)pack_bf16x2(s[i], 0.0f),
+                                                static_cast<uint16_t *>(p.inter_state) + at + i * VD);
+                else
+                    __builtin_nontemporal_store(s[i], static_cast<float *>(p.inter_state) + at + i * VD);
+            }
         }
     };
-    // The tile streams through LDS: the workgroup reads and writes its
-    // 128 rows x C columns with 16-byte accesses (C/4 lanes per row, full
-    // 128- or 256-byte row pieces, 8 per lane), and each lane takes its
-    // column of 32 rows from LDS.  Row r of the staged tile starts at dword
-    // r C + 16 (r / 32): the pad puts the 4 row quarters read by one
-    // instruction on disjoint 16-bank groups.
+    // The tile streams through LDS with 16-byte accesses over full row
+    // pieces, and each lane takes its column of 32 rows from there.
     constexpr int C = 16 * NQ;
+    using Slab = SlabIO<C, BF16S>;
     __shared__ float stage[KD * C + 4 * 16];
-    auto lds_at = [](int r, int c) { return r * C + (r >> 5) * 16 + c; };
-    const int c4 = 4 * ((int)threadIdx.x % (C / 4));
-    const int r16 = (int)threadIdx.x / (C / 4);   // 0 .. 15: row within each 16-row slab
-    f32x4 *slab = reinterpret_cast<f32x4 *>(static_cast<float *>(state) + slot * slot_stride +
-                                            (int64_t)hv * (KD * VD) + vt * C + (int64_t)r16 * VD + c4);
+    const Slab slab(state, slot * slot_stride + (int64_t)hv * (KD * VD) + vt * C, (int)threadIdx.x);
     HeadGate<RAWG> hg;
     PairIn in[PF];
     {
-        f32x4 piece[KD / 16];
+        u32x4 piece[Slab::N];
 #pragma unroll
-        for (int j = 0; j < KD / 16; ++j)
-            piece[j] = __builtin_nontemporal_load(slab + j * 16 * (VD / 4));
+        for (int j = 0; j < Slab::N; ++j)
+            piece[j] = slab.load(j);
         __builtin_amdgcn_sched_barrier(0);
         hg.load(p, hv, row0, cp);
         // token j < PF, or the last token again for j >= T (a harmless repeat
@@ -986,13 +1037,13 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
             load_pair<RAWG>(in[j], p, j < T ? bos + j : eos - 1, h, hv, row0, cp, col);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < KD / 16; ++j)
-            *reinterpret_cast<f32x4 *>(&stage[lds_at(16 * j + r16, c4)]) = piece[j];
+        for (int j = 0; j < Slab::N; ++j)
+            slab.to_lds(stage, j, piece[j]);
     }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < Q_ROWS; ++i)
-        s[i] = stage[lds_at(row0 + i, 16 * wave + cp)];
+        s[i] = stage[Slab::lds_at(row0 + i, 16 * wave + cp)];
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
         if (j < T) {
@@ -1009,12 +1060,11 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < Q_ROWS; ++i)
-        stage[lds_at(row0 + i, 16 * wave + cp)] = s[i];
+        stage[Slab::lds_at(row0 + i, 16 * wave + cp)] = s[i];
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < KD / 16; ++j)
-        __builtin_nontemporal_store(*reinterpret_cast<const f32x4 *>(&stage[lds_at(16 * j + r16, c4)]),
-                                    slab + j * 16 * (VD / 4));
+    for (int j = 0; j < Slab::N; ++j)
+        slab.store_from_lds(stage, j);
 }
 
 // Metadata check for KDA_FLAG_VALIDATE: one workgroup, lowest error code wins.
@@ -1272,24 +1322,29 @@ int32_t plan_vtile(int64_t units, int32_t T, bool norm)
     return 128;
 }
 
-// 16-column waves (kda_decode_q_kernel) for an fp32 pool without the norm:
+// 16-column waves (kda_decode_q_kernel) for step calls without the norm:
 // 0 = not used, else waves per workgroup.  They pay off where the per-token
 // chain, not the tile stream, sets the time.  Measured on MI355X with cold
-// caches against the 32-column kernel (H = 8): with one token per request
-// they win up to 64 tiles (N8: 3.88 vs 3.99 us) and lose from 128 (N16: 4.95
-// vs 4.75); with two or more tokens they win or tie up to 512 tiles (T = 2:
-// N16 5.52 vs 6.07, N32 7.78 vs 7.86, N64 12.54 vs 14.19; T = 4: N32 9.50
-// vs 10.17, N64 14.29 vs 16.38) and lose at 1024 (N128/T4: 30.6 vs 29.7).
-// Two waves per workgroup below 128 tiles, four from 128.
-int32_t plan_quarter_waves(int64_t units, int32_t T)
+// caches against the 32-column kernel (H = 8), fp32 pool: with one token
+// per request they win up to 64 tiles (N8: 3.88 vs 3.99 us) and lose from
+// 128 (N16: 4.95 vs 4.75); with two or more tokens they win or tie up to
+// 512 tiles (T = 2: N16 5.52 vs 6.07, N32 7.78 vs 7.86, N64 12.54 vs 14.19;
+// T = 4: N32 9.50 vs 10.17, N64 14.29 vs 16.38) and lose at 1024 (N128/T4:
+// 30.6 vs 29.7).  Two waves per workgroup below 128 tiles, four from 128.
+// bf16 pool: four waves (64 columns: full 128-byte row pieces of bf16) win
+// at every token count up to 512 tiles (T = 1: N32 5.12 vs 5.89, N64 7.21 vs
+// 8.78; T = 4: N32 7.46 vs 9.98).
+int32_t plan_quarter_waves(int64_t units, int32_t T, bool bf16)
 {
+    if (bf16)
+        return units <= 512 ? 4 : 0;
     const int64_t limit = T == 1 ? 64 : 512;
     if (units > limit)
         return 0;
     return units < 128 ? 2 : 4;
 }
 
-template <int NQ, int PF, bool RAWG>
+template <int NQ, int PF, bool RAWG, bool BF16S>
 kda_status launch_q(const DecodeParams &p, int64_t units, hipStream_t stream)
 {
     const int64_t blocks = units * (8 / NQ);
@@ -1302,26 +1357,26 @@ kda_status launch_q(const DecodeParams &p, int64_t units, hipStream_t stream)
     const int32_t *status = p.status;
     void *args[] = {&slot_idx, &cu_seqlens, &state, &slot_stride, &num_slots, &HV, &T, &status,
                     const_cast<DecodeParams *>(&p)};
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&kda_decode_q_kernel<NQ, PF, RAWG>),
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&kda_decode_q_kernel<NQ, PF, RAWG, BF16S>),
                                          dim3((uint32_t)blocks), dim3(64 * NQ), args, 0, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
-template <int NQ, bool RAWG>
+template <int NQ, bool RAWG, bool BF16S>
 kda_status dispatch_q_tokens(const DecodeParams &p, int64_t units, hipStream_t s)
 {
     switch (p.T) {
-    case 1: return launch_q<NQ, 1, RAWG>(p, units, s);
-    case 2: return launch_q<NQ, 2, RAWG>(p, units, s);
-    case 3: return launch_q<NQ, 3, RAWG>(p, units, s);
-    default: return launch_q<NQ, 4, RAWG>(p, units, s);
+    case 1: return launch_q<NQ, 1, RAWG, BF16S>(p, units, s);
+    case 2: return launch_q<NQ, 2, RAWG, BF16S>(p, units, s);
+    case 3: return launch_q<NQ, 3, RAWG, BF16S>(p, units, s);
+    default: return launch_q<NQ, 4, RAWG, BF16S>(p, units, s);
     }
 }
 
-template <bool RAWG>
+template <bool RAWG, bool BF16S>
 kda_status dispatch_q(const DecodeParams &p, int64_t units, int nq, hipStream_t s)
 {
-    return nq == 2 ? dispatch_q_tokens<2, RAWG>(p, units, s) : dispatch_q_tokens<4, RAWG>(p, units, s);
+    return nq == 2 ? dispatch_q_tokens<2, RAWG, BF16S>(p, units, s) : dispatch_q_tokens<4, RAWG, BF16S>(p, units, s);
 }
 
 template <int NW, bool NORM, bool BF16S, bool RAWG>
@@ -1384,9 +1439,9 @@ kda_status run_decode(const kda_decode_args *a, int32_t T, const int32_t *cu_seq
     const bool bf16_pool = (flags & KDA_FLAG_STATE_BF16) != 0;
     const int64_t units = (int64_t)a->N * a->HV;
     int vtile = vtile_from_flags(flags);
-    // a forced width keeps the 32-column waves; otherwise step calls on an
-    // fp32 pool without the norm may take the 16-column waves
-    const int nq = (vtile == 0 && !cu_seqlens && !norm && !bf16_pool) ? plan_quarter_waves(units, T) : 0;
+    // a forced width keeps the 32-column waves; otherwise step calls without
+    // the norm may take the 16-column waves
+    const int nq = (vtile == 0 && !cu_seqlens && !norm) ? plan_quarter_waves(units, T, bf16_pool) : 0;
     if (vtile == 0)
         vtile = plan_vtile(units, cu_seqlens ? 1 : T, norm);
     if (norm && vtile != 128)
@@ -1445,8 +1500,11 @@ kda_status run_decode(const kda_decode_args *a, int32_t T, const int32_t *cu_seq
                             vargs, 0, s) != hipSuccess)
             return KDA_ERR_LAUNCH;
     }
-    if (nq)
-        return a->raw_gate ? dispatch_q<true>(p, units, nq, s) : dispatch_q<false>(p, units, nq, s);
+    if (nq) {
+        if (bf16_pool)
+            return a->raw_gate ? dispatch_q<true, true>(p, units, nq, s) : dispatch_q<false, true>(p, units, nq, s);
+        return a->raw_gate ? dispatch_q<true, false>(p, units, nq, s) : dispatch_q<false, false>(p, units, nq, s);
+    }
     // 32-column waves.  Packed batches: the staged body; step calls with
     // several tokens per request, fewer than 512 tiles (two per compute
     // unit), the fused gate activation or a bf16 pool: the peeled body (its
@@ -1518,7 +1576,7 @@ kda_status kda_gated_rmsnorm(const void *x, const void *gate, const void *weight
 
 int32_t kda_decode_plan(int64_t units, int32_t T, int32_t has_norm)
 {
-    const int32_t nq = has_norm ? 0 : plan_quarter_waves(units, T);
+    const int32_t nq = has_norm ? 0 : plan_quarter_waves(units, T, false);
     return nq ? 16 * nq : plan_vtile(units, T, has_norm != 0);
 }
 

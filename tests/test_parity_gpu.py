@@ -141,11 +141,13 @@ def test_bf16_state_small_cases(case):
 
 
 def test_bf16_state_tile_widths_bit_identical():
+    """The library's choice (16-column waves with a bf16 pool at this shape)
+    and every forced width of the 32-column kernel give the same bits."""
     p = ki.workload("n32_t1_h8")
     results = []
-    for width in (32, 64, 128):
+    for width in (0, 32, 64, 128):
         d = upload(p, state_dtype=torch.bfloat16)
-        run_gpu(d, flags=kda.KDA_FLAG_VTILE(width))
+        run_gpu(d, flags=kda.KDA_FLAG_VTILE(width) if width else 0)
         torch.cuda.synchronize()
         results.append((d.out.view(torch.int16).clone(), d.state.view(torch.int16).clone()))
     for o, s_ in results[1:]:
@@ -709,6 +711,29 @@ def test_quarter_waves_match_wide_waves_bitwise(case):
             assert np.all(np.abs(got[live_rows] - ref_inter[live_rows]) <= 1e-4 * np.abs(ref_inter[live_rows]) + 1e-6)
             assert np.all(got[~live_rows] == 1232.0)
         results.append((d.out.view(torch.int16).clone(), d.state.clone(), inter))
+    for o, st, it in results[1:]:
+        assert torch.equal(o, results[0][0]) and torch.equal(st, results[0][1]) and torch.equal(it, results[0][2])
+
+
+@pytest.mark.parametrize("case", [(1, 8, 8, 1, False), (9, 4, 8, 3, True), (20, 4, 8, 4, False),
+                                  (7, 2, 4, 6, False), (64, 8, 8, 1, False)])
+def test_quarter_waves_bf16_pool_match_wide_waves_bitwise(case):
+    """bf16 pool: the 16-column waves (64-column workgroups, widened exactly
+    into LDS, rounded once on the way out) against the forced 32-column
+    kernel, bit for bit with per-token states; and against the oracle."""
+    N, H, HV, T, raw = case
+    p = ki.make_problem("quarterbf", 400 + N, N=N, H=H, HV=HV, K=128, V=128, num_slots=2 * N + 3, T=T,
+                        n_pad=N // 4, raw_gates=raw)
+    results = []
+    for flags in (0, kda.KDA_FLAG_VTILE(32), kda.KDA_FLAG_VTILE(128)):
+        d = upload(p, background_seed=1234, state_dtype=torch.bfloat16)
+        inter = torch.full((p.tokens, p.HV, p.K, p.V), 1232.0, dtype=torch.bfloat16, device=DEV)
+        run_gpu(d, flags=flags, inter_state=inter)
+        torch.cuda.synchronize()
+        if flags == 0:
+            _log(f"quarter waves bf16 {case}", compare(d, *run_oracle(p, state_bf16=True)))
+        results.append((d.out.view(torch.int16).clone(), d.state.view(torch.int16).clone(),
+                        inter.view(torch.int16).clone()))
     for o, st, it in results[1:]:
         assert torch.equal(o, results[0][0]) and torch.equal(st, results[0][1]) and torch.equal(it, results[0][2])
 
