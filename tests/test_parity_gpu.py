@@ -514,6 +514,23 @@ def test_validate_rejects_and_touches_nothing(case):
     assert torch.all(d.out.view(torch.int16) == np.int16(np.uint16(0xC640).view(np.int16)))
 
 
+@pytest.mark.parametrize("case", ["duplicate", "past_pool"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_validate_rejects_on_quarter_waves(case, dtype):
+    """The 16-column waves (a step call of 64 tiles, four tokens) honour the
+    verdict too: nothing written."""
+    p = ki.workload("n8_t4_h8")
+    code = _corrupt(p, case)
+    d = upload(p, state_dtype=dtype)
+    before = d.state.clone()
+    st = _status_word()
+    run_gpu(d, device_status=st)
+    torch.cuda.synchronize()
+    assert st.item() == code
+    assert torch.equal(d.state, before)
+    assert torch.all(d.out.view(torch.int16) == np.int16(np.uint16(0xC640).view(np.int16)))
+
+
 def test_validate_rejects_cu_seqlens_past_the_tokens():
     """cu_seqlens[N] beyond total_tokens: the call is given fewer token rows
     than the tensors hold, so even an unvalidated run would stay in bounds."""
@@ -805,8 +822,9 @@ def test_deterministic_and_non_default_stream():
     assert torch.equal(d1.out.view(torch.int16), d2.out.view(torch.int16))
 
 
-def test_graph_replay_matches_eager():
-    p = ki.workload("n32_t1_h8")
+@pytest.mark.parametrize("name", ["n32_t1_h8", "n8_t4_h8"])
+def test_graph_replay_matches_eager(name):
+    p = ki.workload(name)
     eager = _fresh(p)
     run_gpu(eager)
     torch.cuda.synchronize()
