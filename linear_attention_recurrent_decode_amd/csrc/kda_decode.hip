@@ -919,9 +919,9 @@ __device__ __forceinline__ void advance_pair(float (&s)[Q_ROWS], const PairIn &i
 // elements per lane and access, so 16 (fp32) or 32 (bf16) rows per
 // instruction across the workgroup's 4C lanes, N pieces per lane.  In LDS
 // the tile is fp32 either way (bf16 widened exactly on the way in, rounded
-// to nearest even on the way out), row r at dword r C + 16 (r / 32): the
-// pad puts the 4 row quarters that one column read touches on disjoint
-// 16-bank groups.
+// to nearest even on the way out), row r at dword r C + 16 (r / 32): rows
+// 32 apart would otherwise sit in the same banks, and the pad puts the 4 row
+// quarters that one column read touches 16 banks apart.
 template <int C, bool BF16S>
 struct SlabIO {
     static constexpr int ELEMS = BF16S ? 8 : 4;            // elements per 16-byte piece
@@ -1030,8 +1030,8 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
             piece[j] = slab.load(j);
         __builtin_amdgcn_sched_barrier(0);
         hg.load(p, hv, row0, cp);
-        // token j < PF, or the last token again for j >= T (a harmless repeat
-        // that keeps the loads unconditional)
+        // the host picks PF = min(T, 4); the clamp only keeps a row index
+        // inside the call should a kernel run with PF > T
 #pragma unroll
         for (int j = 0; j < PF; ++j)
             load_pair<RAWG>(in[j], p, j < T ? bos + j : eos - 1, h, hv, row0, cp, col);
