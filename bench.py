@@ -314,7 +314,7 @@ def main():
                    "norm": p.gate is not None, "state_dtype": args.state,
                    "gate_input": "raw, activated in the kernel" if p.raw else "activated",
                    "cold_slot_sets": len(sets), "cold_pool_copies": R,
-                   "vtile": kda.kda_decode_plan(p.N * p.HV, T or 1, p.gate is not None)},
+                   "vtile": kda.kda_decode_plan(p.N * p.HV, T or 1, p.gate is not None, bf16_state, packed)},
         "state_GBps": round(state_gbps, 1),
         "state_frac_of_peak": round(state_gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_call": nbytes["total"],

@@ -81,7 +81,7 @@ typedef enum kda_status {
 
 /* flags: bits 8..9 force the value-tile width of one workgroup
  * (1 = 32 columns, 2 = 64, 3 = 128; 0 = the library's choice) of 32-column
- * waves; the library's choice may instead use 16-column waves (step calls
+ * waves; the library's choice may instead use 16-column waves (calls
  * without the norm).  Results are bit-identical for every width and wave
  * layout; the knob exists for tests and tuning. */
 #define KDA_FLAG_VTILE_SHIFT 8u
@@ -211,13 +211,16 @@ kda_status kda_decode_packed(const kda_decode_args *args, const int32_t *cu_seql
 kda_status kda_gated_rmsnorm(const void *x, const void *gate, const void *weight, void *y,
                              int64_t rows, int32_t V, float eps, void *stream);
 
-/* The value-tile width (32, 64 or 128 columns per workgroup) the library
- * picks for a step call on an fp32 pool with `units` = N*HV (request, value
- * head) pairs, T tokens and with or without the norm epilogue.  Host-only,
- * no device access.  (Packed calls plan as T = 1; with a bf16 pool step
- * calls without the norm take 64-column workgroups of 16-column waves up to
- * 512 units.) */
-int32_t kda_decode_plan(int64_t units, int32_t T, int32_t has_norm);
+/* options of kda_decode_plan (bit set; 0 = fp32 pool, step call, no norm) */
+#define KDA_PLAN_NORM 1u         /* the gated RMSNorm epilogue */
+#define KDA_PLAN_STATE_BF16 2u   /* a bf16 state pool (KDA_FLAG_STATE_BF16) */
+#define KDA_PLAN_PACKED 4u       /* a packed call (kda_decode_packed) */
+
+/* The columns per workgroup (32, 64 or 128) the library picks for a call of
+ * `units` = N*HV (request, value head) pairs with T tokens per request (any
+ * T >= 1 for a packed call) and the given KDA_PLAN_* options; without a
+ * forced KDA_FLAG_VTILE width.  Host-only, no device access. */
+int32_t kda_decode_plan(int64_t units, int32_t T, uint32_t options);
 
 /* Static description of a status code. */
 const char *kda_status_string(kda_status status);

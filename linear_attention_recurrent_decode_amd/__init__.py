@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "KdaError", "KdaDecodeArgs", "library", "library_path",
     "kda_decode_step", "kda_decode_packed", "kda_gated_rmsnorm",
-    "kda_decode_plan", "kda_status_string", "decode_args",
+    "kda_decode_plan", "KDA_PLAN_NORM", "KDA_PLAN_STATE_BF16", "KDA_PLAN_PACKED", "kda_status_string", "decode_args",
     "KDA_FLAG_VTILE", "KDA_FLAG_STATE_BF16", "KDA_FLAG_VALIDATE", "KDA_DEVICE_STATUS",
 ]
 
@@ -96,7 +96,7 @@ def library() -> ctypes.CDLL:
     lib.kda_gated_rmsnorm.restype = ctypes.c_int
     lib.kda_gated_rmsnorm.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p]
     lib.kda_decode_plan.restype = ctypes.c_int32
-    lib.kda_decode_plan.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+    lib.kda_decode_plan.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -107,8 +107,17 @@ def kda_status_string(status: int) -> str:
     return library().kda_status_string(int(status)).decode()
 
 
-def kda_decode_plan(units: int, T: int = 1, has_norm: bool = False) -> int:
-    return int(library().kda_decode_plan(int(units), int(T), int(bool(has_norm))))
+KDA_PLAN_NORM = 1
+KDA_PLAN_STATE_BF16 = 2
+KDA_PLAN_PACKED = 4
+
+
+def kda_decode_plan(units: int, T: int = 1, has_norm: bool = False, bf16_state: bool = False,
+                    packed: bool = False) -> int:
+    """Columns per workgroup the library picks (include/kda.h, kda_decode_plan)."""
+    options = ((KDA_PLAN_NORM if has_norm else 0) | (KDA_PLAN_STATE_BF16 if bf16_state else 0)
+               | (KDA_PLAN_PACKED if packed else 0))
+    return int(library().kda_decode_plan(int(units), int(T), options))
 
 
 def _stream(stream) -> Optional[int]:

@@ -967,7 +967,8 @@ struct SlabIO {
 };
 
 // No norm epilogue; NQ waves of 16 columns per workgroup; fp32 or bf16
-// pool (BF16S).  The inputs of the first PF tokens are loaded with the tile
+// pool (BF16S); step calls (T tokens per request) or packed ones
+// (cu_seqlens).  The inputs of the first PF tokens are loaded with the tile
 // (later tokens, if any, load at the top of their iteration).
 template <int NQ, int PF, bool RAWG, bool BF16S>
 __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *slot_idx, const int32_t *cu_seqlens,
@@ -992,7 +993,17 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
         return;
     if (slot < 0 || slot >= num_slots)
         return;
-    const int64_t bos = req * T, eos = bos + T;
+    int64_t bos, eos;
+    if (cu_seqlens) {
+        bos = cu_seqlens[req];
+        eos = cu_seqlens[req + 1];
+    } else {
+        bos = req * T;
+        eos = bos + T;
+    }
+    if (eos <= bos)
+        return;
+    const int64_t ntok = eos - bos;
     const int h = qk_head(p, hv);
 
     const int cp = lane & 15;             // column within the wave; owner of row pair cp
@@ -1030,11 +1041,11 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
             piece[j] = slab.load(j);
         __builtin_amdgcn_sched_barrier(0);
         hg.load(p, hv, row0, cp);
-        // the host picks PF = min(T, 4); the clamp only keeps a row index
-        // inside the call should a kernel run with PF > T
+        // token j, or for a request shorter than PF (packed calls) its last
+        // token again: a harmless repeat that keeps the loads unconditional
 #pragma unroll
         for (int j = 0; j < PF; ++j)
-            load_pair<RAWG>(in[j], p, j < T ? bos + j : eos - 1, h, hv, row0, cp, col);
+            load_pair<RAWG>(in[j], p, j < ntok ? bos + j : eos - 1, h, hv, row0, cp, col);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < Slab::N; ++j)
@@ -1046,7 +1057,7 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
         s[i] = stage[Slab::lds_at(row0 + i, 16 * wave + cp)];
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
-        if (j < T) {
+        if (j < ntok) {
             advance_pair<RAWG>(s, in[j], p, hg, bos + j, hv, rq, col);
             keep_state(bos + j);
         }
@@ -1332,12 +1343,16 @@ int32_t plan_vtile(int64_t units, int32_t T, bool norm)
 // T = 4: N32 9.50 vs 10.17, N64 14.29 vs 16.38) and lose at 1024 (N128/T4:
 // 30.6 vs 29.7).  Two waves per workgroup below 128 tiles, four from 128.
 // bf16 pool: four waves (64 columns: full 128-byte row pieces of bf16) win
-// at every token count up to 512 tiles (T = 1: N32 5.12 vs 5.89, N64 7.21 vs
-// 8.78; T = 4: N32 7.46 vs 9.98).
+// at every size and token count, step or packed (T = 1: N32 5.12 vs 5.89,
+// N128 15.8 vs 20.6; T = 4: N32 7.46 vs 9.98; the packed H12 batch 40.9 vs
+// 50.7), where the 32-column kernel moves half lines of bf16.
+// Step calls only with an fp32 pool (T = 0 stands for a packed call).
 int32_t plan_quarter_waves(int64_t units, int32_t T, bool bf16)
 {
     if (bf16)
-        return units <= 512 ? 4 : 0;
+        return 4;
+    if (T == 0)
+        return 0;
     const int64_t limit = T == 1 ? 64 : 512;
     if (units > limit)
         return 0;
@@ -1365,7 +1380,7 @@ kda_status launch_q(const DecodeParams &p, int64_t units, hipStream_t stream)
 template <int NQ, bool RAWG, bool BF16S>
 kda_status dispatch_q_tokens(const DecodeParams &p, int64_t units, hipStream_t s)
 {
-    switch (p.T) {
+    switch (p.cu_seqlens ? 4 : p.T) {
     case 1: return launch_q<NQ, 1, RAWG, BF16S>(p, units, s);
     case 2: return launch_q<NQ, 2, RAWG, BF16S>(p, units, s);
     case 3: return launch_q<NQ, 3, RAWG, BF16S>(p, units, s);
@@ -1439,9 +1454,9 @@ kda_status run_decode(const kda_decode_args *a, int32_t T, const int32_t *cu_seq
     const bool bf16_pool = (flags & KDA_FLAG_STATE_BF16) != 0;
     const int64_t units = (int64_t)a->N * a->HV;
     int vtile = vtile_from_flags(flags);
-    // a forced width keeps the 32-column waves; otherwise step calls without
-    // the norm may take the 16-column waves
-    const int nq = (vtile == 0 && !cu_seqlens && !norm) ? plan_quarter_waves(units, T, bf16_pool) : 0;
+    // a forced width keeps the 32-column waves; otherwise calls without the
+    // norm may take the 16-column waves
+    const int nq = (vtile == 0 && !norm) ? plan_quarter_waves(units, cu_seqlens ? 0 : T, bf16_pool) : 0;
     if (vtile == 0)
         vtile = plan_vtile(units, cu_seqlens ? 1 : T, norm);
     if (norm && vtile != 128)
@@ -1574,10 +1589,11 @@ kda_status kda_gated_rmsnorm(const void *x, const void *gate, const void *weight
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
-int32_t kda_decode_plan(int64_t units, int32_t T, int32_t has_norm)
+int32_t kda_decode_plan(int64_t units, int32_t T, uint32_t options)
 {
-    const int32_t nq = has_norm ? 0 : plan_quarter_waves(units, T, false);
-    return nq ? 16 * nq : plan_vtile(units, T, has_norm != 0);
+    const bool norm = (options & KDA_PLAN_NORM) != 0, packed = (options & KDA_PLAN_PACKED) != 0;
+    const int32_t nq = norm ? 0 : plan_quarter_waves(units, packed ? 0 : T, (options & KDA_PLAN_STATE_BF16) != 0);
+    return nq ? 16 * nq : plan_vtile(units, packed ? 1 : T, norm);
 }
 
 const char *kda_status_string(kda_status status)

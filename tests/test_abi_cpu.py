@@ -74,6 +74,14 @@ def test_status_strings_and_plan():
               (8, 4): 32, (127, 4): 32, (128, 4): 64, (512, 4): 64, (513, 4): 128, (384, 9): 64}
     for (units, T), width in expect.items():
         assert kda.kda_decode_plan(units, T, False) == width, (units, T)
+    # packed calls: 32-column waves with an fp32 pool; with a bf16 pool every
+    # call without the norm takes 64-column workgroups of 16-column waves
+    for units, width in ((8, 32), (256, 64), (3072, 128)):
+        assert kda.kda_decode_plan(units, 4, packed=True) == width
+        for T in (1, 4):
+            assert kda.kda_decode_plan(units, T, bf16_state=True) == 64
+            assert kda.kda_decode_plan(units, T, bf16_state=True, packed=True) == 64
+            assert kda.kda_decode_plan(units, T, True, bf16_state=True) == 128
 
 
 BASE = 0x7F0000000000

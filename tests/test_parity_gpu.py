@@ -733,14 +733,16 @@ def test_quarter_waves_match_wide_waves_bitwise(case):
 
 
 @pytest.mark.parametrize("case", [(1, 8, 8, 1, False), (9, 4, 8, 3, True), (20, 4, 8, 4, False),
-                                  (7, 2, 4, 6, False), (64, 8, 8, 1, False)])
+                                  (7, 2, 4, 6, False), (64, 8, 8, 1, False), (40, 4, 4, None, False),
+                                  (25, 2, 6, None, True)])
 def test_quarter_waves_bf16_pool_match_wide_waves_bitwise(case):
     """bf16 pool: the 16-column waves (64-column workgroups, widened exactly
-    into LDS, rounded once on the way out) against the forced 32-column
-    kernel, bit for bit with per-token states; and against the oracle."""
+    into LDS, rounded once on the way out), step and packed (T None: 1 to 6
+    tokens per request), against the forced 32-column kernel, bit for bit
+    with per-token states; and against the oracle."""
     N, H, HV, T, raw = case
     p = ki.make_problem("quarterbf", 400 + N, N=N, H=H, HV=HV, K=128, V=128, num_slots=2 * N + 3, T=T,
-                        n_pad=N // 4, raw_gates=raw)
+                        t_max=6, n_pad=N // 4, raw_gates=raw)
     results = []
     for flags in (0, kda.KDA_FLAG_VTILE(32), kda.KDA_FLAG_VTILE(128)):
         d = upload(p, background_seed=1234, state_dtype=torch.bfloat16)
