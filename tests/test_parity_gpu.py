@@ -126,7 +126,8 @@ def test_packed_and_step_bodies_bit_identical():
 
 
 # ------------------------------------------------------- bf16 state pool
-@pytest.mark.parametrize("name", ["n1_t1_h8", "n32_t1_h8", "n8_t4_h8", "n32_t1_h16_norm", "packed_n256_h12"])
+@pytest.mark.parametrize("name", ["n1_t1_h8", "n32_t1_h8", "n1_t4_h8", "n8_t4_h8", "n32_t4_h8", "n32_t1_h16_norm",
+                                  "packed_n256_h12", "packed_n256_h12_rawgate"])
 def test_bf16_state_workloads(name):
     p = ki.workload(name)
     _log(f"{name} bf16 state", parity(p, state_dtype=torch.bfloat16))
