@@ -1012,26 +1012,32 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
     const int row0 = rq * Q_ROWS;
 
     float s[Q_ROWS];
-    // per-token states: each lane writes its column (one element per row)
-    auto keep_state = [&](int64_t t) {
-        if (p.inter_state) {
-            const int64_t at = t * p.inter_stride + (int64_t)hv * (KD * VD) + (int64_t)row0 * VD + col;
-#pragma unroll
-            for (int i = 0; i < Q_ROWS; ++i) {
-                if constexpr (BF16S)
-                    __builtin_nontemporal_store((uint16_t)pack_bf16x2(s[i], 0.0f),
-                                                static_cast<uint16_t *>(p.inter_state) + at + i * VD);
-                else
-                    __builtin_nontemporal_store(s[i], static_cast<float *>(p.inter_state) + at + i * VD);
-            }
-        }
-    };
     // The tile streams through LDS with 16-byte accesses over full row
     // pieces, and each lane takes its column of 32 rows from there.
     constexpr int C = 16 * NQ;
     using Slab = SlabIO<C, BF16S>;
     __shared__ float stage[KD * C + 4 * 16];
     const Slab slab(state, slot * slot_stride + (int64_t)hv * (KD * VD) + vt * C, (int)threadIdx.x);
+    // the lanes' columns back into the staged tile (every wave is done with
+    // its previous contents first)
+    auto stage_columns = [&]() {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < Q_ROWS; ++i)
+            stage[Slab::lds_at(row0 + i, 16 * wave + cp)] = s[i];
+        __syncthreads();
+    };
+    // per-token states leave through LDS as full row pieces too
+    // (p.inter_state is uniform, so every wave reaches the barriers)
+    auto keep_state = [&](int64_t t) {
+        if (p.inter_state) {
+            stage_columns();
+            const Slab it(p.inter_state, t * p.inter_stride + (int64_t)hv * (KD * VD) + vt * C, (int)threadIdx.x);
+#pragma unroll
+            for (int j = 0; j < Slab::N; ++j)
+                it.store_from_lds(stage, j);
+        }
+    };
     HeadGate<RAWG> hg;
     PairIn in[PF];
     {
@@ -1067,12 +1073,8 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
         advance_pair<RAWG>(s, in[0], p, hg, t, hv, rq, col);
         keep_state(t);
     }
-    // back through LDS (every wave is done reading its column first)
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < Q_ROWS; ++i)
-        stage[Slab::lds_at(row0 + i, 16 * wave + cp)] = s[i];
-    __syncthreads();
+    // back through LDS
+    stage_columns();
 #pragma unroll
     for (int j = 0; j < Slab::N; ++j)
         slab.store_from_lds(stage, j);
