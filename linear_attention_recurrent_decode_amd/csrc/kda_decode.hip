@@ -184,6 +184,7 @@ struct TileIO {
 constexpr int DPP_ROW_ROR8 = 0x128;          // lane l <- l^8 within its 16-lane row
 constexpr int DPP_ROW_HALF_MIRROR = 0x141;   // lane l <- 7 - l within its 8-lane half row
 constexpr int DPP_ROW_MIRROR = 0x140;        // lane l <- 15 - l within its 16-lane row
+constexpr int DPP_ROW_SR1 = 0x111;           // lane l <- l - 1 within its 16-lane row
 constexpr int DPP_QUAD_XOR1 = 0xB1;          // quad_perm [1,0,3,2]
 constexpr int DPP_QUAD_XOR2 = 0x4E;          // quad_perm [2,3,0,1]
 
@@ -799,9 +800,10 @@ struct PairIn {
     float2 g;
     uint32_t v;
     float beta;
+    uint32_t z;   // the norm epilogue's gate of the lane's column (NORM)
 };
 
-template <bool RAWG>
+template <bool NORM, bool RAWG>
 __device__ __forceinline__ void load_pair(PairIn &in, const DecodeParams &p, int64_t t, int h, int hv, int row0,
                                           int cp, int col)
 {
@@ -816,6 +818,8 @@ __device__ __forceinline__ void load_pair(PairIn &in, const DecodeParams &p, int
         in.beta = p.beta[t * p.beta_stride + hv];
     }
     in.v = p.v[t * p.v_stride + (int64_t)hv * VD + col];
+    if constexpr (NORM)
+        in.z = p.gate[t * p.gate_stride + (int64_t)hv * VD + col];
 }
 
 // Partial sums over rows 8B .. 8B+7 of the lane's quarter, whose owners are
@@ -866,10 +870,19 @@ __device__ __forceinline__ void quarter_update8(float (&s)[Q_ROWS], float a_lo, 
 }
 
 // Advance the lane's column of its row quarter by one token and write its
-// output (the same recurrence as advance_token).
-template <bool RAWG>
+// output (the same recurrence as advance_token).  With the norm epilogue
+// (NORM, 8 waves: the workgroup holds the head's 128 columns) the sum of o^2
+// is formed in the 32-column kernel's order: per group of 4 columns the
+// chain fmaf(o3, o3, fmaf(o2, o2, fmaf(o1, o1, o0 o0))), which here runs
+// across the group's 4 lanes by DPP row shifts; then per 32 columns the
+// tree ((C0 + C7) + (C1 + C6)) + ((C2 + C5) + (C3 + C4)) over the 8 group
+// sums C, and over the 4 such parts (P0 + P1) + (P2 + P3).  The group sums
+// meet in LDS (norm_c, double-buffered by token parity: one barrier per
+// token) and every lane evaluates the tree itself.
+template <bool NORM, bool RAWG>
 __device__ __forceinline__ void advance_pair(float (&s)[Q_ROWS], const PairIn &in, const DecodeParams &p,
-                                             const HeadGate<RAWG> &hg, int64_t t, int hv, int rq, int col)
+                                             const HeadGate<RAWG> &hg, int64_t t, int hv, int rq, int col,
+                                             int wave, int cp, float nw, float *norm_c)
 {
     const float k_lo = bf16_lo(in.k), k_hi = bf16_hi(in.k), q_lo = bf16_lo(in.q), q_hi = bf16_hi(in.q);
     float b, g_lo, g_hi;
@@ -905,11 +918,30 @@ __device__ __forceinline__ void advance_pair(float (&s)[Q_ROWS], const PairIn &i
     const float w = add_permlane32_swap(add_permlane16_swap(w_lo + w_hi));
 
     const float vp = b * (bf16_lo(in.v) - u);
-    const float o = p.scale * fmaf(vp, kq, w);
+    float o = p.scale * fmaf(vp, kq, w);
     quarter_update8<0>(s, a_lo, a_hi, k_lo, k_hi, vp);
     quarter_update8<1>(s, a_lo, a_hi, k_lo, k_hi, vp);
     quarter_update8<2>(s, a_lo, a_hi, k_lo, k_hi, vp);
     quarter_update8<3>(s, a_lo, a_hi, k_lo, k_hi, vp);
+    if constexpr (NORM) {
+        const float x1 = fmaf(o, o, KDA_DPP(o * o, DPP_ROW_SR1));
+        const float x2 = fmaf(o, o, KDA_DPP(x1, DPP_ROW_SR1));
+        const float x3 = fmaf(o, o, KDA_DPP(x2, DPP_ROW_SR1));   // the group sum, in lane 4m + 3
+        float *part = norm_c + (t & 1) * 32;
+        if (rq == 0 && (cp & 3) == 3)
+            part[4 * wave + (cp >> 2)] = x3;
+        __syncthreads();
+        float P[4];
+#pragma unroll
+        for (int q32 = 0; q32 < 4; ++q32) {
+            const f32x4 lo = *reinterpret_cast<const f32x4 *>(part + 8 * q32);
+            const f32x4 hi = *reinterpret_cast<const f32x4 *>(part + 8 * q32 + 4);
+            P[q32] = ((lo.x + hi.w) + (lo.y + hi.z)) + ((lo.z + hi.y) + (lo.w + hi.x));
+        }
+        const float total = (P[0] + P[1]) + (P[2] + P[3]);
+        const float r = rsqrtf(fmaf(total, 1.0f / VD, p.eps));
+        o = o * r * nw * silu(bf16_lo(in.z));
+    }
     if (rq == 0)
         p.out[t * p.out_stride + (int64_t)hv * VD + col] = (uint16_t)pack_bf16x2(o, 0.0f);
 }
@@ -966,17 +998,20 @@ struct SlabIO {
     }
 };
 
-// No norm epilogue; NQ waves of 16 columns per workgroup; fp32 or bf16
-// pool (BF16S); step calls (T tokens per request) or packed ones
-// (cu_seqlens).  The inputs of the first PF tokens are loaded with the tile
-// (later tokens, if any, load at the top of their iteration).
-template <int NQ, int PF, bool RAWG, bool BF16S>
+// NQ waves of 16 columns per workgroup; the norm epilogue (NORM) with 8
+// waves only; fp32 or bf16 pool (BF16S); step calls (T tokens per request)
+// or packed ones (cu_seqlens).  The inputs of the first PF tokens are loaded
+// with the tile (later tokens, if any, load at the top of their iteration).
+// LDS is dynamic: the staged tile (C = 16 NQ columns) plus 64 floats for
+// the norm's group sums.
+template <int NQ, int PF, bool NORM, bool RAWG, bool BF16S>
 __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *slot_idx, const int32_t *cu_seqlens,
                                                                void *state, int64_t slot_stride, int64_t num_slots,
                                                                int32_t HV, int32_t T, const int32_t *status,
                                                                DecodeParams p)
 {
-    static_assert(NQ == 2 || NQ == 4, "a workgroup is 2 or 4 waves of 16 columns");
+    static_assert(NQ == 2 || NQ == 4 || NQ == 8, "a workgroup is 2, 4 or 8 waves of 16 columns");
+    static_assert(!NORM || NQ == 8, "the norm epilogue needs all 128 columns in one workgroup");
     static_assert(PF >= 1 && PF <= 4, "up to 4 tokens' inputs ahead");
     constexpr int NVT = 8 / NQ;   // value tiles per head
 
@@ -1016,7 +1051,8 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
     // pieces, and each lane takes its column of 32 rows from there.
     constexpr int C = 16 * NQ;
     using Slab = SlabIO<C, BF16S>;
-    __shared__ float stage[KD * C + 4 * 16];
+    extern __shared__ float stage[];        // KD * C + 64 floats, then 64 for the norm
+    float *norm_c = stage + KD * C + 64;
     const Slab slab(state, slot * slot_stride + (int64_t)hv * (KD * VD) + vt * C, (int)threadIdx.x);
     // the lanes' columns back into the staged tile (every wave is done with
     // its previous contents first)
@@ -1040,6 +1076,9 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
     };
     HeadGate<RAWG> hg;
     PairIn in[PF];
+    float nw = 0.0f;
+    if constexpr (NORM)
+        nw = bf16_lo(p.norm_weight[col]);
     {
         u32x4 piece[Slab::N];
 #pragma unroll
@@ -1051,7 +1090,7 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
         // token again: a harmless repeat that keeps the loads unconditional
 #pragma unroll
         for (int j = 0; j < PF; ++j)
-            load_pair<RAWG>(in[j], p, j < ntok ? bos + j : eos - 1, h, hv, row0, cp, col);
+            load_pair<NORM, RAWG>(in[j], p, j < ntok ? bos + j : eos - 1, h, hv, row0, cp, col);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < Slab::N; ++j)
@@ -1064,13 +1103,13 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
         if (j < ntok) {
-            advance_pair<RAWG>(s, in[j], p, hg, bos + j, hv, rq, col);
+            advance_pair<NORM, RAWG>(s, in[j], p, hg, bos + j, hv, rq, col, wave, cp, nw, norm_c);
             keep_state(bos + j);
         }
     }
     for (int64_t t = bos + PF; t < eos; ++t) {
-        load_pair<RAWG>(in[0], p, t, h, hv, row0, cp, col);
-        advance_pair<RAWG>(s, in[0], p, hg, t, hv, rq, col);
+        load_pair<NORM, RAWG>(in[0], p, t, h, hv, row0, cp, col);
+        advance_pair<NORM, RAWG>(s, in[0], p, hg, t, hv, rq, col, wave, cp, nw, norm_c);
         keep_state(t);
     }
     // back through LDS
@@ -1349,8 +1388,15 @@ int32_t plan_vtile(int64_t units, int32_t T, bool norm)
 // N128 15.8 vs 20.6; T = 4: N32 7.46 vs 9.98; the packed H12 batch 40.9 vs
 // 50.7), where the 32-column kernel moves half lines of bf16.
 // Step calls only with an fp32 pool (T = 0 stands for a packed call).
-int32_t plan_quarter_waves(int64_t units, int32_t T, bool bf16)
+// With the norm epilogue (eight waves, the head's 128 columns in one
+// workgroup): every bf16-pool call (normed N64/H16 T=1 17.4 vs 20.1 us, N8
+// T=4 9.3 vs 10.8) and fp32 step calls with two or more tokens up to 512
+// tiles (N8/H16 T=4 10.0 vs 10.7, N32 18.8 vs 19.3); one-token fp32 calls
+// gain nothing (N32/H16 12.8-13.0 both) or lose (N16: 8.9 vs 7.8).
+int32_t plan_quarter_waves(int64_t units, int32_t T, bool bf16, bool norm)
 {
+    if (norm)
+        return (bf16 || (T >= 2 && units <= 512)) ? 8 : 0;
     if (bf16)
         return 4;
     if (T == 0)
@@ -1361,7 +1407,7 @@ int32_t plan_quarter_waves(int64_t units, int32_t T, bool bf16)
     return units < 128 ? 2 : 4;
 }
 
-template <int NQ, int PF, bool RAWG, bool BF16S>
+template <int NQ, int PF, bool NORM, bool RAWG, bool BF16S>
 kda_status launch_q(const DecodeParams &p, int64_t units, hipStream_t stream)
 {
     const int64_t blocks = units * (8 / NQ);
@@ -1374,26 +1420,37 @@ kda_status launch_q(const DecodeParams &p, int64_t units, hipStream_t stream)
     const int32_t *status = p.status;
     void *args[] = {&slot_idx, &cu_seqlens, &state, &slot_stride, &num_slots, &HV, &T, &status,
                     const_cast<DecodeParams *>(&p)};
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&kda_decode_q_kernel<NQ, PF, RAWG, BF16S>),
-                                         dim3((uint32_t)blocks), dim3(64 * NQ), args, 0, stream);
+    const void *fn = reinterpret_cast<const void *>(&kda_decode_q_kernel<NQ, PF, NORM, RAWG, BF16S>);
+    const size_t lds = (size_t)(KD * 16 * NQ + 128) * sizeof(float);
+    if (lds > 65536) {
+        // above the default limit of dynamic LDS: raise it once per kernel
+        static const hipError_t raised =
+            hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (raised != hipSuccess)
+            return KDA_ERR_LAUNCH;
+    }
+    const hipError_t e = hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(64 * NQ), args, lds, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
-template <int NQ, bool RAWG, bool BF16S>
+template <int NQ, bool NORM, bool RAWG, bool BF16S>
 kda_status dispatch_q_tokens(const DecodeParams &p, int64_t units, hipStream_t s)
 {
     switch (p.cu_seqlens ? 4 : p.T) {
-    case 1: return launch_q<NQ, 1, RAWG, BF16S>(p, units, s);
-    case 2: return launch_q<NQ, 2, RAWG, BF16S>(p, units, s);
-    case 3: return launch_q<NQ, 3, RAWG, BF16S>(p, units, s);
-    default: return launch_q<NQ, 4, RAWG, BF16S>(p, units, s);
+    case 1: return launch_q<NQ, 1, NORM, RAWG, BF16S>(p, units, s);
+    case 2: return launch_q<NQ, 2, NORM, RAWG, BF16S>(p, units, s);
+    case 3: return launch_q<NQ, 3, NORM, RAWG, BF16S>(p, units, s);
+    default: return launch_q<NQ, 4, NORM, RAWG, BF16S>(p, units, s);
     }
 }
 
 template <bool RAWG, bool BF16S>
-kda_status dispatch_q(const DecodeParams &p, int64_t units, int nq, hipStream_t s)
+kda_status dispatch_q(const DecodeParams &p, int64_t units, int nq, bool norm, hipStream_t s)
 {
-    return nq == 2 ? dispatch_q_tokens<2, RAWG, BF16S>(p, units, s) : dispatch_q_tokens<4, RAWG, BF16S>(p, units, s);
+    if (norm)
+        return dispatch_q_tokens<8, true, RAWG, BF16S>(p, units, s);
+    return nq == 2 ? dispatch_q_tokens<2, false, RAWG, BF16S>(p, units, s)
+                   : dispatch_q_tokens<4, false, RAWG, BF16S>(p, units, s);
 }
 
 template <int NW, bool NORM, bool BF16S, bool RAWG>
@@ -1456,9 +1513,9 @@ kda_status run_decode(const kda_decode_args *a, int32_t T, const int32_t *cu_seq
     const bool bf16_pool = (flags & KDA_FLAG_STATE_BF16) != 0;
     const int64_t units = (int64_t)a->N * a->HV;
     int vtile = vtile_from_flags(flags);
-    // a forced width keeps the 32-column waves; otherwise calls without the
-    // norm may take the 16-column waves
-    const int nq = (vtile == 0 && !norm) ? plan_quarter_waves(units, cu_seqlens ? 0 : T, bf16_pool) : 0;
+    // a forced width keeps the 32-column waves; otherwise the plan may pick
+    // the 16-column waves
+    const int nq = vtile == 0 ? plan_quarter_waves(units, cu_seqlens ? 0 : T, bf16_pool, norm) : 0;
     if (vtile == 0)
         vtile = plan_vtile(units, cu_seqlens ? 1 : T, norm);
     if (norm && vtile != 128)
@@ -1519,8 +1576,10 @@ kda_status run_decode(const kda_decode_args *a, int32_t T, const int32_t *cu_seq
     }
     if (nq) {
         if (bf16_pool)
-            return a->raw_gate ? dispatch_q<true, true>(p, units, nq, s) : dispatch_q<false, true>(p, units, nq, s);
-        return a->raw_gate ? dispatch_q<true, false>(p, units, nq, s) : dispatch_q<false, false>(p, units, nq, s);
+            return a->raw_gate ? dispatch_q<true, true>(p, units, nq, norm, s)
+                               : dispatch_q<false, true>(p, units, nq, norm, s);
+        return a->raw_gate ? dispatch_q<true, false>(p, units, nq, norm, s)
+                           : dispatch_q<false, false>(p, units, nq, norm, s);
     }
     // 32-column waves.  Packed batches: the staged body; step calls with
     // several tokens per request, fewer than 512 tiles (two per compute
@@ -1594,7 +1653,7 @@ kda_status kda_gated_rmsnorm(const void *x, const void *gate, const void *weight
 int32_t kda_decode_plan(int64_t units, int32_t T, uint32_t options)
 {
     const bool norm = (options & KDA_PLAN_NORM) != 0, packed = (options & KDA_PLAN_PACKED) != 0;
-    const int32_t nq = norm ? 0 : plan_quarter_waves(units, packed ? 0 : T, (options & KDA_PLAN_STATE_BF16) != 0);
+    const int32_t nq = plan_quarter_waves(units, packed ? 0 : T, (options & KDA_PLAN_STATE_BF16) != 0, norm);
     return nq ? 16 * nq : plan_vtile(units, packed ? 1 : T, norm);
 }
 

@@ -758,6 +758,40 @@ def test_quarter_waves_bf16_pool_match_wide_waves_bitwise(case):
         assert torch.equal(o, results[0][0]) and torch.equal(st, results[0][1]) and torch.equal(it, results[0][2])
 
 
+NORM_QUARTER_CASES = [
+    # (N, H, HV, T, raw gates, pool dtype): the library picks eight 16-column waves per workgroup
+    (9, 4, 4, 2, False, torch.float32),
+    (5, 2, 6, 5, True, torch.float32),       # tokens past the four loaded ahead
+    (32, 16, 16, 4, False, torch.float32),
+    (3, 2, 4, 1, False, torch.bfloat16),
+    (32, 16, 16, 1, True, torch.bfloat16),
+    (6, 1, 2, None, False, torch.bfloat16),  # packed, 1 to 6 tokens per request
+]
+
+
+@pytest.mark.parametrize("case", NORM_QUARTER_CASES)
+def test_quarter_waves_norm_match_wide_waves_bitwise(case):
+    """The gated RMSNorm epilogue on the 16-column waves (one head per
+    workgroup, the sum of squares in the 32-column kernel's order) against
+    the forced 32-column kernel, bit for bit with per-token states; and
+    against the oracle."""
+    N, H, HV, T, raw, dtype = case
+    p = ki.make_problem("quarternorm", 600 + N, N=N, H=H, HV=HV, K=128, V=128, num_slots=2 * N + 3, T=T,
+                        t_max=6, n_pad=N // 4, norm=True, raw_gates=raw)
+    results = []
+    for flags in (0, kda.KDA_FLAG_VTILE(128)):
+        d = upload(p, background_seed=1234, state_dtype=dtype)
+        inter = torch.full((p.tokens, p.HV, p.K, p.V), 1232.0, dtype=dtype, device=DEV)
+        run_gpu(d, flags=flags, inter_state=inter)
+        torch.cuda.synchronize()
+        if flags == 0:
+            _log(f"quarter waves norm {case}", compare(d, *run_oracle(p, state_bf16=dtype == torch.bfloat16)))
+        results.append((d.out.view(torch.int16).clone(), d.state.view(torch.int16).clone(),
+                        inter.view(torch.int16).clone()))
+    o, st, it = results[1]
+    assert torch.equal(o, results[0][0]) and torch.equal(st, results[0][1]) and torch.equal(it, results[0][2])
+
+
 def test_quarter_waves_full_t4_sweep_match_wide_waves():
     """The T = 4 serving sweep: the library's choice against the forced
     32-column kernel, bit for bit."""
