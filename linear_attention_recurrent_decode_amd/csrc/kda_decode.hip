@@ -1374,35 +1374,42 @@ int32_t plan_vtile(int64_t units, int32_t T, bool norm)
     return 128;
 }
 
-// 16-column waves (kda_decode_q_kernel) for step calls without the norm:
-// 0 = not used, else waves per workgroup.  They pay off where the per-token
-// chain, not the tile stream, sets the time.  Measured on MI355X with cold
-// caches against the 32-column kernel (H = 8), fp32 pool: with one token
-// per request they win up to 64 tiles (N8: 3.88 vs 3.99 us) and lose from
-// 128 (N16: 4.95 vs 4.75); with two or more tokens they win or tie up to
-// 512 tiles (T = 2: N16 5.52 vs 6.07, N32 7.78 vs 7.86, N64 12.54 vs 14.19;
-// T = 4: N32 9.50 vs 10.17, N64 14.29 vs 16.38) and lose at 1024 (N128/T4:
-// 30.6 vs 29.7).  Two waves per workgroup below 128 tiles, four from 128.
-// bf16 pool: four waves (64 columns: full 128-byte row pieces of bf16) win
-// at every size and token count, step or packed (T = 1: N32 5.12 vs 5.89,
-// N128 15.8 vs 20.6; T = 4: N32 7.46 vs 9.98; the packed H12 batch 40.9 vs
-// 50.7), where the 32-column kernel moves half lines of bf16.
-// Step calls only with an fp32 pool (T = 0 stands for a packed call).
-// With the norm epilogue (eight waves, the head's 128 columns in one
-// workgroup): every bf16-pool call (normed N64/H16 T=1 17.4 vs 20.1 us, N8
-// T=4 9.3 vs 10.8) and fp32 step calls with two or more tokens up to 512
-// tiles (N8/H16 T=4 10.0 vs 10.7, N32 18.8 vs 19.3); one-token fp32 calls
-// gain nothing (N32/H16 12.8-13.0 both) or lose (N16: 8.9 vs 7.8).
+// 16-column waves (kda_decode_q_kernel): 0 = not used, else waves per
+// workgroup (2, 4 or 8: 32, 64 or 128 columns).  Measured on MI355X with
+// cold caches against the 32-column kernel (H = 8 unless noted):
+//   fp32 pool, no norm, one token per request: two waves win up to 64
+//     tiles (N8: 3.88 vs 3.99 us) and lose from 128 (N16: 4.95 vs 4.75);
+//     eight waves (full 512-byte rows of the staged tile) win from 512
+//     (N64: 12.14 vs 12.94, N128: 26.8 vs 27.7, N256/H12: 76.1 vs 78.3)
+//     and lose below (N48: 10.2 vs 9.6);
+//   fp32 pool, no norm, two or more tokens: win or tie up to 512 tiles
+//     (T = 2: N16 5.52 vs 6.07, N64 12.54 vs 14.19; T = 4: N32 9.50 vs
+//     10.17, N64 14.29 vs 16.38), lose beyond (N96/T4: 24.7 vs 21.2 with
+//     eight waves); two waves below 128 tiles, four from 128;
+//   fp32 pool, packed: eight waves from 512 tiles (the H12 batch 69.0 vs
+//     69.7 us, every run);
+//   bf16 pool, no norm: four waves (64 columns: full 128-byte row pieces of
+//     bf16) win at every size and token count, step or packed (T = 1: N32
+//     5.12 vs 5.89, N128 15.8 vs 20.6; T = 4: N32 7.46 vs 9.98; the packed
+//     H12 batch 40.9 vs 50.7), where the 32-column kernel moves half lines;
+//   with the norm epilogue (eight waves: the head's 128 columns in one
+//     workgroup): every bf16-pool call (normed N64/H16 T=1 17.4 vs 20.1, N8
+//     T=4 9.3 vs 10.8) and fp32 step calls with two or more tokens up to
+//     512 tiles (N8/H16 T=4 10.0 vs 10.7, N32 18.8 vs 19.3); one-token fp32
+//     calls gain nothing (N32/H16 12.8-13.0 both) or lose (N16: 8.9 vs 7.8).
+// T = 0 stands for a packed call.
 int32_t plan_quarter_waves(int64_t units, int32_t T, bool bf16, bool norm)
 {
     if (norm)
         return (bf16 || (T >= 2 && units <= 512)) ? 8 : 0;
     if (bf16)
         return 4;
-    if (T == 0)
-        return 0;
-    const int64_t limit = T == 1 ? 64 : 512;
-    if (units > limit)
+    if (T == 0 || T == 1) {
+        if (units >= 512)
+            return 8;
+        return (T == 1 && units <= 64) ? 2 : 0;
+    }
+    if (units > 512)
         return 0;
     return units < 128 ? 2 : 4;
 }
@@ -1450,6 +1457,7 @@ kda_status dispatch_q(const DecodeParams &p, int64_t units, int nq, bool norm, h
     if (norm)
         return dispatch_q_tokens<8, true, RAWG, BF16S>(p, units, s);
     return nq == 2 ? dispatch_q_tokens<2, false, RAWG, BF16S>(p, units, s)
+         : nq == 8 ? dispatch_q_tokens<8, false, RAWG, BF16S>(p, units, s)
                    : dispatch_q_tokens<4, false, RAWG, BF16S>(p, units, s);
 }
 

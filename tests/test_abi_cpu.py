@@ -67,16 +67,18 @@ def test_status_strings_and_plan():
             assert kda.kda_decode_plan(units, T, False) in (32, 64, 128)
             assert kda.kda_decode_plan(units, T, True) == 128
     # the launch table: 16-column waves (2 or 4 per workgroup) up to 64 tiles
-    # with one token and up to 512 with two or more; 32-column waves (32, 64
-    # or 128 columns per workgroup) above
+    # with one token and up to 512 with two or more, 8 per workgroup from 512
+    # tiles with one token; 32-column waves (32, 64 or 128 columns per
+    # workgroup) in between
     expect = {(8, 1): 32, (64, 1): 32, (65, 1): 32, (256, 1): 64, (1024, 1): 128,
               (128, 2): 64, (512, 2): 64, (513, 2): 128, (192, 3): 64,
-              (8, 4): 32, (127, 4): 32, (128, 4): 64, (512, 4): 64, (513, 4): 128, (384, 9): 64}
+              (8, 4): 32, (127, 4): 32, (128, 4): 64, (512, 4): 64, (513, 4): 128, (384, 9): 64,
+              (511, 1): 64, (512, 1): 128}
     for (units, T), width in expect.items():
         assert kda.kda_decode_plan(units, T, False) == width, (units, T)
     # packed calls: 32-column waves with an fp32 pool; with a bf16 pool every
     # call without the norm takes 64-column workgroups of 16-column waves
-    for units, width in ((8, 32), (256, 64), (3072, 128)):
+    for units, width in ((8, 32), (256, 64), (511, 64), (512, 128), (3072, 128)):
         assert kda.kda_decode_plan(units, 4, packed=True) == width
         for T in (1, 4):
             assert kda.kda_decode_plan(units, T, bf16_state=True) == 64

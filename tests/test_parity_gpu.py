@@ -97,18 +97,24 @@ def test_step_six_tokens():
 
 @pytest.mark.parametrize("N", [64, 128])
 def test_loop_body_shapes(N):
-    """One token per request from 512 tiles up with an fp32 pool takes the
-    prefetching loop body (64- and 128-column tiles): parity with the oracle,
-    and bit for bit the staged body of the packed call over the same tokens."""
+    """One token per request from 512 tiles up with an fp32 pool: the
+    library's choice (eight 16-column waves per workgroup), the prefetching
+    loop body of the 32-column kernel (a forced 64- or 128-column tile) and
+    the packed call over the same tokens give the same bits; and parity
+    with the oracle."""
     p = ki.make_problem("loop", 60 + N, N=N, H=8, HV=8, K=128, V=128, num_slots=2 * N + 8, T=1)
-    assert kda.kda_decode_plan(N * 8, 1, False) == (64 if N * 8 < 1024 else 128)
-    _log(f"loop body N={N}", parity(p))
-    a = _fresh(p)
-    run_gpu(a, packed=False)
-    b = _fresh(p)
-    run_gpu(b, packed=True)
-    torch.cuda.synchronize()
-    assert torch.equal(a.state, b.state) and torch.equal(a.out.view(torch.int16), b.out.view(torch.int16))
+    assert kda.kda_decode_plan(N * 8, 1, False) == 128
+    assert kda.kda_decode_plan(N * 8, 1, packed=True) == 128
+    _log(f"one token, {N * 8} tiles", parity(p))
+    width = 64 if N * 8 < 1024 else 128
+    runs = []
+    for packed, flags in ((False, 0), (False, kda.KDA_FLAG_VTILE(width)), (True, 0), (True, kda.KDA_FLAG_VTILE(128))):
+        d = _fresh(p)
+        run_gpu(d, packed=packed, flags=flags)
+        torch.cuda.synchronize()
+        runs.append((d.state.clone(), d.out.view(torch.int16).clone()))
+    for st, o in runs[1:]:
+        assert torch.equal(st, runs[0][0]) and torch.equal(o, runs[0][1])
 
 
 def test_packed_and_step_bodies_bit_identical():
