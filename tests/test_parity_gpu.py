@@ -798,6 +798,29 @@ def test_quarter_waves_norm_match_wide_waves_bitwise(case):
     assert torch.equal(o, results[0][0]) and torch.equal(st, results[0][1]) and torch.equal(it, results[0][2])
 
 
+@pytest.mark.parametrize("case", [(64, 8, 8, 1, True), (130, 4, 4, None, False), (130, 4, 4, None, True)])
+def test_eight_quarter_waves_match_wide_waves_bitwise(case):
+    """Eight 16-column waves per workgroup (one-token and packed fp32 calls
+    from 512 tiles) against the forced 32-column kernel, bit for bit with
+    per-token states, fused gate or not; the final state against the
+    oracle."""
+    N, H, HV, T, raw = case
+    p = ki.make_problem("eightq", 800 + N, N=N, H=H, HV=HV, K=128, V=128, num_slots=N + 9, T=T, t_max=3,
+                        n_pad=N // 8, raw_gates=raw)
+    assert kda.kda_decode_plan(N * HV, T or 1, packed=T is None) == 128
+    results = []
+    for flags in (0, kda.KDA_FLAG_VTILE(128)):
+        d = _fresh(p)
+        inter = torch.full((p.tokens, p.HV, p.K, p.V), 1232.0, device=DEV)
+        run_gpu(d, flags=flags, inter_state=inter)
+        torch.cuda.synchronize()
+        if flags == 0:
+            _log(f"eight quarter waves {case}", compare(d, *run_oracle(p)))
+        results.append((d.out.view(torch.int16).clone(), d.state.clone(), inter))
+    o, st, it = results[1]
+    assert torch.equal(o, results[0][0]) and torch.equal(st, results[0][1]) and torch.equal(it, results[0][2])
+
+
 def test_quarter_waves_full_t4_sweep_match_wide_waves():
     """The T = 4 serving sweep: the library's choice against the forced
     32-column kernel, bit for bit."""
