@@ -581,22 +581,25 @@ __device__ __forceinline__ int qk_head(const DecodeParams &p, int hv)
     return (int)(__umulhi((uint32_t)hv, p.qk_magic) + (uint32_t)hv * p.qk_magic_hi);
 }
 
-// Three bodies share advance_token and round identically:
+// Three bodies of the 32-column kernel share advance_token and round
+// identically (the launch plan sends many calls to the 16-column waves
+// instead; these are the bodies of the calls it keeps here):
 //   BODY_LOOP: the token loop prefetches token t+1 while token t computes;
-//     the first token's inputs go out just before the state tile.  Fastest
-//     for one token per request from two tiles per compute unit up with an
-//     fp32 pool.
+//     the first token's inputs go out just before the state tile.  The
+//     32-column body for one token per request from two tiles per compute
+//     unit up with an fp32 pool.
 //   BODY_PEELED: the first token is peeled off the loop and the tile's loads
 //     are issued around the first token's input loads (4 rows, the inputs,
 //     12 rows), pinned by scheduling fences; later tokens load at the top of
-//     their iteration.  Fastest for step calls with several tokens per
-//     request, for launches below two tiles per compute unit, with the fused
-//     gate activation and with a bf16 pool.
+//     their iteration.  Fastest among the three for step calls with several
+//     tokens per request, for launches below two tiles per compute unit
+//     (the one-token serving shape), with the fused gate activation and with
+//     a bf16 pool.
 //   BODY_STAGED: the workgroup copies the inputs of up to STAGE_TOKENS tokens
 //     into LDS while the tile is in flight, so the token loop reads no global
 //     memory (longer requests restage in chunks; with a bf16 pool they load
-//     the remaining tokens directly).  Fastest for packed batches of mixed
-//     lengths.
+//     the remaining tokens directly).  Fastest among the three for packed
+//     batches of mixed lengths.
 constexpr int BODY_LOOP = 0, BODY_PEELED = 1, BODY_STAGED = 2;
 
 // The scalars on the critical path (slot lookup -> tile address, and the
