@@ -1212,6 +1212,26 @@ __global__ __launch_bounds__(256) void kda_gated_rmsnorm_kernel(const uint16_t *
 
 std::atomic<int> g_device_kind[MAX_DEVICES];   // 0 unknown, 1 gfx950, 2 other
 
+// Dynamic LDS of a 16-column-wave kernel with NQ waves: the staged tile
+// (16 NQ columns, padded) and the norm's group sums.  At eight waves it is
+// above the default 64 KiB limit, which is raised once per device, before
+// the first launch (so that no attribute call happens inside a caller's
+// graph capture).
+constexpr size_t q_lds_bytes(int nq) { return (size_t)(KD * 16 * nq + 128) * sizeof(float); }
+
+template <bool NORM, bool RAWG, bool BF16S>
+bool raise_q8_lds_limit()
+{
+    const void *fns[] = {reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 1, NORM, RAWG, BF16S>),
+                         reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 2, NORM, RAWG, BF16S>),
+                         reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 3, NORM, RAWG, BF16S>),
+                         reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 4, NORM, RAWG, BF16S>)};
+    for (const void *fn : fns)
+        if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)q_lds_bytes(8)) != hipSuccess)
+            return false;
+    return true;
+}
+
 kda_status check_device()
 {
     int dev = -1;
@@ -1223,6 +1243,14 @@ kda_status check_device()
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
             return KDA_ERR_DEVICE;
         kind = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        if (kind == 1) {
+            const bool raised = raise_q8_lds_limit<false, false, false>() && raise_q8_lds_limit<false, false, true>() &&
+                                raise_q8_lds_limit<false, true, false>() && raise_q8_lds_limit<false, true, true>() &&
+                                raise_q8_lds_limit<true, false, false>() && raise_q8_lds_limit<true, false, true>() &&
+                                raise_q8_lds_limit<true, true, false>() && raise_q8_lds_limit<true, true, true>();
+            if (!raised)
+                return KDA_ERR_DEVICE;
+        }
         g_device_kind[dev].store(kind, std::memory_order_relaxed);
     }
     return kind == 1 ? KDA_OK : KDA_ERR_DEVICE;
@@ -1431,15 +1459,7 @@ kda_status launch_q(const DecodeParams &p, int64_t units, hipStream_t stream)
     void *args[] = {&slot_idx, &cu_seqlens, &state, &slot_stride, &num_slots, &HV, &T, &status,
                     const_cast<DecodeParams *>(&p)};
     const void *fn = reinterpret_cast<const void *>(&kda_decode_q_kernel<NQ, PF, NORM, RAWG, BF16S>);
-    const size_t lds = (size_t)(KD * 16 * NQ + 128) * sizeof(float);
-    if (lds > 65536) {
-        // above the default limit of dynamic LDS: raise it once per kernel
-        static const hipError_t raised =
-            hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (raised != hipSuccess)
-            return KDA_ERR_LAUNCH;
-    }
-    const hipError_t e = hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(64 * NQ), args, lds, stream);
+    const hipError_t e = hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(64 * NQ), args, q_lds_bytes(NQ), stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 

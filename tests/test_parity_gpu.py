@@ -913,6 +913,50 @@ def test_graph_replay_matches_eager(name):
         assert torch.equal(d.out.view(torch.int16), eager.out.view(torch.int16))
 
 
+_FIRST_CALL_IN_CAPTURE = r"""
+import sys, torch
+sys.path[:0] = [sys.argv[1], sys.argv[1] + "/tests"]
+import kda_inputs as ki
+from kda_harness import run_gpu, upload
+p = ki.make_problem("capture", 5, N=130, H=4, HV=4, K=128, V=128, num_slots=140, T=None, t_max=3, n_pad=5)
+d = upload(p)
+init = d.state.clone()
+g = torch.cuda.CUDAGraph()
+s = torch.cuda.Stream()
+s.wait_stream(torch.cuda.current_stream())
+with torch.cuda.stream(s):
+    with torch.cuda.graph(g, stream=s):
+        run_gpu(d)                       # the process's first library call
+torch.cuda.synchronize()
+outs = []
+for _ in range(2):
+    d.state.copy_(init)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    outs.append((d.state.clone(), d.out.clone()))
+e = upload(p)
+run_gpu(e)
+torch.cuda.synchronize()
+for st, o in outs:
+    assert torch.equal(st, e.state) and torch.equal(o.view(torch.int16), e.out.view(torch.int16))
+print("first call in capture ok")
+"""
+
+
+def test_first_library_call_inside_graph_capture():
+    """A process whose first call is captured into a HIP graph (eight
+    16-column waves: the library raises their LDS limit at its first call
+    on a device) replays it correctly."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _FIRST_CALL_IN_CAPTURE, root], capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0 and "first call in capture ok" in r.stdout, r.stdout[-2000:] + r.stderr[-2000:]
+
+
 # ------------------------------------------------------- standalone norm
 @pytest.mark.parametrize("rows,V", [(512, 128), (5, 128), (3, 2), (7, 130), (33, 1024), (2, 8192)])
 def test_gated_rmsnorm(rows, V):
