@@ -208,6 +208,32 @@ __device__ __forceinline__ float add_permlane32_swap(float x)
     return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 
+// Three values at once over lane pairs l, l^16 and then l, l^32 (the
+// quarters of a 16-column wave): the same additions as add_permlane16_swap
+// and add_permlane32_swap on each value, with the three swaps of a level
+// issued back to back between one pair of wait-state pads.
+__device__ __forceinline__ void add_swaps3(float &x, float &y, float &z)
+{
+    uint32_t x0 = __builtin_bit_cast(uint32_t, x), x1 = x0;
+    uint32_t y0 = __builtin_bit_cast(uint32_t, y), y1 = y0;
+    uint32_t z0 = __builtin_bit_cast(uint32_t, z), z1 = z0;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_permlane16_swap_b32 %2, %3\n\t"
+                 "v_permlane16_swap_b32 %4, %5\n\ts_nop 1"
+                 : "+v"(x0), "+v"(x1), "+v"(y0), "+v"(y1), "+v"(z0), "+v"(z1));
+    x = __builtin_bit_cast(float, x0) + __builtin_bit_cast(float, x1);
+    y = __builtin_bit_cast(float, y0) + __builtin_bit_cast(float, y1);
+    z = __builtin_bit_cast(float, z0) + __builtin_bit_cast(float, z1);
+    x0 = x1 = __builtin_bit_cast(uint32_t, x);
+    y0 = y1 = __builtin_bit_cast(uint32_t, y);
+    z0 = z1 = __builtin_bit_cast(uint32_t, z);
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\tv_permlane32_swap_b32 %2, %3\n\t"
+                 "v_permlane32_swap_b32 %4, %5\n\ts_nop 1"
+                 : "+v"(x0), "+v"(x1), "+v"(y0), "+v"(y1), "+v"(z0), "+v"(z1));
+    x = __builtin_bit_cast(float, x0) + __builtin_bit_cast(float, x1);
+    y = __builtin_bit_cast(float, y0) + __builtin_bit_cast(float, y1);
+    z = __builtin_bit_cast(float, z0) + __builtin_bit_cast(float, z1);
+}
+
 // Sum over the 8 lanes that share a column group (lane bits 3..5: lanes l,
 // l+8, .., l+56), all on the VALU.  Each level adds the same two operands on
 // both lanes of a pair, so every lane of the group ends with the same bits,
@@ -916,9 +942,8 @@ __device__ __forceinline__ void advance_pair(float (&s)[Q_ROWS], const PairIn &i
     kq += KDA_DPP(kq, DPP_QUAD_XOR2);
     kq += KDA_DPP(kq, DPP_ROW_HALF_MIRROR);
     kq += KDA_DPP(kq, DPP_ROW_MIRROR);
-    kq = add_permlane32_swap(add_permlane16_swap(kq));
-    const float u = add_permlane32_swap(add_permlane16_swap(u_lo + u_hi));
-    const float w = add_permlane32_swap(add_permlane16_swap(w_lo + w_hi));
+    float u = u_lo + u_hi, w = w_lo + w_hi;
+    add_swaps3(kq, u, w);
 
     const float vp = b * (bf16_lo(in.v) - u);
     float o = p.scale * fmaf(vp, kq, w);
