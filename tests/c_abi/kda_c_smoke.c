@@ -2,8 +2,9 @@
  * The C ABI used from plain C: no Python, no torch.  Allocates device memory
  * with the HIP runtime, fills the inputs with a small deterministic generator
  * of its own (no step of the decode), runs kda_decode_step and
- * kda_decode_packed through kda.h, and compares outputs and states with the
- * CPU oracle (test infrastructure, linked only here).
+ * kda_decode_packed through kda.h with an fp32 and a bf16 state pool, and
+ * compares outputs and states with the CPU oracle (test infrastructure,
+ * linked only here).
  *
  * Exit status 0 and a last line "c abi ok" on success; 1 with a message on
  * the first mismatch; 2 when the HIP runtime or the library reports an error.
@@ -77,8 +78,11 @@ static void *device_copy(const void *host, size_t bytes)
 }
 
 /* One call of N requests x T tokens (packed: per-request lengths in lens),
- * H q/k heads, HV value heads, checked against the oracle. */
-static int run_case(const char *name, int N, int H, int HV, int T, const int *lens, int num_slots)
+ * H q/k heads, HV value heads, an fp32 or bf16 state pool, checked against
+ * the oracle (which starts from the pool's values and keeps fp64 state; a
+ * bf16 pool is compared within half a bf16 ulp plus the recurrence's own
+ * rounding). */
+static int run_case(const char *name, int N, int H, int HV, int T, const int *lens, int num_slots, int bf16_pool)
 {
     int32_t *cu = malloc(sizeof(int32_t) * (size_t)(N + 1));
     cu[0] = 0;
@@ -103,12 +107,18 @@ static int run_case(const char *name, int N, int H, int HV, int T, const int *le
         beta[i] = (float)(0.5 + 0.4 * uniform_pm1());
     for (size_t i = 0; i < pool_elems; ++i)
         pool[i] = (float)(0.05 * uniform_pm1());
+    uint16_t *pool16 = malloc(pool_elems * 2);
+    if (bf16_pool)
+        for (size_t i = 0; i < pool_elems; ++i) {
+            pool16[i] = to_bf16(pool[i]);
+            pool[i] = bf16_to_float(pool16[i]);      /* the oracle starts from the stored values */
+        }
     for (int n = 0; n < N; ++n)     /* distinct slots (7 is odd and coprime to the pool sizes); every third request a padding row */
         slot[n] = (n % 3 == 2) ? -1 : (int32_t)((n * 7 + 1) % num_slots);
 
     uint16_t *dq = device_copy(q, nq * 2), *dk = device_copy(k, nq * 2), *dv = device_copy(v, nv * 2);
     float *dg = device_copy(g, ng * 4), *dbeta = device_copy(beta, (size_t)tokens * HV * 4);
-    float *dpool = device_copy(pool, pool_elems * 4);
+    void *dpool = bf16_pool ? device_copy(pool16, pool_elems * 2) : device_copy(pool, pool_elems * 4);
     int32_t *dslot = device_copy(slot, sizeof(int32_t) * (size_t)N), *dcu = device_copy(cu, sizeof(int32_t) * (size_t)(N + 1));
     uint16_t *dout = NULL;
     const size_t out_bytes = nv > 0 ? nv * 2 : 1;
@@ -127,7 +137,8 @@ static int run_case(const char *name, int N, int H, int HV, int T, const int *le
     a.state = dpool; a.num_slots = num_slots; a.slot_stride = (int64_t)slot_elems;
     a.slot_idx = dslot;
     a.out = dout; a.out_stride = HV * V;
-    kda_status st = lens ? kda_decode_packed(&a, dcu, tokens, 0, NULL) : kda_decode_step(&a, T, 0, NULL);
+    const uint32_t flags = bf16_pool ? KDA_FLAG_STATE_BF16 : 0;
+    kda_status st = lens ? kda_decode_packed(&a, dcu, tokens, flags, NULL) : kda_decode_step(&a, T, flags, NULL);
     if (st != KDA_OK) {
         fprintf(stderr, "%s: library status %d (%s)\n", name, (int)st, kda_status_string(st));
         return 2;
@@ -137,7 +148,13 @@ static int run_case(const char *name, int N, int H, int HV, int T, const int *le
     uint16_t *out = malloc(nv * 2);
     float *gpool = malloc(pool_elems * 4);
     CHECK_HIP(hipMemcpy(out, dout, nv * 2, hipMemcpyDeviceToHost));
-    CHECK_HIP(hipMemcpy(gpool, dpool, pool_elems * 4, hipMemcpyDeviceToHost));
+    if (bf16_pool) {
+        CHECK_HIP(hipMemcpy(pool16, dpool, pool_elems * 2, hipMemcpyDeviceToHost));
+        for (size_t i = 0; i < pool_elems; ++i)
+            gpool[i] = bf16_to_float(pool16[i]);
+    } else {
+        CHECK_HIP(hipMemcpy(gpool, dpool, pool_elems * 4, hipMemcpyDeviceToHost));
+    }
 
     double *ref_pool = malloc(pool_elems * 8), *ref_out = malloc(nv * 8);
     for (size_t i = 0; i < pool_elems; ++i)
@@ -170,7 +187,7 @@ static int run_case(const char *name, int N, int H, int HV, int T, const int *le
     }
     for (size_t i = 0; i < pool_elems; ++i) {
         const double err = fabs((double)gpool[i] - ref_pool[i]);
-        if (err > 1e-4 * fabs(ref_pool[i]) + 1e-6) {
+        if (err > (bf16_pool ? ldexp(fabs(ref_pool[i]), -8) : 1e-4 * fabs(ref_pool[i])) + 1e-6) {
             fprintf(stderr, "%s: state %zu: %g vs %g\n", name, i, (double)gpool[i], ref_pool[i]);
             return 1;
         }
@@ -181,7 +198,8 @@ static int run_case(const char *name, int N, int H, int HV, int T, const int *le
 
     hipFree(dq); hipFree(dk); hipFree(dv); hipFree(dg); hipFree(dbeta); hipFree(dpool); hipFree(dslot);
     hipFree(dcu); hipFree(dout);
-    free(q); free(k); free(v); free(g); free(beta); free(pool); free(slot); free(cu); free(out); free(gpool);
+    free(q); free(k); free(v); free(g); free(beta); free(pool); free(pool16); free(slot); free(cu); free(out);
+    free(gpool);
     free(ref_pool); free(ref_out);
     return 0;
 }
@@ -201,12 +219,21 @@ int main(void)
         fprintf(stderr, "K = 64 was not rejected\n");
         return 1;
     }
+    /* the plan for a packed bf16 call: 64-column workgroups */
+    if (kda_decode_plan(4096, 1, KDA_PLAN_STATE_BF16 | KDA_PLAN_PACKED) != 64 || kda_decode_plan(256, 1, 0) != 64) {
+        fprintf(stderr, "unexpected launch plan\n");
+        return 1;
+    }
     static const int lens[7] = {1, 4, 2, 3, 1, 2, 4};
-    int rc = run_case("step N=9 H=2 HV=4 T=3", 9, 2, 4, 3, NULL, 16);
+    int rc = run_case("step N=9 H=2 HV=4 T=3", 9, 2, 4, 3, NULL, 16, 0);
     if (rc == 0)
-        rc = run_case("step N=40 H=8 HV=8 T=1", 40, 8, 8, 1, NULL, 64);
+        rc = run_case("step N=40 H=8 HV=8 T=1", 40, 8, 8, 1, NULL, 64, 0);
     if (rc == 0)
-        rc = run_case("packed N=7 H=1 HV=3", 7, 1, 3, 0, lens, 12);
+        rc = run_case("packed N=7 H=1 HV=3", 7, 1, 3, 0, lens, 12, 0);
+    if (rc == 0)
+        rc = run_case("bf16 pool, step N=40 H=8 HV=8 T=2", 40, 8, 8, 2, NULL, 64, 1);
+    if (rc == 0)
+        rc = run_case("bf16 pool, packed N=7 H=1 HV=3", 7, 1, 3, 0, lens, 12, 1);
     if (rc == 0)
         printf("c abi ok\n");
     return rc;
