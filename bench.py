@@ -42,6 +42,8 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 COLD_BYTES = 1 << 30            # state traffic between two uses of the same slots
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "linear_attention_recurrent_decode_amd", "csrc", "kda_decode.hip")
+# kda_decode_plan(..., layout=True) values
+LAYOUT_NAMES = {0: "32-column waves", 1: "16-column waves", 2: "16-column waves, split key rows"}
 
 
 def log(*a):
@@ -314,7 +316,11 @@ def main():
                    "norm": p.gate is not None, "state_dtype": args.state,
                    "gate_input": "raw, activated in the kernel" if p.raw else "activated",
                    "cold_slot_sets": len(sets), "cold_pool_copies": R,
-                   "vtile": kda.kda_decode_plan(p.N * p.HV, T or 1, p.gate is not None, bf16_state, packed)},
+                   "vtile": kda.kda_decode_plan(p.N * p.HV, T or 1, p.gate is not None, bf16_state, packed,
+                                                raw_gate=p.raw),
+                   "lane_layout": LAYOUT_NAMES[kda.kda_decode_plan(p.N * p.HV, T or 1, p.gate is not None,
+                                                                   bf16_state, packed, layout=True,
+                                                                   raw_gate=p.raw)]},
         "state_GBps": round(state_gbps, 1),
         "state_frac_of_peak": round(state_gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_call": nbytes["total"],

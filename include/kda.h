@@ -81,9 +81,10 @@ typedef enum kda_status {
 
 /* flags: bits 8..9 force the value-tile width of one workgroup
  * (1 = 32 columns, 2 = 64, 3 = 128; 0 = the library's choice) of 32-column
- * waves; the library's choice may instead use 16-column waves (calls
- * without the norm).  Results are bit-identical for every width and wave
- * layout; the knob exists for tests and tuning. */
+ * waves; the library's choice may instead use one of the 16-column-wave
+ * layouts (kda_decode_plan with KDA_PLAN_LAYOUT names it).  Results are
+ * bit-identical for every width and lane layout; the knob exists for tests
+ * and tuning. */
 #define KDA_FLAG_VTILE_SHIFT 8u
 #define KDA_FLAG_VTILE_MASK (3u << KDA_FLAG_VTILE_SHIFT)
 #define KDA_FLAG_VTILE(code) (((uint32_t)(code) & 3u) << KDA_FLAG_VTILE_SHIFT)
@@ -215,11 +216,21 @@ kda_status kda_gated_rmsnorm(const void *x, const void *gate, const void *weight
 #define KDA_PLAN_NORM 1u         /* the gated RMSNorm epilogue */
 #define KDA_PLAN_STATE_BF16 2u   /* a bf16 state pool (KDA_FLAG_STATE_BF16) */
 #define KDA_PLAN_PACKED 4u       /* a packed call (kda_decode_packed) */
+#define KDA_PLAN_LAYOUT 8u       /* report the lane layout (KDA_LAYOUT_*) instead */
+#define KDA_PLAN_RAW_GATE 16u    /* the fused gate activation (raw_gate set) */
+
+/* lane layouts of the same arithmetic (the results are bitwise the same) */
+#define KDA_LAYOUT_WIDE 0      /* 32-column waves: a lane holds 4 columns x 16 key rows */
+#define KDA_LAYOUT_QUARTER 1   /* 16-column waves: a lane holds 1 column x 32 key rows */
+#define KDA_LAYOUT_SPLIT 2     /* 16-column waves with the key rows split over two waves:
+                                  a lane holds 1 column x 16 key rows */
 
 /* The columns per workgroup (32, 64 or 128) the library picks for a call of
  * `units` = N*HV (request, value head) pairs with T tokens per request (any
- * T >= 1 for a packed call) and the given KDA_PLAN_* options; without a
- * forced KDA_FLAG_VTILE width.  Host-only, no device access. */
+ * T >= 1 for a packed call) and the given KDA_PLAN_* options, or with
+ * KDA_PLAN_LAYOUT the lane layout it picks; without a forced KDA_FLAG_VTILE
+ * width (which always selects KDA_LAYOUT_WIDE).  Host-only, no device
+ * access. */
 int32_t kda_decode_plan(int64_t units, int32_t T, uint32_t options);
 
 /* Static description of a status code. */

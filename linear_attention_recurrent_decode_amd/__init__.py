@@ -21,7 +21,9 @@ import torch
 __all__ = [
     "KdaError", "KdaDecodeArgs", "library", "library_path",
     "kda_decode_step", "kda_decode_packed", "kda_gated_rmsnorm",
-    "kda_decode_plan", "KDA_PLAN_NORM", "KDA_PLAN_STATE_BF16", "KDA_PLAN_PACKED", "kda_status_string", "decode_args",
+    "kda_decode_plan", "KDA_PLAN_NORM", "KDA_PLAN_STATE_BF16", "KDA_PLAN_PACKED", "KDA_PLAN_LAYOUT",
+    "KDA_PLAN_RAW_GATE",
+    "KDA_LAYOUT_WIDE", "KDA_LAYOUT_QUARTER", "KDA_LAYOUT_SPLIT", "kda_status_string", "decode_args",
     "KDA_FLAG_VTILE", "KDA_FLAG_STATE_BF16", "KDA_FLAG_VALIDATE", "KDA_DEVICE_STATUS",
 ]
 
@@ -110,13 +112,20 @@ def kda_status_string(status: int) -> str:
 KDA_PLAN_NORM = 1
 KDA_PLAN_STATE_BF16 = 2
 KDA_PLAN_PACKED = 4
+KDA_PLAN_LAYOUT = 8
+KDA_PLAN_RAW_GATE = 16
+KDA_LAYOUT_WIDE = 0
+KDA_LAYOUT_QUARTER = 1
+KDA_LAYOUT_SPLIT = 2
 
 
 def kda_decode_plan(units: int, T: int = 1, has_norm: bool = False, bf16_state: bool = False,
-                    packed: bool = False) -> int:
-    """Columns per workgroup the library picks (include/kda.h, kda_decode_plan)."""
+                    packed: bool = False, layout: bool = False, raw_gate: bool = False) -> int:
+    """Columns per workgroup the library picks, or with layout=True its lane
+    layout, a KDA_LAYOUT_* value (include/kda.h, kda_decode_plan)."""
     options = ((KDA_PLAN_NORM if has_norm else 0) | (KDA_PLAN_STATE_BF16 if bf16_state else 0)
-               | (KDA_PLAN_PACKED if packed else 0))
+               | (KDA_PLAN_PACKED if packed else 0) | (KDA_PLAN_LAYOUT if layout else 0)
+               | (KDA_PLAN_RAW_GATE if raw_gate else 0))
     return int(library().kda_decode_plan(int(units), int(T), options))
 
 

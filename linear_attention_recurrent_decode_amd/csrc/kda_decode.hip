@@ -626,6 +626,26 @@ __device__ __forceinline__ int qk_head(const DecodeParams &p, int hv)
 //     memory (longer requests restage in chunks; with a bf16 pool they load
 //     the remaining tokens directly).  Fastest among the three for packed
 //     batches of mixed lengths.
+// The kernel arguments that a token's loads need, requested together with
+// the slot index, so that the two scalar round trips overlap: the asm takes
+// them all in SGPRs, so each of their loads is issued before it and one
+// wait covers them.  Only for kernels that load a token's inputs before the
+// state tile: otherwise the tile's loads go out first, right after the slot
+// arrives, and these arguments follow (measured on MI355X: requesting them
+// early delays the tile by about 0.3 us at one token and a few tiles).
+template <bool RAWG>
+__device__ __forceinline__ void slot_and_token_args(const DecodeParams &p, int64_t slot)
+{
+    if constexpr (RAWG)
+        asm volatile("" ::"s"(slot), "s"(p.q), "s"(p.k), "s"(p.v), "s"(p.raw_gate), "s"(p.raw_beta), "s"(p.A_log),
+                     "s"(p.dt_bias), "s"(p.q_stride), "s"(p.k_stride), "s"(p.v_stride), "s"(p.raw_gate_stride),
+                     "s"(p.raw_beta_stride), "s"(p.qk_magic), "s"(p.qk_magic_hi));
+    else
+        asm volatile("" ::"s"(slot), "s"(p.q), "s"(p.k), "s"(p.v), "s"(p.g), "s"(p.beta), "s"(p.q_stride),
+                     "s"(p.k_stride), "s"(p.v_stride), "s"(p.g_stride), "s"(p.beta_stride), "s"(p.qk_magic),
+                     "s"(p.qk_magic_hi));
+}
+
 constexpr int BODY_LOOP = 0, BODY_PEELED = 1, BODY_STAGED = 2;
 
 // The scalars on the critical path (slot lookup -> tile address, and the
@@ -654,6 +674,8 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot
     // slot gather: padding rows and slots outside the pool are skipped; with
     // validation, every block stops here unless the metadata check passed
     const int64_t slot = slot_idx[req];
+    if constexpr (BODY == BODY_LOOP)
+        slot_and_token_args<RAWG>(p, slot);   // the loop body loads its first token before the tile
     if (status && *status != KDA_DEVICE_OK)
         return;
     if (slot < 0 || slot >= num_slots)
@@ -851,7 +873,7 @@ __device__ __forceinline__ void load_pair(PairIn &in, const DecodeParams &p, int
         in.z = p.gate[t * p.gate_stride + (int64_t)hv * VD + col];
 }
 
-// Partial sums over rows 8B .. 8B+7 of the lane's quarter, whose owners are
+// Partial sums over rows 8B .. 8B+7 of the lane's rows, whose owners are
 // lanes 4B .. 4B+3 of the DPP row (lo values for even rows, hi for odd):
 // u += s_i (a_i k_i), w += s_i (a_i q_i), the factor taken from its owner by
 // row_newbcast.  A DPP operand must not be written by the two VALU
@@ -861,8 +883,8 @@ __device__ __forceinline__ void load_pair(PairIn &in, const DecodeParams &p, int
     "v_fmac_f32_dpp %0, %" AK ", %" S " row_newbcast:%c" IMM " row_mask:0xf bank_mask:0xf\n\t" \
     "v_fmac_f32_dpp %1, %" AQ ", %" S " row_newbcast:%c" IMM " row_mask:0xf bank_mask:0xf\n\t"
 
-template <int B>
-__device__ __forceinline__ void quarter_sums8(const float (&s)[Q_ROWS], float ak_lo, float ak_hi, float aq_lo,
+template <int B, int R>
+__device__ __forceinline__ void quarter_sums8(const float (&s)[R], float ak_lo, float ak_hi, float aq_lo,
                                               float aq_hi, float &u, float &w)
 {
     asm volatile("s_nop 1\n\t"
@@ -883,8 +905,8 @@ __device__ __forceinline__ void quarter_sums8(const float (&s)[Q_ROWS], float ak
     "v_mul_f32_dpp %" S ", %" A ", %" S " row_newbcast:%c" IMM " row_mask:0xf bank_mask:0xf\n\t" \
     "v_fmac_f32_dpp %" S ", %" K ", %12 row_newbcast:%c" IMM " row_mask:0xf bank_mask:0xf\n\t"
 
-template <int B>
-__device__ __forceinline__ void quarter_update8(float (&s)[Q_ROWS], float a_lo, float a_hi, float k_lo, float k_hi,
+template <int B, int R>
+__device__ __forceinline__ void quarter_update8(float (&s)[R], float a_lo, float a_hi, float k_lo, float k_hi,
                                                 float vp)
 {
     asm volatile("s_nop 1\n\t"
@@ -898,6 +920,69 @@ __device__ __forceinline__ void quarter_update8(float (&s)[Q_ROWS], float a_lo, 
                    "i"(4 * B), "i"(4 * B + 1), "i"(4 * B + 2), "i"(4 * B + 3));
 }
 
+// The lane's row pair of one token widened to fp32, its decay factors
+// a = exp(g) and the head's beta (activated first with the fused gate).
+struct PairFactors {
+    float k_lo, k_hi, q_lo, q_hi, a_lo, a_hi, b;
+};
+
+template <bool RAWG>
+__device__ __forceinline__ PairFactors pair_factors(const PairIn &in, const HeadGate<RAWG> &hg)
+{
+    PairFactors f;
+    f.k_lo = bf16_lo(in.k);
+    f.k_hi = bf16_hi(in.k);
+    f.q_lo = bf16_lo(in.q);
+    f.q_hi = bf16_hi(in.q);
+    float g_lo, g_hi;
+    if constexpr (RAWG) {
+        const uint32_t rw = __float_as_uint(in.g.x);
+        const float A = expf(hg.a_log);
+        g_lo = gate_log_decay(bf16_lo(rw), hg.b.x, A);
+        g_hi = gate_log_decay(bf16_hi(rw), hg.b.y, A);
+        f.b = beta_from_raw(bf16_lo(__float_as_uint(in.beta)));
+    } else {
+        g_lo = in.g.x;
+        g_hi = in.g.y;
+        f.b = in.beta;
+    }
+    f.a_lo = __expf(g_lo);
+    f.a_hi = __expf(g_hi);
+    return f;
+}
+
+// The part of a token's step that does not touch the state: the factors,
+// the decayed keys and queries a k and a q of the row pair, and k.q over the
+// lane's ROWS key rows (the row pair, then pairs of pairs across the DPP
+// row: 8 pairs for 16 rows, 16 for 32), before the sums across lanes.  A
+// kernel may evaluate it for its first token while the state tile is still
+// on its way.
+struct PairPre {
+    PairFactors f;
+    float ak_lo, ak_hi, aq_lo, aq_hi;
+    float kq;
+};
+
+template <int ROWS, bool RAWG>
+__device__ __forceinline__ PairPre pair_pre(const PairIn &in, const HeadGate<RAWG> &hg)
+{
+    static_assert(ROWS == 16 || ROWS == 32, "a lane holds 16 or 32 key rows");
+    PairPre r;
+    r.f = pair_factors(in, hg);
+    r.ak_lo = r.f.a_lo * r.f.k_lo;
+    r.ak_hi = r.f.a_hi * r.f.k_hi;
+    r.aq_lo = r.f.a_lo * r.f.q_lo;
+    r.aq_hi = r.f.a_hi * r.f.q_hi;
+    float kq = fmaf(r.f.k_hi, r.f.q_hi, r.f.k_lo * r.f.q_lo);
+    kq += KDA_DPP(kq, DPP_QUAD_XOR1);
+    kq += KDA_DPP(kq, DPP_QUAD_XOR2);
+    kq += KDA_DPP(kq, DPP_ROW_HALF_MIRROR);
+    if constexpr (ROWS == 32)
+        kq += KDA_DPP(kq, DPP_ROW_MIRROR);
+    r.kq = kq;
+    return r;
+}
+
 // Advance the lane's column of its row quarter by one token and write its
 // output (the same recurrence as advance_token).  With the norm epilogue
 // (NORM, 8 waves: the workgroup holds the head's 128 columns) the sum of o^2
@@ -908,26 +993,13 @@ __device__ __forceinline__ void quarter_update8(float (&s)[Q_ROWS], float a_lo, 
 // sums C, and over the 4 such parts (P0 + P1) + (P2 + P3).  The group sums
 // meet in LDS (norm_c, double-buffered by token parity: one barrier per
 // token) and every lane evaluates the tree itself.
-template <bool NORM, bool RAWG>
-__device__ __forceinline__ void advance_pair(float (&s)[Q_ROWS], const PairIn &in, const DecodeParams &p,
-                                             const HeadGate<RAWG> &hg, int64_t t, int hv, int rq, int col,
-                                             int wave, int cp, float nw, float *norm_c)
+template <bool NORM>
+__device__ __forceinline__ void advance_pair(float (&s)[Q_ROWS], const PairPre &pre, const PairIn &in,
+                                             const DecodeParams &p, int64_t t, int hv, int rq, int col, int wave,
+                                             int cp, float nw, float *norm_c)
 {
-    const float k_lo = bf16_lo(in.k), k_hi = bf16_hi(in.k), q_lo = bf16_lo(in.q), q_hi = bf16_hi(in.q);
-    float b, g_lo, g_hi;
-    if constexpr (RAWG) {
-        const uint32_t rw = __float_as_uint(in.g.x);
-        const float A = expf(hg.a_log);
-        g_lo = gate_log_decay(bf16_lo(rw), hg.b.x, A);
-        g_hi = gate_log_decay(bf16_hi(rw), hg.b.y, A);
-        b = beta_from_raw(bf16_lo(__float_as_uint(in.beta)));
-    } else {
-        g_lo = in.g.x;
-        g_hi = in.g.y;
-        b = in.beta;
-    }
-    const float a_lo = __expf(g_lo), a_hi = __expf(g_hi);
-    const float ak_lo = a_lo * k_lo, ak_hi = a_hi * k_hi, aq_lo = a_lo * q_lo, aq_hi = a_hi * q_hi;
+    const float k_lo = pre.f.k_lo, k_hi = pre.f.k_hi, a_lo = pre.f.a_lo, a_hi = pre.f.a_hi, b = pre.f.b;
+    const float ak_lo = pre.ak_lo, ak_hi = pre.ak_hi, aq_lo = pre.aq_lo, aq_hi = pre.aq_hi;
 
     // both key-axis partial sums, each 16-row half in row order
     float u_lo = 0.f, w_lo = 0.f, u_hi = 0.f, w_hi = 0.f;
@@ -936,12 +1008,8 @@ __device__ __forceinline__ void advance_pair(float (&s)[Q_ROWS], const PairIn &i
     quarter_sums8<1>(s, ak_lo, ak_hi, aq_lo, aq_hi, u_lo, w_lo);
     quarter_sums8<3>(s, ak_lo, ak_hi, aq_lo, aq_hi, u_hi, w_hi);
 
-    // k.q: the row pair, then pairs of pairs across the DPP row, then the quarters
-    float kq = fmaf(k_hi, q_hi, k_lo * q_lo);
-    kq += KDA_DPP(kq, DPP_QUAD_XOR1);
-    kq += KDA_DPP(kq, DPP_QUAD_XOR2);
-    kq += KDA_DPP(kq, DPP_ROW_HALF_MIRROR);
-    kq += KDA_DPP(kq, DPP_ROW_MIRROR);
+    // k.q of the quarter, then the quarters
+    float kq = pre.kq;
     float u = u_lo + u_hi, w = w_lo + w_hi;
     add_swaps3(kq, u, w);
 
@@ -975,18 +1043,19 @@ __device__ __forceinline__ void advance_pair(float (&s)[Q_ROWS], const PairIn &i
 }
 
 // The workgroup's 128 rows x C columns of a state tile in HBM, moved with
-// 16-byte non-temporal accesses over full row pieces: 4 fp32 or 8 bf16
-// elements per lane and access, so 16 (fp32) or 32 (bf16) rows per
-// instruction across the workgroup's 4C lanes, N pieces per lane.  In LDS
+// 16-byte non-temporal accesses over full row pieces by its THREADS lanes:
+// 4 fp32 or 8 bf16 elements per lane and access, N pieces per lane.  In LDS
 // the tile is fp32 either way (bf16 widened exactly on the way in, rounded
-// to nearest even on the way out), row r at dword r C + 16 (r / 32): rows
-// 32 apart would otherwise sit in the same banks, and the pad puts the 4 row
-// quarters that one column read touches 16 banks apart.
-template <int C, bool BF16S>
+// to nearest even on the way out), row r at dword r C + 16 (r >> PAD): the
+// row groups that one column read touches (32 rows apart with PAD = 5, 16
+// with PAD = 4) would otherwise sit in the same banks, and the pad puts
+// them 16 banks apart.
+template <int C, bool BF16S, int THREADS = 4 * C, int PAD = 5>
 struct SlabIO {
     static constexpr int ELEMS = BF16S ? 8 : 4;            // elements per 16-byte piece
-    static constexpr int ROWS = 4 * C / (C / ELEMS);       // rows per instruction
+    static constexpr int ROWS = THREADS / (C / ELEMS);     // rows per instruction
     static constexpr int N = KD / ROWS;                    // pieces per lane
+    static constexpr int LDS_FLOATS = KD * C + (KD >> PAD) * 16;
     u32x4 *ptr;
     int r0, c0;
 
@@ -996,7 +1065,7 @@ struct SlabIO {
         ptr = reinterpret_cast<u32x4 *>(static_cast<char *>(state) +
                                         (elem_offset + (int64_t)r0 * VD + c0) * (BF16S ? 2 : 4));
     }
-    static __device__ __forceinline__ int lds_at(int r, int c) { return r * C + (r >> 5) * 16 + c; }
+    static __device__ __forceinline__ int lds_at(int r, int c) { return r * C + (r >> PAD) * 16 + c; }
 
     __device__ __forceinline__ u32x4 load(int j) const
     {
@@ -1029,10 +1098,12 @@ struct SlabIO {
 // NQ waves of 16 columns per workgroup; the norm epilogue (NORM) with 8
 // waves only; fp32 or bf16 pool (BF16S); step calls (T tokens per request)
 // or packed ones (cu_seqlens).  The inputs of the first PF tokens are loaded
-// with the tile (later tokens, if any, load at the top of their iteration).
-// LDS is dynamic: the staged tile (C = 16 NQ columns) plus 64 floats for
-// the norm's group sums.
-template <int NQ, int PF, bool NORM, bool RAWG, bool BF16S>
+// with the tile (later tokens, if any, load at the top of their iteration):
+// after the tile's loads, or with EARLY the first token's before them (its
+// kernel arguments requested with the slot index), so that its state-free
+// part runs while the tile is in flight.  LDS is dynamic: the staged tile
+// (C = 16 NQ columns) plus 64 floats for the norm's group sums.
+template <int NQ, int PF, bool NORM, bool RAWG, bool BF16S, bool EARLY>
 __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *slot_idx, const int32_t *cu_seqlens,
                                                                void *state, int64_t slot_stride, int64_t num_slots,
                                                                int32_t HV, int32_t T, const int32_t *status,
@@ -1041,6 +1112,7 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
     static_assert(NQ == 2 || NQ == 4 || NQ == 8, "a workgroup is 2, 4 or 8 waves of 16 columns");
     static_assert(!NORM || NQ == 8, "the norm epilogue needs all 128 columns in one workgroup");
     static_assert(PF >= 1 && PF <= 4, "up to 4 tokens' inputs ahead");
+    static_assert(!EARLY || PF >= 2, "one-token calls load the tile first");
     constexpr int NVT = 8 / NQ;   // value tiles per head
 
     const int lane = threadIdx.x & 63;
@@ -1052,6 +1124,8 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
     const int hv = (int)(unit - req * HV);
 
     const int64_t slot = slot_idx[req];
+    if constexpr (EARLY)
+        slot_and_token_args<RAWG>(p, slot);
     if (status && *status != KDA_DEVICE_OK)
         return;
     if (slot < 0 || slot >= num_slots)
@@ -1105,21 +1179,37 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
     HeadGate<RAWG> hg;
     PairIn in[PF];
     float nw = 0.0f;
-    if constexpr (NORM)
-        nw = bf16_lo(p.norm_weight[col]);
+    PairPre pre0;
     {
+        // EARLY: the first token's inputs go out before the tile (loads
+        // complete in order), so that its state-free part runs while the
+        // tile is in flight; otherwise the tile goes out first
+        if constexpr (EARLY) {
+            hg.load(p, hv, row0, cp);
+            load_pair<NORM, RAWG>(in[0], p, bos, h, hv, row0, cp, col);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         u32x4 piece[Slab::N];
 #pragma unroll
         for (int j = 0; j < Slab::N; ++j)
             piece[j] = slab.load(j);
         __builtin_amdgcn_sched_barrier(0);
-        hg.load(p, hv, row0, cp);
+        if constexpr (!EARLY) {
+            hg.load(p, hv, row0, cp);
+            load_pair<NORM, RAWG>(in[0], p, bos, h, hv, row0, cp, col);
+        }
+        if constexpr (NORM)
+            nw = bf16_lo(p.norm_weight[col]);
         // token j, or for a request shorter than PF (packed calls) its last
         // token again: a harmless repeat that keeps the loads unconditional
 #pragma unroll
-        for (int j = 0; j < PF; ++j)
+        for (int j = 1; j < PF; ++j)
             load_pair<NORM, RAWG>(in[j], p, j < ntok ? bos + j : eos - 1, h, hv, row0, cp, col);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (EARLY) {
+            pre0 = pair_pre<Q_ROWS>(in[0], hg);
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int j = 0; j < Slab::N; ++j)
             slab.to_lds(stage, j, piece[j]);
@@ -1128,19 +1218,193 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
 #pragma unroll
     for (int i = 0; i < Q_ROWS; ++i)
         s[i] = stage[Slab::lds_at(row0 + i, 16 * wave + cp)];
+    // every request here has a first token (ntok >= 1); with the tile first
+    // its inputs arrive after the tile, and its state-free part is evaluated
+    // where it is used (measured faster than ahead of the staging)
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
         if (j < ntok) {
-            advance_pair<NORM, RAWG>(s, in[j], p, hg, bos + j, hv, rq, col, wave, cp, nw, norm_c);
+            const PairPre pre = (EARLY && j == 0) ? pre0 : pair_pre<Q_ROWS>(in[j], hg);
+            advance_pair<NORM>(s, pre, in[j], p, bos + j, hv, rq, col, wave, cp, nw, norm_c);
             keep_state(bos + j);
         }
     }
     for (int64_t t = bos + PF; t < eos; ++t) {
         load_pair<NORM, RAWG>(in[0], p, t, h, hv, row0, cp, col);
-        advance_pair<NORM, RAWG>(s, in[0], p, hg, t, hv, rq, col, wave, cp, nw, norm_c);
+        advance_pair<NORM>(s, pair_pre<Q_ROWS>(in[0], hg), in[0], p, t, hv, rq, col, wave, cp, nw, norm_c);
         keep_state(t);
     }
     // back through LDS
+    stage_columns();
+#pragma unroll
+    for (int j = 0; j < Slab::N; ++j)
+        slab.store_from_lds(stage, j);
+}
+
+// ---------------------------------------------------------------------------
+// Split-key 16-column waves.  A workgroup of 4 waves holds 32 columns: two
+// waves per 16 columns, one for each half of the 128 key rows, so a lane
+// holds one column of one 16-row group (row group rg = 4 rh + lane / 16 of
+// row half rh): half the registers and half the per-token multiply-adds of
+// a kda_decode_q_kernel lane, for one LDS exchange and barrier per token,
+// where the two halves' partial sums meet.  The additions are those of the
+// 32-row quarters: a row group's 16-row chain is the quarter's lo or hi
+// chain, row groups 2m and 2m+1 add up to quarter m by the l^16 swap (lo +
+// hi, the quarter's order), quarters 0 + 1 and 2 + 3 by the l^32 swap, and
+// the two halves in LDS, the quarter tree's last level; k.q the same way
+// from the 8 row pairs of a row group.  So the results are bitwise those of
+// the other layouts.  Lanes 8 .. 15 of a DPP row hold the same row pairs
+// as lanes 0 .. 7 (the row group has 8), so their k.q tree has the same
+// value without a broadcast.
+constexpr int S_ROWS = 16;          // key rows per lane
+constexpr int S_COLS = 32;          // columns per workgroup
+constexpr int S_XCH = 3 * S_COLS;   // one row half's u, w and k.q per column
+
+__device__ __forceinline__ void advance_split(float (&s)[S_ROWS], const PairPre &pre, const PairIn &in,
+                                              const DecodeParams &p, int64_t t, int hv, int rh, int rgl, int cl,
+                                              int col, float *xch)
+{
+    const PairFactors &f = pre.f;
+    float u = 0.f, w = 0.f;
+    quarter_sums8<0>(s, pre.ak_lo, pre.ak_hi, pre.aq_lo, pre.aq_hi, u, w);
+    quarter_sums8<1>(s, pre.ak_lo, pre.ak_hi, pre.aq_lo, pre.aq_hi, u, w);
+    float kq = pre.kq;
+    add_swaps3(kq, u, w);
+    // the halves meet in LDS, double-buffered by token parity: a buffer is
+    // written again two tokens later, after every wave has passed the
+    // barrier of the token between, so after its reads of this one
+    float *x = xch + (int)(t & 1) * (2 * S_XCH);
+    if (rgl == 0) {
+        float *mine = x + rh * S_XCH + 3 * cl;
+        mine[0] = u;
+        mine[1] = w;
+        mine[2] = kq;
+    }
+    __syncthreads();
+    const float *other = x + (rh ^ 1) * S_XCH + 3 * cl;
+    u = u + other[0];
+    w = w + other[1];
+    kq = kq + other[2];
+    const float vp = f.b * (bf16_lo(in.v) - u);
+    const float o = p.scale * fmaf(vp, kq, w);
+    quarter_update8<0>(s, f.a_lo, f.a_hi, f.k_lo, f.k_hi, vp);
+    quarter_update8<1>(s, f.a_lo, f.a_hi, f.k_lo, f.k_hi, vp);
+    if (rh == 0 && rgl == 0)
+        p.out[t * p.out_stride + (int64_t)hv * VD + col] = (uint16_t)pack_bf16x2(o, 0.0f);
+}
+
+// Step calls (T tokens per request) without the norm epilogue, fp32 or bf16
+// pool.  Waves 0, 1 hold row half 0 of columns 0 .. 15 and 16 .. 31 of the
+// workgroup's 32, waves 2, 3 row half 1.  The tile streams through LDS as
+// in kda_decode_q_kernel (here with rows 16 apart padded to other banks),
+// followed there by the exchange buffers.
+template <int PF, bool RAWG, bool BF16S, bool EARLY>
+__global__ __launch_bounds__(256) void kda_decode_split_kernel(const int32_t *slot_idx, void *state,
+                                                               int64_t slot_stride, int64_t num_slots, int32_t HV,
+                                                               int32_t T, const int32_t *status, DecodeParams p)
+{
+    static_assert(PF >= 1 && PF <= 4, "up to 4 tokens' inputs ahead");
+    static_assert(!EARLY || PF >= 2, "one-token calls load the tile first");
+    constexpr int NVT = VD / S_COLS;   // value tiles per head
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t block = blockIdx.x;
+    const int vt = (int)(block % NVT);
+    const int64_t unit = block / NVT;
+    const int64_t req = unit / HV;
+    const int hv = (int)(unit - req * HV);
+
+    const int64_t slot = slot_idx[req];
+    if constexpr (EARLY)
+        slot_and_token_args<RAWG>(p, slot);
+    if (status && *status != KDA_DEVICE_OK)
+        return;
+    if (slot < 0 || slot >= num_slots)
+        return;
+    const int64_t bos = req * T, eos = bos + T;
+    const int h = qk_head(p, hv);
+
+    const int cp = lane & 15;           // column within the wave
+    const int rgl = lane >> 4;          // row group within the row half
+    const int cw = wave & 1;            // column wave
+    const int rh = wave >> 1;           // row half
+    const int cl = 16 * cw + cp;        // column within the workgroup
+    const int col = vt * S_COLS + cl;
+    const int row0 = S_ROWS * (4 * rh + rgl);
+    const int pair = cp & 7;            // row pair of the lane's row group
+
+    float s[S_ROWS];
+    using Slab = SlabIO<S_COLS, BF16S, 256, 4>;
+    extern __shared__ float stage[];    // the tile, then 2 x 2 exchange buffers
+    float *xch = stage + Slab::LDS_FLOATS;
+    const Slab slab(state, slot * slot_stride + (int64_t)hv * (KD * VD) + vt * S_COLS, (int)threadIdx.x);
+    auto stage_columns = [&]() {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < S_ROWS; ++i)
+            stage[Slab::lds_at(row0 + i, cl)] = s[i];
+        __syncthreads();
+    };
+    // p.inter_state is uniform, so every wave reaches the barriers
+    auto keep_state = [&](int64_t t) {
+        if (p.inter_state) {
+            stage_columns();
+            const Slab it(p.inter_state, t * p.inter_stride + (int64_t)hv * (KD * VD) + vt * S_COLS,
+                          (int)threadIdx.x);
+#pragma unroll
+            for (int j = 0; j < Slab::N; ++j)
+                it.store_from_lds(stage, j);
+        }
+    };
+    HeadGate<RAWG> hg;
+    PairIn in[PF];
+    PairPre pre0;
+    {
+        // the load order as in kda_decode_q_kernel
+        if constexpr (EARLY) {
+            hg.load(p, hv, row0, pair);
+            load_pair<false, RAWG>(in[0], p, bos, h, hv, row0, pair, col);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        u32x4 piece[Slab::N];
+#pragma unroll
+        for (int j = 0; j < Slab::N; ++j)
+            piece[j] = slab.load(j);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!EARLY) {
+            hg.load(p, hv, row0, pair);
+            load_pair<false, RAWG>(in[0], p, bos, h, hv, row0, pair, col);
+        }
+#pragma unroll
+        for (int j = 1; j < PF; ++j)
+            load_pair<false, RAWG>(in[j], p, j < T ? bos + j : eos - 1, h, hv, row0, pair, col);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (EARLY) {
+            pre0 = pair_pre<S_ROWS>(in[0], hg);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < Slab::N; ++j)
+            slab.to_lds(stage, j, piece[j]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < S_ROWS; ++i)
+        s[i] = stage[Slab::lds_at(row0 + i, cl)];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+        if (j < T) {
+            const PairPre pre = (EARLY && j == 0) ? pre0 : pair_pre<S_ROWS>(in[j], hg);
+            advance_split(s, pre, in[j], p, bos + j, hv, rh, rgl, cl, col, xch);
+            keep_state(bos + j);
+        }
+    }
+    for (int64_t t = bos + PF; t < eos; ++t) {
+        load_pair<false, RAWG>(in[0], p, t, h, hv, row0, pair, col);
+        advance_split(s, pair_pre<S_ROWS>(in[0], hg), in[0], p, t, hv, rh, rgl, cl, col, xch);
+        keep_state(t);
+    }
     stage_columns();
 #pragma unroll
     for (int j = 0; j < Slab::N; ++j)
@@ -1244,16 +1508,28 @@ std::atomic<int> g_device_kind[MAX_DEVICES];   // 0 unknown, 1 gfx950, 2 other
 // graph capture).
 constexpr size_t q_lds_bytes(int nq) { return (size_t)(KD * 16 * nq + 128) * sizeof(float); }
 
+// The split-key kernel's: the staged tile (32 columns, rows 16 apart padded)
+// and the two token parities' exchange buffers of both row halves.
+constexpr size_t split_lds_bytes() { return (size_t)(KD * S_COLS + (KD / 16) * 16 + 4 * S_XCH) * sizeof(float); }
+
 template <bool NORM, bool RAWG, bool BF16S>
 bool raise_q8_lds_limit()
 {
-    const void *fns[] = {reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 1, NORM, RAWG, BF16S>),
-                         reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 2, NORM, RAWG, BF16S>),
-                         reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 3, NORM, RAWG, BF16S>),
-                         reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 4, NORM, RAWG, BF16S>)};
+    const void *fns[] = {reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 1, NORM, RAWG, BF16S, false>),
+                         reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 2, NORM, RAWG, BF16S, false>),
+                         reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 3, NORM, RAWG, BF16S, false>),
+                         reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 4, NORM, RAWG, BF16S, false>)};
     for (const void *fn : fns)
         if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)q_lds_bytes(8)) != hipSuccess)
             return false;
+    if constexpr (!BF16S) {   // the inputs-first order serves fp32 pools only
+        const void *early[] = {reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 2, NORM, RAWG, false, true>),
+                               reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 3, NORM, RAWG, false, true>),
+                               reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 4, NORM, RAWG, false, true>)};
+        for (const void *fn : early)
+            if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)q_lds_bytes(8)) != hipSuccess)
+                return false;
+    }
     return true;
 }
 
@@ -1430,47 +1706,93 @@ int32_t plan_vtile(int64_t units, int32_t T, bool norm)
     return 128;
 }
 
-// 16-column waves (kda_decode_q_kernel): 0 = not used, else waves per
-// workgroup (2, 4 or 8: 32, 64 or 128 columns).  Measured on MI355X with
-// cold caches against the 32-column kernel (H = 8 unless noted):
-//   fp32 pool, no norm, one token per request: two waves win up to 64
-//     tiles (N8: 3.88 vs 3.99 us) and lose from 128 (N16: 4.95 vs 4.75);
-//     eight waves (full 512-byte rows of the staged tile) win from 512
-//     (N64: 12.14 vs 12.94, N128: 26.8 vs 27.7, N256/H12: 76.1 vs 78.3)
-//     and lose below (N48: 10.2 vs 9.6);
-//   fp32 pool, no norm, two or more tokens: win or tie up to 512 tiles
-//     (T = 2: N16 5.52 vs 6.07, N64 12.54 vs 14.19; T = 4: N32 9.50 vs
-//     10.17, N64 14.29 vs 16.38), lose beyond (N96/T4: 24.7 vs 21.2 with
-//     eight waves); two waves below 128 tiles, four from 128;
-//   fp32 pool, packed: eight waves from 512 tiles (the H12 batch 69.0 vs
-//     69.7 us, every run);
+// 16-column waves: 0 = not used (the 32-column kernel), PLAN_SPLIT = the
+// split-key kernel (32 columns per workgroup), else kda_decode_q_kernel's
+// waves per workgroup (2, 4 or 8: 32, 64 or 128 columns).  Measured on
+// MI355X with cold caches against the 32-column kernel (us per call, H = 8
+// unless noted):
+//   fp32 pool, no norm, one token: the split-key kernel wins up to 128
+//     tiles (N1 3.05 vs 3.42, N8 3.74 vs 4.00, N16 4.68 vs 4.75) and loses
+//     from 192 (N24 5.68 vs 5.50); with the fused gate activation two waves
+//     of kda_decode_q_kernel win up to 64 tiles instead (N1 3.32, split-key
+//     3.41, 32-column 3.53; N8 3.98, 4.06, 4.09); from 512 tiles eight
+//     waves (full 512-byte rows of the staged tile; N64: 12.14 vs 12.94,
+//     N128: 26.8 vs 27.7, N256/H12: 76.1 vs 78.3), which lose below (N48:
+//     10.2 vs 9.6);
+//   fp32 pool, no norm, two or more tokens: the split-key kernel up to 192
+//     tiles (T = 4: N1 4.59 vs 4.73 with four waves, N8 5.13 vs 5.27, N24
+//     7.8 vs 8.3), and with two or three tokens up to 256 (N32/T2 7.1 vs
+//     7.8, N32/T3 7.9 vs 8.2); four waves beyond that, up to 512 tiles (T =
+//     4: N48 11.5-12.0 vs 12.4, N64 13.9-14.1 vs 17.3 split-key and 16.4
+//     32-column), which lose above (N96/T4: 24.7 vs 21.2 with the
+//     32-column kernel);
+//   fp32 pool, packed: eight waves from 512 tiles (the H12 batch 68.0 vs
+//     69.7 us);
 //   bf16 pool, no norm: four waves (64 columns: full 128-byte row pieces of
 //     bf16) win at every size and token count, step or packed (T = 1: N32
 //     5.12 vs 5.89, N128 15.8 vs 20.6; T = 4: N32 7.46 vs 9.98; the packed
 //     H12 batch 40.9 vs 50.7), where the 32-column kernel moves half lines;
+//     only the split-key kernel beats them, with two or more tokens up to
+//     32 tiles (T = 4: N1 4.85 vs 5.05, N4 5.02 vs 5.07; one token ties or
+//     loses: N4 3.59 vs 3.46);
 //   with the norm epilogue (eight waves: the head's 128 columns in one
 //     workgroup): every bf16-pool call (normed N64/H16 T=1 17.4 vs 20.1, N8
 //     T=4 9.3 vs 10.8) and fp32 step calls with two or more tokens up to
-//     512 tiles (N8/H16 T=4 10.0 vs 10.7, N32 18.8 vs 19.3); one-token fp32
+//     512 tiles (N8/H16 T=4 10.0 vs 10.7, N32 17.8 vs 19.3); one-token fp32
 //     calls gain nothing (N32/H16 12.8-13.0 both) or lose (N16: 8.9 vs 7.8).
-// T = 0 stands for a packed call.
-int32_t plan_quarter_waves(int64_t units, int32_t T, bool bf16, bool norm)
+// T = 0 stands for a packed call; raw = the fused gate activation.
+constexpr int32_t PLAN_SPLIT = 1;
+
+int32_t plan_quarter_waves(int64_t units, int32_t T, bool bf16, bool norm, bool raw)
 {
     if (norm)
         return (bf16 || (T >= 2 && units <= 512)) ? 8 : 0;
     if (bf16)
-        return 4;
-    if (T == 0 || T == 1) {
+        return (T >= 2 && units <= 32) ? PLAN_SPLIT : 4;
+    if (T == 0)
+        return units >= 512 ? 8 : 0;
+    if (T == 1) {
         if (units >= 512)
             return 8;
-        return (T == 1 && units <= 64) ? 2 : 0;
+        if (raw)
+            return units <= 64 ? 2 : 0;
+        return units <= 128 ? PLAN_SPLIT : 0;
     }
-    if (units > 512)
-        return 0;
-    return units < 128 ? 2 : 4;
+    if (units <= 192 || (units <= 256 && T <= 3))
+        return PLAN_SPLIT;
+    return units > 512 ? 0 : 4;
 }
 
-template <int NQ, int PF, bool NORM, bool RAWG, bool BF16S>
+template <int PF, bool RAWG, bool BF16S, bool EARLY>
+kda_status launch_split(const DecodeParams &p, int64_t units, hipStream_t stream)
+{
+    const int64_t blocks = units * (VD / S_COLS);
+    if (blocks > 0x7FFFFFFF)
+        return KDA_ERR_SHAPE;
+    const int32_t *slot_idx = p.slot_idx;
+    void *state = p.state;
+    int64_t slot_stride = p.slot_stride, num_slots = p.num_slots;
+    int32_t HV = p.HV, T = p.T;
+    const int32_t *status = p.status;
+    void *args[] = {&slot_idx, &state, &slot_stride, &num_slots, &HV, &T, &status, const_cast<DecodeParams *>(&p)};
+    const void *fn = reinterpret_cast<const void *>(&kda_decode_split_kernel<PF, RAWG, BF16S, EARLY>);
+    const hipError_t e = hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(256), args, split_lds_bytes(), stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+template <bool RAWG, bool BF16S>
+kda_status dispatch_split(const DecodeParams &p, int64_t units, bool early, hipStream_t s)
+{
+    constexpr bool E = !BF16S;   // bf16 pools load the tile first
+    switch (p.T) {
+    case 1: return launch_split<1, RAWG, BF16S, false>(p, units, s);
+    case 2: return E && early ? launch_split<2, RAWG, BF16S, E>(p, units, s) : launch_split<2, RAWG, BF16S, false>(p, units, s);
+    case 3: return E && early ? launch_split<3, RAWG, BF16S, E>(p, units, s) : launch_split<3, RAWG, BF16S, false>(p, units, s);
+    default: return E && early ? launch_split<4, RAWG, BF16S, E>(p, units, s) : launch_split<4, RAWG, BF16S, false>(p, units, s);
+    }
+}
+
+template <int NQ, int PF, bool NORM, bool RAWG, bool BF16S, bool EARLY>
 kda_status launch_q(const DecodeParams &p, int64_t units, hipStream_t stream)
 {
     const int64_t blocks = units * (8 / NQ);
@@ -1483,30 +1805,64 @@ kda_status launch_q(const DecodeParams &p, int64_t units, hipStream_t stream)
     const int32_t *status = p.status;
     void *args[] = {&slot_idx, &cu_seqlens, &state, &slot_stride, &num_slots, &HV, &T, &status,
                     const_cast<DecodeParams *>(&p)};
-    const void *fn = reinterpret_cast<const void *>(&kda_decode_q_kernel<NQ, PF, NORM, RAWG, BF16S>);
+    const void *fn = reinterpret_cast<const void *>(&kda_decode_q_kernel<NQ, PF, NORM, RAWG, BF16S, EARLY>);
     const hipError_t e = hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(64 * NQ), args, q_lds_bytes(NQ), stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+template <int NQ, int PF, bool NORM, bool RAWG, bool BF16S>
+kda_status launch_q_order(const DecodeParams &p, int64_t units, bool early, hipStream_t s)
+{
+    if constexpr (PF == 1 || BF16S)
+        return launch_q<NQ, PF, NORM, RAWG, BF16S, false>(p, units, s);
+    else
+        return early ? launch_q<NQ, PF, NORM, RAWG, BF16S, true>(p, units, s)
+                     : launch_q<NQ, PF, NORM, RAWG, BF16S, false>(p, units, s);
+}
+
 template <int NQ, bool NORM, bool RAWG, bool BF16S>
-kda_status dispatch_q_tokens(const DecodeParams &p, int64_t units, hipStream_t s)
+kda_status dispatch_q_tokens(const DecodeParams &p, int64_t units, bool early, hipStream_t s)
 {
     switch (p.cu_seqlens ? 4 : p.T) {
-    case 1: return launch_q<NQ, 1, NORM, RAWG, BF16S>(p, units, s);
-    case 2: return launch_q<NQ, 2, NORM, RAWG, BF16S>(p, units, s);
-    case 3: return launch_q<NQ, 3, NORM, RAWG, BF16S>(p, units, s);
-    default: return launch_q<NQ, 4, NORM, RAWG, BF16S>(p, units, s);
+    case 1: return launch_q_order<NQ, 1, NORM, RAWG, BF16S>(p, units, early, s);
+    case 2: return launch_q_order<NQ, 2, NORM, RAWG, BF16S>(p, units, early, s);
+    case 3: return launch_q_order<NQ, 3, NORM, RAWG, BF16S>(p, units, early, s);
+    default: return launch_q_order<NQ, 4, NORM, RAWG, BF16S>(p, units, early, s);
     }
+}
+
+// The load order of a 16-column-wave launch: the first token's inputs
+// before the state tile (the kernels' EARLY order) for fp32-pool calls with
+// two or more tokens per request, or packed, from 192 tiles; otherwise the
+// tile first.  Measured on MI355X with cold caches (us per call, tile first
+// vs inputs first): N8/T4/H8 5.22 vs 5.46, N16/T4 6.56 vs 6.61, N24/T4 8.03
+// vs 7.77, N32/T3 8.56 vs 8.03, N32/T4 9.47 vs 9.06, the packed H12 batch
+// 69.2 vs 68.0, normed N32/H16/T4 18.7 vs 17.8; with one token the tile
+// first wins at every size (N1 3.04 vs 3.54, N64 12.2 vs 12.9), and with a
+// bf16 pool, whose tiles are half the bytes (N32/T4 7.48 vs 7.59).
+bool plan_early(int64_t units, int32_t T, bool bf16)
+{
+    return !bf16 && T != 1 && units >= 192;
 }
 
 template <bool RAWG, bool BF16S>
 kda_status dispatch_q(const DecodeParams &p, int64_t units, int nq, bool norm, hipStream_t s)
 {
+    const bool early = plan_early(units, p.cu_seqlens ? 0 : p.T, BF16S);
     if (norm)
-        return dispatch_q_tokens<8, true, RAWG, BF16S>(p, units, s);
-    return nq == 2 ? dispatch_q_tokens<2, false, RAWG, BF16S>(p, units, s)
-         : nq == 8 ? dispatch_q_tokens<8, false, RAWG, BF16S>(p, units, s)
-                   : dispatch_q_tokens<4, false, RAWG, BF16S>(p, units, s);
+        return dispatch_q_tokens<8, true, RAWG, BF16S>(p, units, early, s);
+    if (nq == PLAN_SPLIT)
+        return dispatch_split<RAWG, BF16S>(p, units, early, s);
+    // two waves serve only one-token fp32 calls with the fused gate
+    if constexpr (RAWG && !BF16S) {
+        if (nq == 2) {
+            if (p.T != 1 || p.cu_seqlens)
+                return KDA_ERR_UNSUPPORTED;
+            return launch_q<2, 1, false, true, false, false>(p, units, s);
+        }
+    }
+    return nq == 8 ? dispatch_q_tokens<8, false, RAWG, BF16S>(p, units, early, s)
+                   : dispatch_q_tokens<4, false, RAWG, BF16S>(p, units, early, s);
 }
 
 template <int NW, bool NORM, bool BF16S, bool RAWG>
@@ -1571,7 +1927,8 @@ kda_status run_decode(const kda_decode_args *a, int32_t T, const int32_t *cu_seq
     int vtile = vtile_from_flags(flags);
     // a forced width keeps the 32-column waves; otherwise the plan may pick
     // the 16-column waves
-    const int nq = vtile == 0 ? plan_quarter_waves(units, cu_seqlens ? 0 : T, bf16_pool, norm) : 0;
+    const int nq =
+        vtile == 0 ? plan_quarter_waves(units, cu_seqlens ? 0 : T, bf16_pool, norm, a->raw_gate != nullptr) : 0;
     if (vtile == 0)
         vtile = plan_vtile(units, cu_seqlens ? 1 : T, norm);
     if (norm && vtile != 128)
@@ -1709,8 +2066,11 @@ kda_status kda_gated_rmsnorm(const void *x, const void *gate, const void *weight
 int32_t kda_decode_plan(int64_t units, int32_t T, uint32_t options)
 {
     const bool norm = (options & KDA_PLAN_NORM) != 0, packed = (options & KDA_PLAN_PACKED) != 0;
-    const int32_t nq = plan_quarter_waves(units, packed ? 0 : T, (options & KDA_PLAN_STATE_BF16) != 0, norm);
-    return nq ? 16 * nq : plan_vtile(units, packed ? 1 : T, norm);
+    const int32_t nq = plan_quarter_waves(units, packed ? 0 : T, (options & KDA_PLAN_STATE_BF16) != 0, norm,
+                                          (options & KDA_PLAN_RAW_GATE) != 0);
+    if (options & KDA_PLAN_LAYOUT)
+        return nq == 0 ? KDA_LAYOUT_WIDE : nq == PLAN_SPLIT ? KDA_LAYOUT_SPLIT : KDA_LAYOUT_QUARTER;
+    return nq == PLAN_SPLIT ? S_COLS : nq ? 16 * nq : plan_vtile(units, packed ? 1 : T, norm);
 }
 
 const char *kda_status_string(kda_status status)

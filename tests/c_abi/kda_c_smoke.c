@@ -219,8 +219,11 @@ int main(void)
         fprintf(stderr, "K = 64 was not rejected\n");
         return 1;
     }
-    /* the plan for a packed bf16 call: 64-column workgroups */
-    if (kda_decode_plan(4096, 1, KDA_PLAN_STATE_BF16 | KDA_PLAN_PACKED) != 64 || kda_decode_plan(256, 1, 0) != 64) {
+    /* the plan for a packed bf16 call: 64-column workgroups; a small step
+     * call: the split-key layout */
+    if (kda_decode_plan(4096, 1, KDA_PLAN_STATE_BF16 | KDA_PLAN_PACKED) != 64 || kda_decode_plan(256, 1, 0) != 64 ||
+        kda_decode_plan(36, 3, KDA_PLAN_LAYOUT) != KDA_LAYOUT_SPLIT ||
+        kda_decode_plan(9, 2, KDA_PLAN_STATE_BF16 | KDA_PLAN_LAYOUT) != KDA_LAYOUT_SPLIT) {
         fprintf(stderr, "unexpected launch plan\n");
         return 1;
     }
@@ -234,6 +237,8 @@ int main(void)
         rc = run_case("bf16 pool, step N=40 H=8 HV=8 T=2", 40, 8, 8, 2, NULL, 64, 1);
     if (rc == 0)
         rc = run_case("bf16 pool, packed N=7 H=1 HV=3", 7, 1, 3, 0, lens, 12, 1);
+    if (rc == 0)
+        rc = run_case("bf16 pool, step N=3 H=1 HV=3 T=2", 3, 1, 3, 2, NULL, 8, 1);
     if (rc == 0)
         printf("c abi ok\n");
     return rc;

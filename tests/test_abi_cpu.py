@@ -66,24 +66,55 @@ def test_status_strings_and_plan():
         for T in (1, 2, 4):
             assert kda.kda_decode_plan(units, T, False) in (32, 64, 128)
             assert kda.kda_decode_plan(units, T, True) == 128
-    # the launch table: 16-column waves (2 or 4 per workgroup) up to 64 tiles
-    # with one token and up to 512 with two or more, 8 per workgroup from 512
-    # tiles with one token; 32-column waves (32, 64 or 128 columns per
-    # workgroup) in between
-    expect = {(8, 1): 32, (64, 1): 32, (65, 1): 32, (256, 1): 64, (1024, 1): 128,
-              (128, 2): 64, (512, 2): 64, (513, 2): 128, (192, 3): 64,
-              (8, 4): 32, (127, 4): 32, (128, 4): 64, (512, 4): 64, (513, 4): 128, (384, 9): 64,
-              (511, 1): 64, (512, 1): 128}
-    for (units, T), width in expect.items():
+    # the launch table of fp32 step calls without the norm: split-key
+    # 16-column waves (32 columns) up to 128 tiles with one token, up to 192
+    # with more, and up to 256 with two or three; then, with one token,
+    # 32-column waves (32 or 64 columns) below 512 tiles and eight 16-column
+    # waves (128 columns) from 512; with two or more tokens four 16-column
+    # waves (64 columns) up to 512 tiles and 32-column waves of 128 columns
+    # beyond
+    W, Q, S = kda.KDA_LAYOUT_WIDE, kda.KDA_LAYOUT_QUARTER, kda.KDA_LAYOUT_SPLIT
+    expect = {(1, 1): (32, S), (8, 1): (32, S), (64, 1): (32, S), (128, 1): (32, S), (129, 1): (32, W),
+              (192, 1): (32, W), (255, 1): (32, W), (256, 1): (64, W), (511, 1): (64, W), (512, 1): (128, Q),
+              (1024, 1): (128, Q),
+              (128, 2): (32, S), (256, 2): (32, S), (257, 2): (64, Q), (512, 2): (64, Q), (513, 2): (128, W),
+              (192, 3): (32, S), (256, 3): (32, S), (257, 3): (64, Q),
+              (8, 4): (32, S), (192, 4): (32, S), (193, 4): (64, Q), (256, 4): (64, Q), (512, 4): (64, Q),
+              (513, 4): (128, W), (384, 9): (64, Q), (192, 9): (32, S), (256, 9): (64, Q)}
+    for (units, T), (width, layout) in expect.items():
         assert kda.kda_decode_plan(units, T, False) == width, (units, T)
-    # packed calls: 32-column waves with an fp32 pool; with a bf16 pool every
-    # call without the norm takes 64-column workgroups of 16-column waves
-    for units, width in ((8, 32), (256, 64), (511, 64), (512, 128), (3072, 128)):
-        assert kda.kda_decode_plan(units, 4, packed=True) == width
-        for T in (1, 4):
-            assert kda.kda_decode_plan(units, T, bf16_state=True) == 64
+        assert kda.kda_decode_plan(units, T, False, layout=True) == layout, (units, T)
+    # the fused gate activation: one-token calls take two 16-column waves
+    # (32 columns) up to 64 tiles instead of the split-key waves; the rest of
+    # the table is the same
+    raw = {(1, 1): (32, Q), (64, 1): (32, Q), (65, 1): (32, W), (128, 1): (32, W), (512, 1): (128, Q),
+           (8, 4): (32, S), (192, 2): (32, S), (300, 4): (64, Q)}
+    for (units, T), (width, layout) in raw.items():
+        assert kda.kda_decode_plan(units, T, raw_gate=True) == width, (units, T)
+        assert kda.kda_decode_plan(units, T, raw_gate=True, layout=True) == layout, (units, T)
+    # packed calls: 32-column waves with an fp32 pool below 512 tiles, eight
+    # 16-column waves from there
+    for units, width, layout in ((8, 32, W), (256, 64, W), (511, 64, W), (512, 128, Q), (3072, 128, Q)):
+        for r in (False, True):
+            assert kda.kda_decode_plan(units, 4, packed=True, raw_gate=r) == width
+            assert kda.kda_decode_plan(units, 4, packed=True, layout=True, raw_gate=r) == layout
+    # bf16 pool without the norm: split-key waves for calls of two or more
+    # tokens up to 32 tiles, else four 16-column waves (64 columns); with
+    # the norm eight
+    for units in (1, 32, 33, 256, 511, 512, 3072):
+        for T in (1, 2, 4):
+            small = units <= 32 and T >= 2
+            assert kda.kda_decode_plan(units, T, bf16_state=True) == (32 if small else 64)
+            assert kda.kda_decode_plan(units, T, bf16_state=True, layout=True) == (S if small else Q)
             assert kda.kda_decode_plan(units, T, bf16_state=True, packed=True) == 64
+            assert kda.kda_decode_plan(units, T, bf16_state=True, packed=True, layout=True) == Q
             assert kda.kda_decode_plan(units, T, True, bf16_state=True) == 128
+            assert kda.kda_decode_plan(units, T, True, bf16_state=True, layout=True) == Q
+    # the norm with an fp32 pool: eight 16-column waves for step calls of two
+    # or more tokens up to 512 tiles, else 32-column waves of 128 columns
+    for (units, T), layout in {(8, 1): W, (512, 1): W, (8, 2): Q, (512, 4): Q, (513, 4): W}.items():
+        assert kda.kda_decode_plan(units, T, True, layout=True) == layout, (units, T)
+    assert kda.kda_decode_plan(8, 4, True, packed=True, layout=True) == W
 
 
 BASE = 0x7F0000000000

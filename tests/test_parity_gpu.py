@@ -524,7 +524,8 @@ def test_validate_rejects_and_touches_nothing(case):
 @pytest.mark.parametrize("case", ["duplicate", "past_pool"])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_validate_rejects_on_quarter_waves(case, dtype):
-    """The 16-column waves (a step call of 64 tiles, four tokens) honour the
+    """The 16-column waves (a step call of 64 tiles, four tokens: split-key
+    waves with an fp32 pool, four waves per workgroup with bf16) honour the
     verdict too: nothing written."""
     p = ki.workload("n8_t4_h8")
     code = _corrupt(p, case)
@@ -699,27 +700,40 @@ def test_tile_widths_bit_identical():
 
 
 # ------------------------------------------------------- 16-column waves
+SPLIT, QUARTER = kda.KDA_LAYOUT_SPLIT, kda.KDA_LAYOUT_QUARTER
 QUARTER_CASES = [
-    # (N, H, HV, T, raw gates): the library picks the 16-column waves at all of these
-    (1, 8, 8, 4, False),      # 8 tiles, two waves per workgroup
-    (5, 1, 3, 2, False),      # three value heads per q/k head
-    (9, 4, 8, 3, True),       # fused gate activation
-    (20, 4, 8, 4, False),     # 160 tiles: four waves per workgroup
-    (7, 2, 4, 6, True),       # tokens past the four whose inputs load with the tile
-    (8, 8, 8, 1, False),      # one token, 64 tiles
-    (60, 8, 8, 2, False),     # 480 tiles, two tokens
+    # (N, H, HV, T, raw gates, the 16-column-wave layout the library picks);
+    # from 192 tiles, calls of two or more tokens load the first token's
+    # inputs before the tile
+    (1, 8, 8, 4, False, SPLIT),       # 8 tiles
+    (5, 1, 3, 2, False, SPLIT),       # three value heads per q/k head
+    (9, 4, 8, 3, True, SPLIT),        # fused gate activation
+    (24, 4, 8, 4, False, SPLIT),      # 192 tiles: the split-key layout's last size at four tokens
+    (7, 2, 4, 6, True, SPLIT),        # tokens past the four whose inputs load with the tile
+    (8, 8, 8, 1, False, SPLIT),       # one token, 64 tiles
+    (16, 2, 8, 1, False, SPLIT),      # one token, 128 tiles
+    (8, 2, 8, 1, True, QUARTER),      # one token, 64 tiles, fused gate: two waves per workgroup
+    (32, 8, 8, 3, False, SPLIT),      # 256 tiles, three tokens
+    (25, 4, 8, 4, False, QUARTER),    # 200 tiles: four waves per workgroup
+    (33, 8, 8, 2, True, QUARTER),     # 264 tiles, two tokens, fused gate
+    (40, 2, 6, 5, False, QUARTER),    # 240 tiles, five tokens
+    (60, 8, 8, 2, False, QUARTER),    # 480 tiles, two tokens
 ]
 
 
 @pytest.mark.parametrize("case", QUARTER_CASES)
 def test_quarter_waves_match_wide_waves_bitwise(case):
-    """The 16-column-wave kernel (the library's choice at these shapes) and
-    the 32-column kernel (every forced tile width) give the same bits:
-    outputs, final states and per-token states; and they match the oracle."""
-    N, H, HV, T, raw = case
+    """The 16-column-wave kernels (the library's choice at these shapes:
+    split-key waves of 16 key rows per lane, or four waves of 32 rows per
+    lane) and the 32-column kernel (every forced tile width) give the same
+    bits: outputs, final states and per-token states; and they match the
+    oracle."""
+    N, H, HV, T, raw, layout = case
     p = ki.make_problem("quarter", 300 + N, N=N, H=H, HV=HV, K=128, V=128, num_slots=2 * N + 3, T=T,
                         n_pad=N // 4, raw_gates=raw)
-    assert kda.kda_decode_plan(N * HV, T, False) == (32 if N * HV < 128 else 64)
+    assert kda.kda_decode_plan(N * HV, T, False, layout=True, raw_gate=raw) == layout
+    two_waves = raw and T == 1                  # 32 columns per workgroup
+    assert kda.kda_decode_plan(N * HV, T, False, raw_gate=raw) == (64 if layout == QUARTER and not two_waves else 32)
     results = []
     for flags in (0, kda.KDA_FLAG_VTILE(32), kda.KDA_FLAG_VTILE(64), kda.KDA_FLAG_VTILE(128)):
         d = _fresh(p)
@@ -739,17 +753,22 @@ def test_quarter_waves_match_wide_waves_bitwise(case):
         assert torch.equal(o, results[0][0]) and torch.equal(st, results[0][1]) and torch.equal(it, results[0][2])
 
 
-@pytest.mark.parametrize("case", [(1, 8, 8, 1, False), (9, 4, 8, 3, True), (20, 4, 8, 4, False),
-                                  (7, 2, 4, 6, False), (64, 8, 8, 1, False), (40, 4, 4, None, False),
-                                  (25, 2, 6, None, True)])
+@pytest.mark.parametrize("case", [(1, 8, 8, 1, False, QUARTER), (1, 8, 8, 2, False, SPLIT),
+                                  (4, 8, 8, 4, True, SPLIT), (7, 2, 4, 6, False, SPLIT),
+                                  (9, 4, 8, 3, True, QUARTER), (20, 4, 8, 4, False, QUARTER),
+                                  (32, 8, 8, 2, False, QUARTER), (64, 8, 8, 1, False, QUARTER),
+                                  (40, 4, 4, None, False, QUARTER), (25, 2, 6, None, True, QUARTER)])
 def test_quarter_waves_bf16_pool_match_wide_waves_bitwise(case):
-    """bf16 pool: the 16-column waves (64-column workgroups, widened exactly
-    into LDS, rounded once on the way out), step and packed (T None: 1 to 6
-    tokens per request), against the forced 32-column kernel, bit for bit
-    with per-token states; and against the oracle."""
-    N, H, HV, T, raw = case
+    """bf16 pool: the 16-column waves (widened exactly into LDS, rounded once
+    on the way out; split-key waves for several tokens up to 32 tiles, else
+    64-column workgroups), step and packed (T None: 1 to 6 tokens per
+    request), against the forced 32-column kernel, bit for bit with
+    per-token states; and against the oracle."""
+    N, H, HV, T, raw, layout = case
     p = ki.make_problem("quarterbf", 400 + N, N=N, H=H, HV=HV, K=128, V=128, num_slots=2 * N + 3, T=T,
                         t_max=6, n_pad=N // 4, raw_gates=raw)
+    assert kda.kda_decode_plan(N * HV, T or 1, bf16_state=True, packed=T is None, layout=True,
+                               raw_gate=raw) == layout
     results = []
     for flags in (0, kda.KDA_FLAG_VTILE(32), kda.KDA_FLAG_VTILE(128)):
         d = upload(p, background_seed=1234, state_dtype=torch.bfloat16)
