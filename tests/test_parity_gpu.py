@@ -474,7 +474,7 @@ def _status_word():
 
 
 def test_validate_passes_valid_metadata_bit_identical():
-    for name in ("n32_t1_h8", "n8_t4_h8", "packed_n256_h12", "n32_t1_h16_norm"):
+    for name in ("n32_t1_h8", "n8_t4_h8", "n24_t4_h8", "n32_t4_h8", "packed_n256_h12", "n32_t1_h16_norm"):
         p = ki.workload(name)
         a = _fresh(p)
         run_gpu(a)
@@ -523,11 +523,14 @@ def test_validate_rejects_and_touches_nothing(case):
 
 @pytest.mark.parametrize("case", ["duplicate", "past_pool"])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_validate_rejects_on_quarter_waves(case, dtype):
-    """The 16-column waves (a step call of 64 tiles, four tokens: split-key
-    waves with an fp32 pool, four waves per workgroup with bf16) honour the
-    verdict too: nothing written."""
-    p = ki.workload("n8_t4_h8")
+@pytest.mark.parametrize("name", ["n8_t4_h8", "n24_t4_h8", "n32_t4_h8"])
+def test_validate_rejects_on_quarter_waves(case, dtype, name):
+    """The 16-column waves honour the verdict too, nothing written: step
+    calls of four tokens at 64 tiles (split-key waves with an fp32 pool,
+    four waves per workgroup with bf16, both loading the tile first), 192
+    tiles (split-key, fp32: the first token's inputs before the tile) and
+    256 tiles (four waves, fp32: inputs first)."""
+    p = ki.workload(name)
     code = _corrupt(p, case)
     d = upload(p, state_dtype=dtype)
     before = d.state.clone()
@@ -907,7 +910,7 @@ def test_deterministic_and_non_default_stream():
     assert torch.equal(d1.out.view(torch.int16), d2.out.view(torch.int16))
 
 
-@pytest.mark.parametrize("name", ["n32_t1_h8", "n8_t4_h8"])
+@pytest.mark.parametrize("name", ["n32_t1_h8", "n8_t4_h8", "n32_t4_h8"])
 def test_graph_replay_matches_eager(name):
     p = ki.workload(name)
     eager = _fresh(p)
