@@ -717,6 +717,7 @@ QUARTER_CASES = [
     (16, 2, 8, 1, False, SPLIT),      # one token, 128 tiles
     (8, 2, 8, 1, True, QUARTER),      # one token, 64 tiles, fused gate: two waves per workgroup
     (32, 8, 8, 3, False, SPLIT),      # 256 tiles, three tokens
+    (24, 2, 8, 2, True, SPLIT),       # 192 tiles, two tokens, fused gate, inputs first
     (25, 4, 8, 4, False, QUARTER),    # 200 tiles: four waves per workgroup
     (33, 8, 8, 2, True, QUARTER),     # 264 tiles, two tokens, fused gate
     (40, 2, 6, 5, False, QUARTER),    # 240 tiles, five tokens
