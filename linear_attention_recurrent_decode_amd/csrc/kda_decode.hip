@@ -1179,7 +1179,7 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
     HeadGate<RAWG> hg;
     PairIn in[PF];
     float nw = 0.0f;
-    PairPre pre0;
+    PairPre pre0;   // the first token's state-free part, evaluated ahead (EARLY only)
     {
         // EARLY: the first token's inputs go out before the tile (loads
         // complete in order), so that its state-free part runs while the
@@ -1359,7 +1359,7 @@ __global__ __launch_bounds__(256) void kda_decode_split_kernel(const int32_t *sl
     };
     HeadGate<RAWG> hg;
     PairIn in[PF];
-    PairPre pre0;
+    PairPre pre0;   // the first token's state-free part, evaluated ahead (EARLY only)
     {
         // the load order as in kda_decode_q_kernel
         if constexpr (EARLY) {
