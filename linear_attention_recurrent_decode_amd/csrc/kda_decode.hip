@@ -1831,24 +1831,33 @@ kda_status dispatch_q_tokens(const DecodeParams &p, int64_t units, bool early, h
     }
 }
 
-// The load order of a 16-column-wave launch: the first token's inputs
-// before the state tile (the kernels' EARLY order) for fp32-pool calls with
-// two or more tokens per request, or packed, from 192 tiles; otherwise the
-// tile first.  Measured on MI355X with cold caches (us per call, tile first
-// vs inputs first): N8/T4/H8 5.22 vs 5.46, N16/T4 6.56 vs 6.61, N24/T4 8.03
-// vs 7.77, N32/T3 8.56 vs 8.03, N32/T4 9.47 vs 9.06, the packed H12 batch
-// 69.2 vs 68.0, normed N32/H16/T4 18.7 vs 17.8; with one token the tile
-// first wins at every size (N1 3.04 vs 3.54, N64 12.2 vs 12.9), and with a
-// bf16 pool, whose tiles are half the bytes (N32/T4 7.48 vs 7.59).
-bool plan_early(int64_t units, int32_t T, bool bf16)
+// The load order of a 16-column-wave launch (nq: waves per workgroup, or
+// PLAN_SPLIT): the first token's inputs before the state tile (the
+// kernels' EARLY order) for fp32-pool calls with two or more tokens per
+// request, or packed, from 192 tiles; with fewer than eight waves only up
+// to 256 tiles, or 384 with three or more tokens; otherwise the tile first.
+// Measured on MI355X with cold caches (us per call, H = 8, tile first vs
+// inputs first): N8/T4 5.22 vs 5.46, N16/T4 6.56 vs 6.61, N24/T4 8.03 vs
+// 7.77, N32/T3 8.56 vs 8.03, N32/T4 9.47 vs 9.06; four waves at 384 tiles
+// N48/T2 9.96 vs 10.60, N48/T3 11.07 vs 10.75, N48/T4 12.45 vs 11.86, and
+// at 512 N64/T2 12.53 vs 13.58, N64/T3 12.78 vs 13.72, N64/T4 14.61 vs
+// 14.98; eight waves: the packed H12 batch 69.2 vs 68.0, normed
+// N32/H16/T4 (512 tiles) 18.7 vs 17.8.  With one token the tile first wins
+// at every size (N1 3.04 vs 3.54, N64 12.2 vs 12.9), and with a bf16 pool,
+// whose tiles are half the bytes (N32/T4 7.48 vs 7.59).
+bool plan_early(int64_t units, int32_t T, bool bf16, int nq)
 {
-    return !bf16 && T != 1 && units >= 192;
+    if (bf16 || T == 1 || units < 192)
+        return false;
+    if (nq == 8)
+        return true;
+    return units <= 256 || (T >= 3 && units <= 384);
 }
 
 template <bool RAWG, bool BF16S>
 kda_status dispatch_q(const DecodeParams &p, int64_t units, int nq, bool norm, hipStream_t s)
 {
-    const bool early = plan_early(units, p.cu_seqlens ? 0 : p.T, BF16S);
+    const bool early = plan_early(units, p.cu_seqlens ? 0 : p.T, BF16S, norm ? 8 : nq);
     if (norm)
         return dispatch_q_tokens<8, true, RAWG, BF16S>(p, units, early, s);
     if (nq == PLAN_SPLIT)

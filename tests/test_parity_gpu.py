@@ -706,8 +706,9 @@ def test_tile_widths_bit_identical():
 SPLIT, QUARTER = kda.KDA_LAYOUT_SPLIT, kda.KDA_LAYOUT_QUARTER
 QUARTER_CASES = [
     # (N, H, HV, T, raw gates, the 16-column-wave layout the library picks);
-    # from 192 tiles, calls of two or more tokens load the first token's
-    # inputs before the tile
+    # the library also picks the load order: the first token's inputs before
+    # the tile for calls of two or more tokens from 192 tiles to 256 (384
+    # with three or more tokens), the tile first otherwise
     (1, 8, 8, 4, False, SPLIT),       # 8 tiles
     (5, 1, 3, 2, False, SPLIT),       # three value heads per q/k head
     (9, 4, 8, 3, True, SPLIT),        # fused gate activation
