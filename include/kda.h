@@ -230,7 +230,10 @@ kda_status kda_gated_rmsnorm(const void *x, const void *gate, const void *weight
  * T >= 1 for a packed call) and the given KDA_PLAN_* options, or with
  * KDA_PLAN_LAYOUT the lane layout it picks; without a forced KDA_FLAG_VTILE
  * width (which always selects KDA_LAYOUT_WIDE).  Host-only, no device
- * access. */
+ * access.  The launch choice keyed on N*HV and T is the role of vLLM PR
+ * 57585's stage predicate (description: two pipeline stages for grids of at
+ * most 32 N*HV pairs) and of FlashInfer PR 4562's qualified batch selector
+ * (description); the thresholds here are this chip's measurements. */
 int32_t kda_decode_plan(int64_t units, int32_t T, uint32_t options);
 
 /* Static description of a status code. */
