@@ -649,11 +649,14 @@ def test_reset_and_identity_on_gpu():
     compare(d, ref_out, ref_state)
 
 
-def test_large_slot_offsets():
-    """Slots whose element offset exceeds 2^31 (pool > 8 GiB at HV = 8)."""
+@pytest.mark.parametrize("N,T", [(4, 2), (25, 4)])
+def test_large_slot_offsets(N, T):
+    """Slots whose element offset exceeds 2^31 (pool > 8 GiB at HV = 8): 32
+    tiles (split-key waves, tile first) and 200 tiles (four 16-column waves,
+    the first token's inputs before the tile)."""
     HV, slots = 8, 16400
-    p = ki.make_problem("big", 10, N=4, H=8, HV=HV, K=128, V=128, num_slots=slots, T=2)
-    p.slot_idx[:] = [16399, 16384, 3, 16390]
+    p = ki.make_problem("big", 10, N=N, H=8, HV=HV, K=128, V=128, num_slots=slots, T=T)
+    p.slot_idx[:] = ([16399, 16384, 3, 16390] + list(range(16360, 16381)))[:N]
     d = upload(p)
     run_gpu(d)
     torch.cuda.synchronize()
