@@ -732,8 +732,8 @@ QUARTER_CASES = [
 @pytest.mark.parametrize("case", QUARTER_CASES)
 def test_quarter_waves_match_wide_waves_bitwise(case):
     """The 16-column-wave kernels (the library's choice at these shapes:
-    split-key waves of 16 key rows per lane, or four waves of 32 rows per
-    lane) and the 32-column kernel (every forced tile width) give the same
+    split-key waves of 16 key rows per lane, or two or four waves of 32 rows
+    per lane) and the 32-column kernel (every forced tile width) give the same
     bits: outputs, final states and per-token states; and they match the
     oracle."""
     N, H, HV, T, raw, layout = case
