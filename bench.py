@@ -15,13 +15,30 @@ copies of the pool: a call's state was last touched at least 1 GiB of state
 traffic earlier.  Every call is still exactly the workload: N requests on N
 distinct slots of a pool of num_slots slots.
 
-Timing.  The K timed calls are captured once into a HIP graph (no host
-launch overhead) and replayed between two HIP events recorded on the replay
-stream; the per-call time is the event interval over K.  Prints one JSON line.
+Protocol (after vLLM PR 57585, "Microbenchmark and earlier serving limits":
+graph replay, cold caches, untimed warmup, interleaved blocks; and FlashInfer
+PR 4562, description: a duration-calibrated graph warmup):
+  1. --warmup eager calls, then graph replays of one full slot rotation until
+     at least --warmup-ms of wall time have passed (untimed);
+  2. --blocks timed blocks of exactly --steps calls each.  Each block is one
+     HIP graph over the next --steps calls of the rotation, replayed once
+     untimed (so that the timed replay is not the graph's first), then a
+     1 GiB read sweep that evicts the caches, then a spin kernel that keeps
+     the GPU busy while the host enqueues the two events and the replay; the
+     block's time is the interval between HIP events recorded on the replay
+     stream around it.  ``value`` is the median block's us per call, with
+     the p10 and p90 of the blocks beside it.
+Then, as extra keys: a plain device copy of the call's state bytes (read and
+write, the same rotation and protocol), the host cost of one enqueue through
+the C ABI, the cache-resident time (--warm), and the CPU oracle on all host
+cores and on one.  With --flags-b the blocks alternate A B B A ... between the
+library's choice (A) and a call with extra flag bits (B), and the line
+carries both medians.  Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import concurrent.futures
 import ctypes
 import hashlib
 import json
@@ -39,11 +56,12 @@ if ROOT not in sys.path:
 
 METRIC = "KDA decode µs/call + state HBM GB/s (% of peak), N32/T1/H8/K=V=128"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
-COLD_BYTES = 1 << 30            # state traffic between two uses of the same slots
+COLD_BYTES = 1 << 30            # state traffic between two uses of the same slots; also the flush sweep
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "linear_attention_recurrent_decode_amd", "csrc", "kda_decode.hip")
 # kda_decode_plan(..., layout=True) values
-LAYOUT_NAMES = {0: "32-column waves", 1: "16-column waves", 2: "16-column waves, split key rows"}
+LAYOUT_NAMES = {0: "32-column waves", 1: "16-column waves", 2: "16-column waves, split key rows",
+                3: "16-column waves, tokens chunked"}
 
 
 def log(*a):
@@ -91,6 +109,23 @@ def slot_sets(p, ki):
     return sets
 
 
+def block_order(n_blocks: int, two_arms: bool) -> list:
+    """Arm of each timed block: all 'A', or A B B A A B B A ... (each arm
+    n_blocks times), so that a drift over the run weighs on both arms alike."""
+    if not two_arms:
+        return ["A"] * n_blocks
+    order = []
+    for i in range(n_blocks):
+        order += ["A", "B"] if i % 2 == 0 else ["B", "A"]
+    return order
+
+
+def spread(values) -> dict:
+    """Median, p10 and p90 of a list of per-block figures."""
+    v = np.asarray(values, dtype=np.float64)
+    return {"median": float(np.median(v)), "p10": float(np.percentile(v, 10)), "p90": float(np.percentile(v, 90))}
+
+
 def kernel_code_sha256(path: str = KERNEL_SRC) -> str:
     """SHA-256 of the kernel source's code: comments and whitespace removed,
     so that editing a comment does not void the recorded counters (the
@@ -116,43 +151,152 @@ def traffic_for(workload: str):
         return None
 
 
-def cpu_baseline(p, pool_live: np.ndarray, budget_s: float) -> dict:
-    """The CPU oracle, single-threaded, on full calls of the same workload."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def request_chunks(n: int, parts: int) -> list:
+    """Contiguous ranges of a call's requests, one per worker (empty ones dropped)."""
+    parts = max(1, min(parts, n))
+    bounds = np.linspace(0, n, parts + 1).round().astype(int)
+    return [(int(a), int(b)) for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
+
+
+def cpu_baseline(p, pool_live: np.ndarray, budget_s: float, threads: int) -> dict:
+    """The CPU oracle on full calls of the same workload and inputs, on a
+    compact pool that holds the live requests' slots.  With threads > 1 the
+    call's requests are split into contiguous ranges that threads run at
+    once (the oracle's C code releases the interpreter lock; each range owns
+    its requests' state slots and output rows)."""
     import oracle
     live = p.live_requests()
     remap = np.full(p.N, -1, dtype=np.int32)
     remap[live] = np.arange(len(live), dtype=np.int32)
+    cu = p.cu_seqlens.astype(np.int32)
     kw = {}
     if p.gate is not None:
         kw = dict(gate=p.gate, norm_weight=p.norm_weight, eps=p.eps)
     if p.raw:
         kw.update(raw_gate=p.raw_gate, raw_beta=p.raw_beta, A_log=p.A_log, dt_bias=p.dt_bias)
     pool = pool_live.astype(np.float64)
-    oracle.decode_packed(p.q, p.k, p.v, p.g, p.beta, pool, remap, p.cu_seqlens, p.scale, **kw)  # warm-up
-    n, t0 = 0, time.perf_counter()
-    while True:
-        oracle.decode_packed(p.q, p.k, p.v, p.g, p.beta, pool, remap, p.cu_seqlens, p.scale, **kw)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
+    out = np.zeros((p.tokens, p.HV, p.V), dtype=np.float64)
+    jobs = [(np.ascontiguousarray(remap[a:b]), np.ascontiguousarray(cu[a:b + 1]))
+            for a, b in request_chunks(p.N, threads)]
+
+    def run(job):
+        slots, cu_r = job
+        oracle.decode_packed(p.q, p.k, p.v, p.g, p.beta, pool, slots, cu_r, p.scale, out=out, **kw)
+
+    ex = concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) if len(jobs) > 1 else None
+
+    def one_call():
+        if ex is None:
+            run(jobs[0])
+        else:
+            list(ex.map(run, jobs))
+
+    try:
+        one_call()   # warm-up
+        n, t0 = 0, time.perf_counter()
+        while True:
+            one_call()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+    finally:
+        if ex is not None:
+            ex.shutdown()
     us = el / n * 1e6
-    return {"value": round(us, 3), "unit": "us/call", "cores": 1, "kind": "oracle",
+    how = (f"the call's requests split into {len(jobs)} contiguous ranges run by {len(jobs)} threads at once"
+           if len(jobs) > 1 else "one host thread")
+    return {"value": round(us, 3), "unit": "us/call", "cores": len(jobs), "kind": "oracle",
             "sample": f"{n} full calls of the {p.name} workload ({p.N} requests x {p.HV} value heads, "
-                      f"{p.tokens} tokens), same inputs as the GPU run, double-precision sequential oracle "
-                      f"on one host thread, {el:.1f} s"}
+                      f"{p.tokens} tokens), same inputs as the GPU run, double-precision sequential oracle, "
+                      f"{how}, {el:.1f} s",
+            "cpu_model": cpu_model(), "host_cores_available": len(os.sched_getaffinity(0))}
+
+
+class Timer:
+    """Graph-replay timing on one stream with the protocol of the module
+    docstring: upload replay, cache flush, busy preamble, events."""
+
+    def __init__(self, torch, stream, dev):
+        self.torch = torch
+        self.stream = stream
+        self.flush_buf = torch.ones(COLD_BYTES // 4, dtype=torch.float32, device=dev)
+        self.sink = torch.zeros((), dtype=torch.float32, device=dev)
+        self.spin_cycles = self._calibrate_spin()
+
+    def _calibrate_spin(self) -> int:
+        """Cycles of torch's spin kernel that take about 0.3 ms here."""
+        torch = self.torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cycles = 200_000
+        with torch.cuda.stream(self.stream):
+            torch.cuda._sleep(cycles)
+            e0.record(self.stream)
+            torch.cuda._sleep(cycles)
+            e1.record(self.stream)
+        torch.cuda.synchronize()
+        ms = max(e0.elapsed_time(e1), 1e-3)
+        return int(min(max(cycles * 0.3 / ms, 10_000), 50_000_000))
+
+    def flush(self):
+        """Read 1 GiB through the caches (MI355X: 256 MiB memory-side cache,
+        8 x 4 MiB L2), so that the next block starts cold."""
+        with self.torch.cuda.stream(self.stream):
+            self.torch.sum(self.flush_buf, dim=0, out=self.sink)
+
+    def capture(self, body):
+        torch = self.torch
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(self.stream):
+            with torch.cuda.graph(graph, stream=self.stream):
+                body()
+        torch.cuda.synchronize()
+        return graph
+
+    def time_graph(self, graph, calls: int, cold: bool = True) -> float:
+        """us per call of one timed replay of ``graph`` (``calls`` calls)."""
+        torch = self.torch
+        graph.replay()                     # not the graph's first replay when timed
+        if cold:
+            self.flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(self.stream):
+            torch.cuda._sleep(self.spin_cycles)   # the GPU is busy while the host enqueues what follows
+            e0.record(self.stream)
+            graph.replay()
+            e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / calls
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=2000, help="calls per timed block")
+    ap.add_argument("--warmup", type=int, default=200, help="untimed eager calls before the calibrated warmup")
+    ap.add_argument("--warmup-ms", type=float, default=100.0, help="minimum wall time of graph-replayed warmup")
+    ap.add_argument("--blocks", type=int, default=5, help="timed blocks (at least 3)")
     ap.add_argument("--workload", default="n32_t1_h8")
-    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=8.0, help="seconds of oracle work per cpu_baseline run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the copy reference and the enqueue cost")
     ap.add_argument("--warm", action="store_true", help="also time cache-resident calls (same slots every call)")
     ap.add_argument("--state", choices=("fp32", "bf16"), default="fp32", help="state pool element type")
+    ap.add_argument("--flags-b", type=lambda s: int(s, 0), default=None,
+                    help="extra call flag bits of a second arm, timed in A B B A order against the default")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed region, run 5 plain device copies of this many MiB (untimed), "
                          "a known-size reference for hardware byte counters")
@@ -161,6 +305,9 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: recurrent KDA decode has no cross-GPU step here; "
               "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.blocks < 3 or args.steps < 1:
+        print("bench.py needs --blocks >= 3 and --steps >= 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -178,11 +325,12 @@ def main():
     p = ki.workload(args.workload)
     bf16_state = args.state == "bf16"
     state_dtype = torch.bfloat16 if bf16_state else torch.float32
-    nbytes = algorithmic_bytes(p, 2 if bf16_state else 4)
+    state_elem = 2 if bf16_state else 4
+    nbytes = algorithmic_bytes(p, state_elem)
     sets = slot_sets(p, ki)
     per_call_read = nbytes["state"] // 2
     R = max(1, math.ceil(COLD_BYTES / max(1, len(sets) * per_call_read)))
-    pool_bytes = p.num_slots * p.slot_elems * (2 if bf16_state else 4)
+    pool_bytes = p.num_slots * p.slot_elems * state_elem
     if R * pool_bytes > (96 << 30):
         R = max(1, (96 << 30) // pool_bytes)
     log(f"[bench] workload {p.name}: N={p.N} T={p.T} H={p.H} HV={p.HV} tokens={p.tokens} "
@@ -221,70 +369,119 @@ def main():
     combos = []
     for r in range(R):
         for s in set_t:
-            a = kda.decode_args(q, k, v, g, beta, pools[r], s, out, p.scale, gate, w, p.eps, **raw)
-            combos.append(a)
+            combos.append(kda.decode_args(q, k, v, g, beta, pools[r], s, out, p.scale, gate, w, p.eps, **raw))
     T = p.T if p.T is not None else 0
     packed = p.T is None
-    call_flags = kda.KDA_FLAG_STATE_BF16 if bf16_state else 0
+    base_flags = kda.KDA_FLAG_STATE_BF16 if bf16_state else 0
     cu_ptr = cu.data_ptr()
 
-    def launch(i, stream_handle):
-        a = combos[i % len(combos)]
+    def launch(i, stream_handle, extra_flags=0, which=None):
+        a = (which or combos)[i % len(which or combos)]
         if packed:
-            st = lib.kda_decode_packed(ctypes.byref(a), cu_ptr, p.tokens, call_flags, stream_handle)
+            st = lib.kda_decode_packed(ctypes.byref(a), cu_ptr, p.tokens, base_flags | extra_flags, stream_handle)
         else:
-            st = lib.kda_decode_step(ctypes.byref(a), T, call_flags, stream_handle)
+            st = lib.kda_decode_step(ctypes.byref(a), T, base_flags | extra_flags, stream_handle)
         if st != 0:
             raise kda.KdaError(st, "decode")
 
     stream = torch.cuda.Stream()
     sh = stream.cuda_stream
+    timer = Timer(torch, stream, dev)
 
-    def capture(n, offset=0):
-        graph = torch.cuda.CUDAGraph()
-        torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            with torch.cuda.graph(graph, stream=stream):
-                for i in range(n):
-                    launch(offset + i, sh)
-        torch.cuda.synchronize()
-        return graph
-
-    # warm-up: eager calls, then the warm-up graph
+    # 1. warmup: eager calls, then replays of one full rotation for >= warmup_ms
+    pos = 0
     with torch.cuda.stream(stream):
-        for i in range(min(args.warmup, 20)):
-            launch(i, sh)
+        for i in range(args.warmup):
+            launch(pos + i, sh)
+    pos += args.warmup
     torch.cuda.synchronize()
-    g_warm = capture(max(1, args.warmup))
-    g_warm.replay()
-    torch.cuda.synchronize()
-    g_timed = capture(args.steps, offset=args.warmup)
+    start = pos
+    g_warm = timer.capture(lambda: [launch(start + i, sh) for i in range(len(combos))])
+    warm_calls, t0 = 0, time.perf_counter()
+    while True:
+        g_warm.replay()
+        torch.cuda.synchronize()
+        warm_calls += len(combos)
+        warm_ms = (time.perf_counter() - t0) * 1000.0
+        if warm_ms >= args.warmup_ms and warm_calls >= 20:
+            break
+    del g_warm
+    log(f"[bench] calibrated warmup: {warm_calls} calls in {warm_ms:.1f} ms")
 
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        g_timed.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
-    us_per_call = ms * 1000.0 / args.steps
-    log(f"[bench] timed {args.steps} calls: {ms:.3f} ms, {us_per_call:.3f} us/call")
+    # 2. timed blocks, each its own graph over the next `steps` calls of the rotation
+    arms = {"A": 0}
+    if args.flags_b is not None:
+        arms["B"] = int(args.flags_b)
+    per_arm = {a: [] for a in arms}
+    for arm in block_order(args.blocks, len(arms) > 1):
+        start = pos
+        graph = timer.capture(lambda: [launch(start + i, sh, arms[arm]) for i in range(args.steps)])
+        pos += args.steps
+        us = timer.time_graph(graph, args.steps)
+        per_arm[arm].append(us)
+        del graph
+    blocks_a = per_arm["A"]
+    sp = spread(blocks_a)
+    us_per_call = sp["median"]
+    log(f"[bench] {len(blocks_a)} blocks of {args.steps} calls: median {us_per_call:.3f} us/call "
+        f"(p10 {sp['p10']:.3f}, p90 {sp['p90']:.3f}); blocks {[round(x, 3) for x in blocks_a]}")
 
-    warm = None
+    extras = {}
     if args.warm:
-        hot = [combos[0]] * len(combos)
-        saved, combos[:] = list(combos), hot
-        g_hot = capture(args.steps)
-        combos[:] = saved
-        torch.cuda.synchronize()
+        hot = [combos[0]]
+        graph = timer.capture(lambda: [launch(i, sh, which=hot) for i in range(args.steps)])
+        extras["cache_resident_us_per_call"] = round(timer.time_graph(graph, args.steps, cold=False), 4)
+        del graph
+        log(f"[bench] cache-resident: {extras['cache_resident_us_per_call']:.3f} us/call")
+
+    if not args.no_extras:
+        # a plain device copy of the call's state bytes (half read, half written), cold by rotation
+        half = max(4, per_call_read // 4) * 4
+        n_chunks = max(2, math.ceil(COLD_BYTES / half))
+        src = torch.ones(n_chunks * half // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        ch = half // 4
+
+        def copies(first, n):
+            for i in range(first, first + n):
+                j = i % n_chunks
+                dst[j * ch:(j + 1) * ch].copy_(src[j * ch:(j + 1) * ch])
+
+        copy_blocks = []
+        cpos = 0
+        for _ in range(3):
+            c0 = cpos
+            graph = timer.capture(lambda: copies(c0, args.steps))
+            cpos += args.steps
+            copy_blocks.append(timer.time_graph(graph, args.steps))
+            del graph
+        copy_us = float(np.median(copy_blocks))
+        extras["copy_reference"] = {
+            "us_per_call": round(copy_us, 4), "GBps": round(2 * half / (copy_us * 1e-6) / 1e9, 1),
+            "bytes_per_call": 2 * half,
+            "what": "torch device copy of the call's state bytes (read + write), one copy per call, the same "
+                    "cold rotation, graph replay and timing protocol: the achievable streaming rate at this size "
+                    "with the same per-launch cost"}
+        del src, dst
+        log(f"[bench] copy reference: {copy_us:.3f} us/call, {extras['copy_reference']['GBps']} GB/s")
+
+        # host cost of one enqueue through the C ABI (validation + launch), from Python via ctypes
+        batch, batches = 1000, 10
+        per_batch = []
         with torch.cuda.stream(stream):
-            e0.record(stream)
-            g_hot.replay()
-            e1.record(stream)
+            for b in range(batches):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter_ns()
+                for i in range(batch):
+                    launch(i, sh)
+                per_batch.append((time.perf_counter_ns() - t0) / batch)
         torch.cuda.synchronize()
-        warm = e0.elapsed_time(e1) * 1000.0 / args.steps
-        log(f"[bench] cache-resident: {warm:.3f} us/call")
+        extras["host_enqueue_ns"] = {
+            "median": round(float(np.median(per_batch)), 1), "calls": batch * batches,
+            "what": "host time per kda_decode_step / kda_decode_packed call (argument validation and kernel "
+                    "launch), called from Python through ctypes, batches of 1000 enqueues with the GPU drained "
+                    "between batches"}
+        log(f"[bench] host enqueue: {extras['host_enqueue_ns']['median']:.0f} ns per call")
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 18            # floats
@@ -297,7 +494,7 @@ def main():
 
     achieved = nbytes["total"] / (us_per_call * 1e-6) / 1e9
     state_gbps = nbytes["state"] / (us_per_call * 1e-6) / 1e9
-    traffic = traffic_for(p.name)
+    traffic = traffic_for(p.name) if not bf16_state else traffic_for(p.name + "_bf16state")
     result = {
         "metric": METRIC,
         "value": round(us_per_call, 4),
@@ -305,7 +502,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms / args.steps, 6),
+        "ms_per_step": round(us_per_call / 1000.0, 6),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -321,17 +518,30 @@ def main():
                    "lane_layout": LAYOUT_NAMES[kda.kda_decode_plan(p.N * p.HV, T or 1, p.gate is not None,
                                                                    bf16_state, packed, layout=True,
                                                                    raw_gate=p.raw)]},
+        "blocks": len(blocks_a),
+        "block_us_per_call": [round(x, 4) for x in blocks_a],
+        "median": round(sp["median"], 4), "p10": round(sp["p10"], 4), "p90": round(sp["p90"], 4),
+        "warmup_calibrated": {"calls": warm_calls, "ms": round(warm_ms, 1)},
         "state_GBps": round(state_gbps, 1),
         "state_frac_of_peak": round(state_gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_call": nbytes["total"],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
     }
-    if warm is not None:
-        result["cache_resident_us_per_call"] = round(warm, 4)
+    if "B" in per_arm:
+        sb = spread(per_arm["B"])
+        result["ab"] = {"flags_b": arms["B"], "order": "ABBA", "a_blocks": [round(x, 4) for x in blocks_a],
+                        "b_blocks": [round(x, 4) for x in per_arm["B"]], "a_median": round(sp["median"], 4),
+                        "b_median": round(sb["median"], 4),
+                        "b_vs_a_pct": round(100.0 * (sb["median"] / sp["median"] - 1.0), 2)}
+    result.update(extras)
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle ...")
-        result["cpu_baseline"] = cpu_baseline(p, pool_live, args.cpu_budget)
+        threads = len(os.sched_getaffinity(0))
+        log(f"[bench] timing the CPU oracle on {threads} threads ...")
+        result["cpu_baseline"] = cpu_baseline(p, pool_live, args.cpu_budget, threads)
+        if threads > 1:
+            log("[bench] timing the CPU oracle on one thread ...")
+            result["cpu_baseline_one_thread"] = cpu_baseline(p, pool_live, args.cpu_budget / 2, 1)
     print(json.dumps(result), flush=True)
 
 

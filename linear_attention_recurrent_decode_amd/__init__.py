@@ -137,9 +137,27 @@ def _stream(stream) -> Optional[int]:
     return int(stream)
 
 
-def _check(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int):
+def _current_device() -> torch.device:
+    """The GPU every tensor of a call must live on: torch's current device."""
+    return torch.device("cuda", torch.cuda.current_device())
+
+
+def _on_device(t: torch.Tensor, name: str, device: Optional[torch.device]):
+    """Raise unless ``t`` lives on ``device`` (None: torch's current GPU).  A
+    host tensor's data_ptr() is a host address; handed to a kernel it would
+    fault the GPU, so it is refused here, before any library call."""
+    if device is None:
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor, got one on {t.device}")
+        device = _current_device()
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call runs on {device}")
+
+
+def _check(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int, device: Optional[torch.device] = None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
+    _on_device(t, name, device)
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if t.dim() != ndim:
@@ -171,13 +189,25 @@ def decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate=None, norm_w
     """Marshal tensors into a ``kda_decode_args`` struct (no validation of
     values; the library validates sizes, alignment and overlap).  The gate
     inputs come either activated (g, beta) or raw (raw_gate, raw_beta, A_log,
-    dt_bias, with g = beta = None): the kernel then activates them."""
-    _check(q, "q", torch.bfloat16, 3)
-    _check(k, "k", torch.bfloat16, 3)
-    _check(v, "v", torch.bfloat16, 3)
-    _check(state, "state", state.dtype if state.dtype in (torch.float32, torch.bfloat16) else torch.float32, 4)
-    _check(slot_idx, "slot_idx", torch.int32, 1)
-    _check(out, "out", torch.bfloat16, 3)
+    dt_bias, with g = beta = None): the kernel then activates them.  Every
+    tensor must live on torch's current GPU (ValueError otherwise)."""
+    return _marshal_args(q, k, v, g, beta, state, slot_idx, out, scale, gate, norm_weight, eps, device_status,
+                         inter_state, raw_gate, raw_beta, A_log, dt_bias, device=None)
+
+
+def _marshal_args(q, k, v, g, beta, state, slot_idx, out, scale, gate, norm_weight, eps, device_status,
+                  inter_state, raw_gate, raw_beta, A_log, dt_bias, *, device) -> KdaDecodeArgs:
+    """decode_args with the device every tensor must be on made explicit
+    (None: torch's current GPU, the only value the library calls use)."""
+    if device is None:
+        _on_device(q, "q", None)   # a host tensor is refused before any device query
+        device = _current_device()
+    _check(q, "q", torch.bfloat16, 3, device)
+    _check(k, "k", torch.bfloat16, 3, device)
+    _check(v, "v", torch.bfloat16, 3, device)
+    _check(state, "state", state.dtype if state.dtype in (torch.float32, torch.bfloat16) else torch.float32, 4, device)
+    _check(slot_idx, "slot_idx", torch.int32, 1, device)
+    _check(out, "out", torch.bfloat16, 3, device)
     tokens, H, K = q.shape
     HV, V = v.shape[1], v.shape[2]
     if k.shape != q.shape or v.shape[0] != tokens or out.shape != (tokens, HV, V) or state.shape[1:] != (HV, K, V):
@@ -192,10 +222,10 @@ def decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate=None, norm_w
     a.k, a.k_stride = k.data_ptr(), _lead_stride(k)
     a.v, a.v_stride = v.data_ptr(), _lead_stride(v)
     if raw:
-        _check(raw_gate, "raw_gate", torch.bfloat16, 3)
-        _check(raw_beta, "raw_beta", torch.bfloat16, 2)
-        _check(A_log, "A_log", torch.float32, 1)
-        _check(dt_bias, "dt_bias", torch.float32, 2)
+        _check(raw_gate, "raw_gate", torch.bfloat16, 3, device)
+        _check(raw_beta, "raw_beta", torch.bfloat16, 2, device)
+        _check(A_log, "A_log", torch.float32, 1, device)
+        _check(dt_bias, "dt_bias", torch.float32, 2, device)
         if raw_gate.shape != (tokens, HV, K) or raw_beta.shape != (tokens, HV) or A_log.shape != (HV,) or \
                 dt_bias.shape != (HV, K):
             raise ValueError("inconsistent raw gate shapes")
@@ -203,8 +233,8 @@ def decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate=None, norm_w
         a.raw_beta, a.raw_beta_stride = raw_beta.data_ptr(), _lead_stride(raw_beta)
         a.A_log, a.dt_bias = A_log.data_ptr(), dt_bias.data_ptr()
     else:
-        _check(g, "g", torch.float32, 3)
-        _check(beta, "beta", torch.float32, 2)
+        _check(g, "g", torch.float32, 3, device)
+        _check(beta, "beta", torch.float32, 2, device)
         if g.shape != (tokens, HV, K) or beta.shape != (tokens, HV):
             raise ValueError("inconsistent shapes")
         a.g, a.g_stride = g.data_ptr(), _lead_stride(g)
@@ -215,18 +245,18 @@ def decode_args(q, k, v, g, beta, state, slot_idx, out, scale, gate=None, norm_w
     if (gate is None) != (norm_weight is None):
         raise ValueError("gate and norm_weight go together")
     if gate is not None:
-        _check(gate, "gate", torch.bfloat16, 3)
-        _check(norm_weight, "norm_weight", torch.bfloat16, 1)
+        _check(gate, "gate", torch.bfloat16, 3, device)
+        _check(norm_weight, "norm_weight", torch.bfloat16, 1, device)
         if gate.shape != out.shape or norm_weight.shape != (V,):
             raise ValueError("inconsistent gate / norm_weight shapes")
         a.gate, a.gate_stride = gate.data_ptr(), _lead_stride(gate)
         a.norm_weight = norm_weight.data_ptr()
     a.norm_eps = float(eps)
     if device_status is not None:
-        _check(device_status, "device_status", torch.int32, 1)
+        _check(device_status, "device_status", torch.int32, 1, device)
         a.device_status = device_status.data_ptr()
     if inter_state is not None:
-        _check(inter_state, "inter_state", state.dtype, 4)
+        _check(inter_state, "inter_state", state.dtype, 4, device)
         if inter_state.shape != (tokens, HV, K, V):
             raise ValueError("inter_state must be [tokens, HV, K, V]")
         a.inter_state, a.inter_stride = inter_state.data_ptr(), _lead_stride(inter_state)
@@ -270,7 +300,7 @@ def kda_decode_packed(q, k, v, g, beta, state, slot_idx, cu_seqlens, out, *, sca
                     inter_state, raw_gate, raw_beta, A_log, dt_bias)
     if device_status is not None:
         flags = int(flags) | KDA_FLAG_VALIDATE
-    _check(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, 1, q.device)
     if cu_seqlens.shape[0] != a.N + 1:
         raise ValueError("cu_seqlens must hold N+1 entries")
     flags = _state_flag(state, flags)
@@ -282,6 +312,10 @@ def kda_decode_packed(q, k, v, g, beta, state, slot_idx, cu_seqlens, out, *, sca
 
 def kda_gated_rmsnorm(x, gate, weight, y, eps: float = 1e-6, stream=None):
     """y = x / sqrt(mean(x^2) + eps) * weight * silu(gate) over the last dim."""
+    _on_device(x, "x", None)
+    device = _current_device()
+    for t, n in ((x, "x"), (gate, "gate"), (y, "y"), (weight, "weight")):
+        _on_device(t, n, device)
     for t, n in ((x, "x"), (gate, "gate"), (y, "y")):
         if t.dtype != torch.bfloat16 or not t.is_contiguous():
             raise ValueError(f"{n} must be a contiguous bf16 tensor")

@@ -33,6 +33,64 @@ import oracle
 
 DEV = "cuda:0"
 SENTINEL_BITS = 0xC640     # bf16 -12288.0: marks output rows nobody may write
+GUARD_BYTES = 4096         # guard region on each side of every buffer the library writes
+GUARD_WORD = 0x7FA5        # 16-bit guard pattern (a NaN as bf16, and as the high half of an fp32)
+
+
+class Guarded:
+    """A device tensor with GUARD_BYTES of a fixed bit pattern on each side,
+    carved out of one allocation, so that a write past either end of the
+    tensor lands in a guard region and is seen by ``intact()``, instead of
+    corrupting whatever torch put next to it."""
+
+    def __init__(self, shape, dtype: torch.dtype):
+        self.shape, self.dtype = tuple(shape), dtype
+        nbytes = int(np.prod(self.shape)) * torch.empty((), dtype=dtype).element_size()
+        self.nbytes = nbytes
+        self.raw = torch.empty(2 * GUARD_BYTES + nbytes, dtype=torch.uint8, device=DEV)
+        self.raw.view(torch.int16).fill_(GUARD_WORD)
+        self.tensor = self.raw[GUARD_BYTES:GUARD_BYTES + nbytes].view(dtype).view(self.shape)
+
+    def intact(self) -> bool:
+        words = self.raw.view(torch.int16)
+        g = GUARD_BYTES // 2
+        return bool((words[:g] == GUARD_WORD).all()) and bool((words[g + self.nbytes // 2:] == GUARD_WORD).all())
+
+
+# every DeviceProblem upload() made since the last reset: a test's teardown
+# checks all their guards (check_all_guards), whether or not it compared
+CREATED: list = []
+
+
+def check_all_guards():
+    """Assert the guards of every problem uploaded since the last call, then forget them."""
+    try:
+        for d in CREATED:
+            assert_guards(d)
+    finally:
+        CREATED.clear()
+
+
+def guarded_empty(d, shape, dtype) -> torch.Tensor:
+    """A guarded tensor whose guards ``compare`` (and ``assert_guards``)
+    check along with the problem's own (for inter_state buffers and the like)."""
+    gt = Guarded(shape, dtype)
+    d.guards.append(gt)
+    return gt.tensor
+
+
+def guarded_full(d, shape, value, dtype=torch.float32) -> torch.Tensor:
+    """guarded_empty filled with ``value``."""
+    t = guarded_empty(d, shape, dtype)
+    t.fill_(value)
+    return t
+
+
+def assert_guards(d):
+    """Every guard region around the problem's written buffers still holds its pattern."""
+    torch.cuda.synchronize()
+    for gt in d.guards:
+        assert gt.intact(), f"a write past the end of a {gt.dtype} {gt.shape} buffer"
 
 
 def bf16_tensor(bits: np.ndarray) -> torch.Tensor:
@@ -67,6 +125,7 @@ class DeviceProblem:
     raw_beta: torch.Tensor | None = None
     A_log: torch.Tensor | None = None
     dt_bias: torch.Tensor | None = None
+    guards: list = dataclasses.field(default_factory=list)
 
     def gate_kwargs(self) -> dict:
         """The raw gate inputs as keyword arguments of the binding (empty for
@@ -85,8 +144,9 @@ def upload(p: ki.Problem, background_seed: int = 1234, state_dtype=torch.float32
     live_slots = p.slot_idx[live].astype(np.int64)
     gen = torch.Generator(device=DEV)
     gen.manual_seed(background_seed)
-    state = (torch.randn((p.num_slots, p.HV, p.K, p.V), generator=gen, device=DEV, dtype=torch.float32) * 0.05
-             ).to(state_dtype)
+    state_g = Guarded((p.num_slots, p.HV, p.K, p.V), state_dtype)
+    state = state_g.tensor
+    state.copy_(torch.randn((p.num_slots, p.HV, p.K, p.V), generator=gen, device=DEV, dtype=torch.float32) * 0.05)
     if len(live_slots):
         vals = p.state_slots(live_slots)
         if state_dtype == torch.bfloat16:
@@ -94,20 +154,23 @@ def upload(p: ki.Problem, background_seed: int = 1234, state_dtype=torch.float32
         else:
             live_t = f32_tensor(vals)
         state[torch.from_numpy(live_slots).to(DEV)] = live_t
-    out = torch.empty((p.tokens, p.HV, p.V), device=DEV, dtype=torch.int16).fill_(
-        np.int16(np.uint16(SENTINEL_BITS).view(np.int16))).view(torch.bfloat16)
+    out_g = Guarded((p.tokens, p.HV, p.V), torch.bfloat16)
+    out = out_g.tensor
+    out.view(torch.int16).fill_(int(np.uint16(SENTINEL_BITS).view(np.int16)))
     raw = {}
     if p.raw:
         raw = dict(raw_gate=bf16_tensor(p.raw_gate), raw_beta=bf16_tensor(p.raw_beta), A_log=f32_tensor(p.A_log),
                    dt_bias=f32_tensor(p.dt_bias))
-    return DeviceProblem(
+    d = DeviceProblem(
         p=p, q=bf16_tensor(p.q), k=bf16_tensor(p.k), v=bf16_tensor(p.v),
         g=None if p.g is None else f32_tensor(p.g), beta=None if p.beta is None else f32_tensor(p.beta), state=state,
         slot_idx=torch.from_numpy(p.slot_idx.astype(np.int32)).to(DEV),
         cu_seqlens=torch.from_numpy(p.cu_seqlens.astype(np.int32)).to(DEV), out=out,
         gate=None if p.gate is None else bf16_tensor(p.gate),
         norm_weight=None if p.norm_weight is None else bf16_tensor(p.norm_weight),
-        live_slots=live_slots, **raw)
+        live_slots=live_slots, guards=[state_g, out_g], **raw)
+    CREATED.append(d)
+    return d
 
 
 def run_gpu(d: DeviceProblem, packed: bool | None = None, flags: int = 0, stream=None, device_status=None,
@@ -166,8 +229,9 @@ class Report:
 
 def compare(d: DeviceProblem, ref_out: np.ndarray, ref_state: np.ndarray, strict: bool = True) -> Report:
     """Stated and strict tolerances on outputs and final state; skipped rows
-    must still hold the sentinel."""
+    must still hold the sentinel; every guard region is intact."""
     p = d.p
+    assert_guards(d)
     out = bf16_to_f64(d.out)
     live = np.isfinite(ref_out)
     dead_rows = ~live

@@ -66,3 +66,45 @@ def test_more_than_one_gpu_is_refused():
                          text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_block_order_interleaves_two_arms():
+    assert bench.block_order(3, False) == ["A"] * 3
+    order = bench.block_order(4, True)
+    assert order == ["A", "B", "B", "A", "A", "B", "B", "A"]
+    assert order.count("A") == order.count("B") == 4
+
+
+def test_spread_of_blocks():
+    sp = bench.spread([5.0, 1.0, 3.0, 2.0, 4.0])
+    assert sp["median"] == 3.0 and sp["p10"] == 1.4 and abs(sp["p90"] - 4.6) < 1e-12
+
+
+def test_request_chunks_cover_the_call():
+    for n, parts in ((32, 8), (256, 8), (3, 8), (1, 1), (10, 3)):
+        ch = bench.request_chunks(n, parts)
+        assert ch[0][0] == 0 and ch[-1][1] == n
+        assert all(a < b for a, b in ch)
+        assert all(ch[i][1] == ch[i + 1][0] for i in range(len(ch) - 1))
+        assert len(ch) == min(n, parts)
+
+
+def test_threaded_oracle_equals_one_thread():
+    """The all-core CPU baseline splits a call's requests over threads; the
+    split changes nothing in the result (each range owns its slots and rows)."""
+    import oracle
+    p = ki.make_problem("split", 5, N=10, H=2, HV=2, K=8, V=8, num_slots=14, T=None, n_pad=3)
+    live = p.live_requests()
+    pool0 = p.state_slots(p.slot_idx[live]).astype(np.float64)
+    remap = np.full(p.N, -1, dtype=np.int32)
+    remap[live] = np.arange(len(live), dtype=np.int32)
+    one = pool0.copy()
+    ref = oracle.decode_packed(p.q, p.k, p.v, p.g, p.beta, one, remap, p.cu_seqlens, p.scale)
+    split = pool0.copy()
+    out = np.full_like(ref, np.nan)
+    cu = p.cu_seqlens.astype(np.int32)
+    for a, b in bench.request_chunks(p.N, 4):
+        oracle.decode_packed(p.q, p.k, p.v, p.g, p.beta, split, np.ascontiguousarray(remap[a:b]),
+                             np.ascontiguousarray(cu[a:b + 1]), p.scale, out=out)
+    assert np.array_equal(split, one)
+    assert np.array_equal(np.isnan(out), np.isnan(ref)) and np.array_equal(out[~np.isnan(ref)], ref[~np.isnan(ref)])

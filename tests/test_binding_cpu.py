@@ -1,10 +1,17 @@
 """The Python binding's argument marshalling (no library call, no device):
-which gate-input forms it accepts, the shapes and dtypes it insists on, and
-the strides and pointers it writes into kda_decode_args."""
+which gate-input forms it accepts, the shapes and dtypes it insists on, the
+strides and pointers it writes into kda_decode_args, and that host tensors
+are refused before any library call.
+
+The marshalling checks run the binding's marshaller with the device every
+tensor must be on set to the CPU (the library calls always pass torch's
+current GPU), so that they need no GPU."""
 import pytest
 import torch
 
 import linear_attention_recurrent_decode_amd as kda
+
+CPU = torch.device("cpu")
 
 T, H, HV, K, V, SLOTS = 3, 2, 4, 128, 128, 5
 
@@ -22,9 +29,44 @@ def _tensors():
 
 def _args(t, **kw):
     base = dict(q=t["q"], k=t["k"], v=t["v"], g=t["g"], beta=t["beta"], state=t["state"], slot_idx=t["slot_idx"],
-                out=t["out"], scale=0.088)
+                out=t["out"], scale=0.088, gate=None, norm_weight=None, eps=1e-6, device_status=None,
+                inter_state=None, raw_gate=None, raw_beta=None, A_log=None, dt_bias=None)
     base.update(kw)
-    return kda.decode_args(**base)
+    return kda._marshal_args(**base, device=CPU)
+
+
+@pytest.fixture
+def no_library(monkeypatch):
+    """Any attempt to load or call libkda.so fails the test."""
+    def refuse():
+        raise AssertionError("the library was reached")
+    monkeypatch.setattr(kda, "library", refuse)
+
+
+def test_host_tensors_are_refused_before_any_library_call(no_library):
+    t = _tensors()
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kda.kda_decode_step(t["q"], t["k"], t["v"], t["g"], t["beta"], t["state"], t["slot_idx"], t["out"],
+                            T=1, scale=0.088)
+    cu = torch.arange(T + 1, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kda.kda_decode_packed(t["q"], t["k"], t["v"], t["g"], t["beta"], t["state"], t["slot_idx"], cu, t["out"],
+                              scale=0.088)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kda.decode_args(t["q"], t["k"], t["v"], t["g"], t["beta"], t["state"], t["slot_idx"], t["out"], 0.088)
+    x = torch.zeros((2, V), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kda.kda_gated_rmsnorm(x, x.clone(), torch.ones(V, dtype=torch.bfloat16), x.clone())
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "state", "slot_idx", "out"])
+def test_each_tensor_must_be_on_the_call_device(name):
+    """One tensor on another device than the call's (here a meta tensor in a
+    call whose device is the CPU) is refused, whichever it is."""
+    t = _tensors()
+    t[name] = t[name].to("meta")
+    with pytest.raises(ValueError, match=f"{name} is on meta"):
+        _args(t)
 
 
 def test_activated_form():

@@ -8,9 +8,20 @@ import torch
 import kda_inputs as ki
 import linear_attention_recurrent_decode_amd as kda
 import oracle
-from kda_harness import (DEV, bf16_tensor, bf16_to_f64, compare, f32_tensor, parity, run_gpu, run_oracle, upload)
+from kda_harness import (DEV, assert_guards, bf16_tensor, bf16_to_f64, compare, f32_tensor, guarded_full, parity,
+                         run_gpu, run_oracle, upload)
 
 pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def guards_intact():
+    """After every test: no buffer any call of the test wrote through (pool,
+    outputs, per-token states) was written past either end."""
+    import kda_harness
+    kda_harness.CREATED.clear()
+    yield
+    kda_harness.check_all_guards()
 
 
 def _log(name, rep):
@@ -179,9 +190,10 @@ def test_intermediate_states(name, dtype):
         p = ki.workload(name)
     d = upload(p, state_dtype=dtype)
     sentinel = 1232.0                         # exact in fp32 and bf16
-    inter = torch.full((p.tokens, p.HV, p.K, p.V), sentinel, dtype=dtype, device=DEV)
+    inter = guarded_full(d, (p.tokens, p.HV, p.K, p.V), sentinel, dtype)
     run_gpu(d, inter_state=inter)
     torch.cuda.synchronize()
+    assert_guards(d)
     ref_inter = np.full((p.tokens, p.HV, p.K, p.V), np.nan)
     ref_out, ref_state = run_oracle(p, state_bf16=dtype == torch.bfloat16, inter_state=ref_inter)
     compare(d, ref_out, ref_state)
@@ -280,9 +292,10 @@ def test_fused_gate_intermediate_states():
     p = ki.make_problem("ps", 62, N=40, H=4, HV=4, K=128, V=128, num_slots=64, T=None, t_max=6, n_pad=5,
                         raw_gates=True)
     d = upload(p)
-    inter = torch.full((p.tokens, p.HV, p.K, p.V), 1232.0, device=DEV)
+    inter = guarded_full(d, (p.tokens, p.HV, p.K, p.V), 1232.0, torch.float32)
     run_gpu(d, inter_state=inter)
     torch.cuda.synchronize()
+    assert_guards(d)
     ref_inter = np.full((p.tokens, p.HV, p.K, p.V), np.nan)
     ref_out, ref_state = run_oracle(p, inter_state=ref_inter)
     compare(d, ref_out, ref_state)
@@ -428,9 +441,10 @@ def test_random_configurations(i):
     before = d.state.clone()
     inter = None
     if c["inter"]:
-        inter = torch.full((p.tokens, p.HV, p.K, p.V), 1232.0, dtype=dtype, device=DEV)
+        inter = guarded_full(d, (p.tokens, p.HV, p.K, p.V), 1232.0, dtype)
     run_gpu(d, flags=flags, inter_state=inter)
     torch.cuda.synchronize()
+    assert_guards(d)
     ref_inter = np.full((p.tokens, p.HV, p.K, p.V), np.nan) if c["inter"] else None
     ref_out, ref_state = run_oracle(p, state_bf16=c["bf16"], inter_state=ref_inter)
     compare(d, ref_out, ref_state)
@@ -592,6 +606,30 @@ def test_validate_inside_a_graph():
 
 
 # ------------------------------------------------------- edge cases
+def test_host_tensors_in_a_gpu_call_are_refused(monkeypatch):
+    """A host tensor among device tensors is refused by the binding before
+    the library is reached (its address would be a host address on the
+    GPU), and nothing on the device changes."""
+    p = ki.make_problem("host", 12, N=2, H=2, HV=2, K=128, V=128, num_slots=4, T=1)
+    d = upload(p)
+    before = d.state.clone()
+
+    def refuse():
+        raise AssertionError("the library was reached")
+
+    monkeypatch.setattr(kda, "library", refuse)
+    with pytest.raises(ValueError, match="slot_idx is on cpu"):
+        kda.kda_decode_step(d.q, d.k, d.v, d.g, d.beta, d.state, d.slot_idx.cpu(), d.out, T=1, scale=p.scale)
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        kda.kda_decode_step(d.q.cpu(), d.k, d.v, d.g, d.beta, d.state, d.slot_idx, d.out, T=1, scale=p.scale)
+    with pytest.raises(ValueError, match="cu_seqlens is on cpu"):
+        kda.kda_decode_packed(d.q, d.k, d.v, d.g, d.beta, d.state, d.slot_idx, d.cu_seqlens.cpu(), d.out,
+                              scale=p.scale)
+    monkeypatch.undo()
+    torch.cuda.synchronize()
+    assert torch.equal(d.state, before)
+
+
 def test_all_requests_padding():
     p = ki.make_problem("allpad", 5, N=4, H=2, HV=2, K=128, V=128, num_slots=6, T=None, n_pad=4)
     parity(p)
@@ -649,13 +687,16 @@ def test_reset_and_identity_on_gpu():
     compare(d, ref_out, ref_state)
 
 
-@pytest.mark.parametrize("N,T", [(4, 2), (25, 4)])
-def test_large_slot_offsets(N, T):
+@pytest.mark.parametrize("N,T,raw", [(4, 2, False), (25, 4, False), (4, 1, True)])
+def test_large_slot_offsets(N, T, raw):
     """Slots whose element offset exceeds 2^31 (pool > 8 GiB at HV = 8): 32
-    tiles (split-key waves, tile first) and 200 tiles (four 16-column waves,
-    the first token's inputs before the tile)."""
+    tiles at T = 2 and 200 tiles at T = 4 (the multi-token kernels), and 32
+    one-token tiles with the fused gate (two 16-column waves that store the
+    state straight from the lanes)."""
     HV, slots = 8, 16400
-    p = ki.make_problem("big", 10, N=N, H=8, HV=HV, K=128, V=128, num_slots=slots, T=T)
+    p = ki.make_problem("big", 10, N=N, H=8, HV=HV, K=128, V=128, num_slots=slots, T=T, raw_gates=raw)
+    print(f"[parity] large offsets N={N} T={T} raw={raw}: layout "
+          f"{kda.kda_decode_plan(N * HV, T, raw_gate=raw, layout=True)}", flush=True)
     p.slot_idx[:] = ([16399, 16384, 3, 16390] + list(range(16360, 16381)))[:N]
     d = upload(p)
     run_gpu(d)
@@ -745,9 +786,10 @@ def test_quarter_waves_match_wide_waves_bitwise(case):
     results = []
     for flags in (0, kda.KDA_FLAG_VTILE(32), kda.KDA_FLAG_VTILE(64), kda.KDA_FLAG_VTILE(128)):
         d = _fresh(p)
-        inter = torch.full((p.tokens, p.HV, p.K, p.V), 1232.0, device=DEV)
+        inter = guarded_full(d, (p.tokens, p.HV, p.K, p.V), 1232.0, torch.float32)
         run_gpu(d, flags=flags, inter_state=inter)
         torch.cuda.synchronize()
+        assert_guards(d)
         if flags == 0:
             ref_inter = np.full((p.tokens, p.HV, p.K, p.V), np.nan)
             ref_out, ref_state = run_oracle(p, inter_state=ref_inter)
@@ -780,9 +822,10 @@ def test_quarter_waves_bf16_pool_match_wide_waves_bitwise(case):
     results = []
     for flags in (0, kda.KDA_FLAG_VTILE(32), kda.KDA_FLAG_VTILE(128)):
         d = upload(p, background_seed=1234, state_dtype=torch.bfloat16)
-        inter = torch.full((p.tokens, p.HV, p.K, p.V), 1232.0, dtype=torch.bfloat16, device=DEV)
+        inter = guarded_full(d, (p.tokens, p.HV, p.K, p.V), 1232.0, torch.bfloat16)
         run_gpu(d, flags=flags, inter_state=inter)
         torch.cuda.synchronize()
+        assert_guards(d)
         if flags == 0:
             _log(f"quarter waves bf16 {case}", compare(d, *run_oracle(p, state_bf16=True)))
         results.append((d.out.view(torch.int16).clone(), d.state.view(torch.int16).clone(),
@@ -814,9 +857,10 @@ def test_quarter_waves_norm_match_wide_waves_bitwise(case):
     results = []
     for flags in (0, kda.KDA_FLAG_VTILE(128)):
         d = upload(p, background_seed=1234, state_dtype=dtype)
-        inter = torch.full((p.tokens, p.HV, p.K, p.V), 1232.0, dtype=dtype, device=DEV)
+        inter = guarded_full(d, (p.tokens, p.HV, p.K, p.V), 1232.0, dtype)
         run_gpu(d, flags=flags, inter_state=inter)
         torch.cuda.synchronize()
+        assert_guards(d)
         if flags == 0:
             _log(f"quarter waves norm {case}", compare(d, *run_oracle(p, state_bf16=dtype == torch.bfloat16)))
         results.append((d.out.view(torch.int16).clone(), d.state.view(torch.int16).clone(),
@@ -838,9 +882,10 @@ def test_eight_quarter_waves_match_wide_waves_bitwise(case):
     results = []
     for flags in (0, kda.KDA_FLAG_VTILE(128)):
         d = _fresh(p)
-        inter = torch.full((p.tokens, p.HV, p.K, p.V), 1232.0, device=DEV)
+        inter = guarded_full(d, (p.tokens, p.HV, p.K, p.V), 1232.0, torch.float32)
         run_gpu(d, flags=flags, inter_state=inter)
         torch.cuda.synchronize()
+        assert_guards(d)
         if flags == 0:
             _log(f"eight quarter waves {case}", compare(d, *run_oracle(p)))
         results.append((d.out.view(torch.int16).clone(), d.state.clone(), inter))
