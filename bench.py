@@ -16,18 +16,21 @@ traffic earlier.  Every call is still exactly the workload: N requests on N
 distinct slots of a pool of num_slots slots.
 
 Protocol (after vLLM PR 57585, "Microbenchmark and earlier serving limits":
-graph replay, cold caches, untimed warmup, interleaved blocks; and FlashInfer
-PR 4562, description: a duration-calibrated graph warmup):
+cold caches, untimed warmup, interleaved blocks; and FlashInfer PR 4562,
+description: a duration-calibrated graph warmup):
   1. --warmup eager calls, then graph replays of one full slot rotation until
      at least --warmup-ms of wall time have passed (untimed);
-  2. --blocks timed blocks of exactly --steps calls each.  Each block is one
-     HIP graph over the next --steps calls of the rotation, replayed once
-     untimed (so that the timed replay is not the graph's first), then a
-     1 GiB read sweep that evicts the caches, then a spin kernel that keeps
-     the GPU busy while the host enqueues the two events and the replay; the
-     block's time is the interval between HIP events recorded on the replay
-     stream around it.  ``value`` is the median block's us per call, with
-     the p10 and p90 of the blocks beside it.
+  2. --blocks timed blocks of exactly --steps calls each.  A block's calls
+     are enqueued on one stream right behind an untimed HIP graph replay of
+     the calls before them in the rotation (at least a full rotation, and
+     long enough that the host has enqueued the whole block while the GPU
+     still runs the replay), so the GPU runs the block's calls back to back
+     with cold caches; the block's time is the interval between HIP events
+     recorded on that stream around its calls.  ``value`` is the median
+     block's us per call, with the p10 and p90 of the blocks beside it.
+     (Timing one graph replay of the block instead adds the fixed cost of
+     starting a replay, about 12 us on this ROCm, to the block: reported
+     beside, as graph_replay_us_per_call.)
 Then, as extra keys: a plain device copy of the call's state bytes (read and
 write, the same rotation and protocol), the host cost of one enqueue through
 the C ABI, the cache-resident time (--warm), and the CPU oracle on all host
@@ -56,7 +59,9 @@ if ROOT not in sys.path:
 
 METRIC = "KDA decode µs/call + state HBM GB/s (% of peak), N32/T1/H8/K=V=128"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
-COLD_BYTES = 1 << 30            # state traffic between two uses of the same slots; also the flush sweep
+COLD_BYTES = 1 << 30            # state traffic between two uses of the same slots
+HOST_ENQUEUE_US_BOUND = 8.0     # above the host's time per enqueue (about 4 us from Python)
+GAP_MIN_US = 2000.0             # the untimed replay before a block keeps the GPU busy at least this long
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "linear_attention_recurrent_decode_amd", "csrc", "kda_decode.hip")
 # kda_decode_plan(..., layout=True) values
@@ -225,35 +230,14 @@ def cpu_baseline(p, pool_live: np.ndarray, budget_s: float, threads: int) -> dic
 
 
 class Timer:
-    """Graph-replay timing on one stream with the protocol of the module
-    docstring: upload replay, cache flush, busy preamble, events."""
+    """Timing of blocks of calls on one stream (protocol in the module
+    docstring): each timed block is enqueued behind an untimed graph replay
+    of the rotation, so that the GPU is still busy with the replay while the
+    host enqueues the block, and runs the block's calls back to back."""
 
-    def __init__(self, torch, stream, dev):
+    def __init__(self, torch, stream):
         self.torch = torch
         self.stream = stream
-        self.flush_buf = torch.ones(COLD_BYTES // 4, dtype=torch.float32, device=dev)
-        self.sink = torch.zeros((), dtype=torch.float32, device=dev)
-        self.spin_cycles = self._calibrate_spin()
-
-    def _calibrate_spin(self) -> int:
-        """Cycles of torch's spin kernel that take about 0.3 ms here."""
-        torch = self.torch
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        cycles = 200_000
-        with torch.cuda.stream(self.stream):
-            torch.cuda._sleep(cycles)
-            e0.record(self.stream)
-            torch.cuda._sleep(cycles)
-            e1.record(self.stream)
-        torch.cuda.synchronize()
-        ms = max(e0.elapsed_time(e1), 1e-3)
-        return int(min(max(cycles * 0.3 / ms, 10_000), 50_000_000))
-
-    def flush(self):
-        """Read 1 GiB through the caches (MI355X: 256 MiB memory-side cache,
-        8 x 4 MiB L2), so that the next block starts cold."""
-        with self.torch.cuda.stream(self.stream):
-            self.torch.sum(self.flush_buf, dim=0, out=self.sink)
 
     def capture(self, body):
         torch = self.torch
@@ -265,21 +249,26 @@ class Timer:
         torch.cuda.synchronize()
         return graph
 
-    def time_graph(self, graph, calls: int, cold: bool = True) -> float:
-        """us per call of one timed replay of ``graph`` (``calls`` calls)."""
+    def time_block(self, gap_graph, enqueue, calls: int) -> float:
+        """us per call of ``calls`` calls that ``enqueue()`` issues on the
+        stream right after an untimed replay of ``gap_graph``."""
         torch = self.torch
-        graph.replay()                     # not the graph's first replay when timed
-        if cold:
-            self.flush()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         with torch.cuda.stream(self.stream):
-            torch.cuda._sleep(self.spin_cycles)   # the GPU is busy while the host enqueues what follows
+            gap_graph.replay()
             e0.record(self.stream)
-            graph.replay()
+            enqueue()
             e1.record(self.stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1000.0 / calls
+
+    def time_replay(self, gap_graph, graph, calls: int) -> float:
+        """us per call of one replay of ``graph`` (after an untimed replay of
+        it and of ``gap_graph``), events around the replay."""
+        torch = self.torch
+        graph.replay()
+        return self.time_block(gap_graph, graph.replay, calls)
 
 
 def main():
@@ -386,7 +375,7 @@ def main():
 
     stream = torch.cuda.Stream()
     sh = stream.cuda_stream
-    timer = Timer(torch, stream, dev)
+    timer = Timer(torch, stream)
 
     # 1. warmup: eager calls, then replays of one full rotation for >= warmup_ms
     pos = 0
@@ -408,33 +397,60 @@ def main():
     del g_warm
     log(f"[bench] calibrated warmup: {warm_calls} calls in {warm_ms:.1f} ms")
 
-    # 2. timed blocks, each its own graph over the next `steps` calls of the rotation
+    # 2. timed blocks: `steps` calls each, enqueued behind an untimed replay of
+    # the `gap` calls before them in the rotation (at least one full rotation,
+    # so the block's slots are cold, and long enough that the host has
+    # enqueued the whole block before the GPU finishes the replay)
+    est_us = max(0.25, warm_ms * 1000.0 / warm_calls)
+    gap = max(len(combos), math.ceil(args.steps * HOST_ENQUEUE_US_BOUND / est_us),
+              math.ceil(GAP_MIN_US / est_us))
     arms = {"A": 0}
     if args.flags_b is not None:
         arms["B"] = int(args.flags_b)
     per_arm = {a: [] for a in arms}
+
+    def block(extra_flags, which=None):
+        nonlocal pos
+        first = pos
+        gap_graph = timer.capture(lambda: [launch(first + i, sh, which=which) for i in range(gap)])
+        t0_call = first + gap
+        pos = t0_call + args.steps
+        us = timer.time_block(gap_graph, lambda: [launch(t0_call + i, sh, extra_flags, which)
+                                                  for i in range(args.steps)], args.steps)
+        del gap_graph
+        return us
+
     for arm in block_order(args.blocks, len(arms) > 1):
-        start = pos
-        graph = timer.capture(lambda: [launch(start + i, sh, arms[arm]) for i in range(args.steps)])
-        pos += args.steps
-        us = timer.time_graph(graph, args.steps)
-        per_arm[arm].append(us)
-        del graph
+        per_arm[arm].append(block(arms[arm]))
     blocks_a = per_arm["A"]
     sp = spread(blocks_a)
     us_per_call = sp["median"]
-    log(f"[bench] {len(blocks_a)} blocks of {args.steps} calls: median {us_per_call:.3f} us/call "
+    log(f"[bench] {len(blocks_a)} blocks of {args.steps} calls (gap {gap}): median {us_per_call:.3f} us/call "
         f"(p10 {sp['p10']:.3f}, p90 {sp['p90']:.3f}); blocks {[round(x, 3) for x in blocks_a]}")
 
     extras = {}
     if args.warm:
         hot = [combos[0]]
-        graph = timer.capture(lambda: [launch(i, sh, which=hot) for i in range(args.steps)])
-        extras["cache_resident_us_per_call"] = round(timer.time_graph(graph, args.steps, cold=False), 4)
-        del graph
+        extras["cache_resident_us_per_call"] = round(block(0, which=hot), 4)
         log(f"[bench] cache-resident: {extras['cache_resident_us_per_call']:.3f} us/call")
 
     if not args.no_extras:
+        # the same blocks as one graph replay each (events around the replay)
+        replay = []
+        for _ in range(3):
+            first = pos
+            gap_graph = timer.capture(lambda: [launch(first + i, sh) for i in range(gap)])
+            t0_call = first + gap
+            graph = timer.capture(lambda: [launch(t0_call + i, sh) for i in range(args.steps)])
+            pos = t0_call + args.steps
+            replay.append(timer.time_replay(gap_graph, graph, args.steps))
+            del gap_graph, graph
+        extras["graph_replay_us_per_call"] = {
+            "median": round(float(np.median(replay)), 4), "blocks": [round(x, 4) for x in replay],
+            "what": "the same blocks of calls captured as one HIP graph each, events around one replay "
+                    "(after an untimed one): adds the fixed cost of starting a replay to the block"}
+        log(f"[bench] graph replay: {extras['graph_replay_us_per_call']['median']:.3f} us/call")
+
         # a plain device copy of the call's state bytes (half read, half written), cold by rotation
         half = max(4, per_call_read // 4) * 4
         n_chunks = max(2, math.ceil(COLD_BYTES / half))
@@ -447,21 +463,23 @@ def main():
                 j = i % n_chunks
                 dst[j * ch:(j + 1) * ch].copy_(src[j * ch:(j + 1) * ch])
 
+        copy_gap = max(n_chunks, math.ceil(args.steps * 4 * HOST_ENQUEUE_US_BOUND / est_us))
         copy_blocks = []
         cpos = 0
         for _ in range(3):
             c0 = cpos
-            graph = timer.capture(lambda: copies(c0, args.steps))
-            cpos += args.steps
-            copy_blocks.append(timer.time_graph(graph, args.steps))
-            del graph
+            gap_graph = timer.capture(lambda: copies(c0, copy_gap))
+            cpos += copy_gap + args.steps
+            with torch.cuda.stream(stream):
+                copy_blocks.append(timer.time_block(gap_graph, lambda: copies(c0 + copy_gap, args.steps), args.steps))
+            del gap_graph
         copy_us = float(np.median(copy_blocks))
         extras["copy_reference"] = {
             "us_per_call": round(copy_us, 4), "GBps": round(2 * half / (copy_us * 1e-6) / 1e9, 1),
             "bytes_per_call": 2 * half,
             "what": "torch device copy of the call's state bytes (read + write), one copy per call, the same "
-                    "cold rotation, graph replay and timing protocol: the achievable streaming rate at this size "
-                    "with the same per-launch cost"}
+                    "cold rotation and timing protocol: the achievable streaming rate at this size with the "
+                    "same per-launch cost"}
         del src, dst
         log(f"[bench] copy reference: {copy_us:.3f} us/call, {extras['copy_reference']['GBps']} GB/s")
 
