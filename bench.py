@@ -22,9 +22,9 @@ description: a duration-calibrated graph warmup):
      at least --warmup-ms of wall time have passed (untimed);
   2. --blocks timed blocks of exactly --steps calls each.  A block's calls
      are enqueued on one stream right behind an untimed HIP graph replay of
-     the calls before them in the rotation (at least a full rotation, and
-     long enough that the host has enqueued the whole block while the GPU
-     still runs the replay), so the GPU runs the block's calls back to back
+     the calls before them in the rotation (at least a full rotation and
+     2 ms of GPU time, and long enough that the host has enqueued the whole
+     block while the GPU still runs the replay), so the GPU runs the block's calls back to back
      with cold caches; the block's time is the interval between HIP events
      recorded on that stream around its calls.  ``value`` is the median
      block's us per call, with the p10 and p90 of the blocks beside it.
