@@ -65,8 +65,7 @@ GAP_MIN_US = 2000.0             # the untimed replay before a block keeps the GP
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "linear_attention_recurrent_decode_amd", "csrc", "kda_decode.hip")
 # kda_decode_plan(..., layout=True) values
-LAYOUT_NAMES = {0: "32-column waves", 1: "16-column waves", 2: "16-column waves, split key rows",
-                3: "16-column waves, tokens chunked"}
+LAYOUT_NAMES = {0: "32-column waves", 1: "16-column waves", 2: "16-column waves, split key rows"}
 
 
 def log(*a):

@@ -89,6 +89,36 @@ typedef enum kda_status {
 #define KDA_FLAG_VTILE_MASK (3u << KDA_FLAG_VTILE_SHIFT)
 #define KDA_FLAG_VTILE(code) (((uint32_t)(code) & 3u) << KDA_FLAG_VTILE_SHIFT)
 
+/* flags: bits 12..15 force the kernel (lane layout and workgroup) instead
+ * of the library's choice, and bits 16..17 its load order; for tests and
+ * for measuring one choice against another.  Kernel codes:
+ *   KDA_KERNEL_WIDE        32-column waves (the width from KDA_FLAG_VTILE,
+ *                          else the library's)
+ *   KDA_KERNEL_QUARTER2/4/8  16-column waves, 2, 4 or 8 per workgroup
+ *   KDA_KERNEL_SPLIT       split-key 16-column waves (step calls only)
+ * Order codes (16-column and split-key waves): KDA_ORDER_TILE_FIRST (the
+ * state tile's loads first) or KDA_ORDER_INPUTS_FIRST (the first token's
+ * inputs first); 0 = the library's.  A combination no kernel provides (the
+ * norm epilogue outside KDA_KERNEL_WIDE at 128 columns and
+ * KDA_KERNEL_QUARTER8, a packed call on KDA_KERNEL_SPLIT, two 16-column
+ * waves outside one-token fp32 calls with the fused gate, inputs first with
+ * a bf16 pool or one token, an order for the 32-column kernel) is
+ * KDA_ERR_UNSUPPORTED.  Every kernel, width and order gives bitwise the same
+ * results. */
+#define KDA_FLAG_KERNEL_SHIFT 12u
+#define KDA_FLAG_KERNEL_MASK (15u << KDA_FLAG_KERNEL_SHIFT)
+#define KDA_FLAG_KERNEL(code) (((uint32_t)(code) & 15u) << KDA_FLAG_KERNEL_SHIFT)
+#define KDA_KERNEL_WIDE 1
+#define KDA_KERNEL_QUARTER2 2
+#define KDA_KERNEL_QUARTER4 3
+#define KDA_KERNEL_QUARTER8 4
+#define KDA_KERNEL_SPLIT 5
+#define KDA_FLAG_ORDER_SHIFT 16u
+#define KDA_FLAG_ORDER_MASK (3u << KDA_FLAG_ORDER_SHIFT)
+#define KDA_FLAG_ORDER(code) (((uint32_t)(code) & 3u) << KDA_FLAG_ORDER_SHIFT)
+#define KDA_ORDER_TILE_FIRST 1
+#define KDA_ORDER_INPUTS_FIRST 2
+
 /*
  * One decode call.  Token t of the call is row t of every per-token tensor.
  *

@@ -23,8 +23,11 @@ __all__ = [
     "kda_decode_step", "kda_decode_packed", "kda_gated_rmsnorm",
     "kda_decode_plan", "KDA_PLAN_NORM", "KDA_PLAN_STATE_BF16", "KDA_PLAN_PACKED", "KDA_PLAN_LAYOUT",
     "KDA_PLAN_RAW_GATE",
-    "KDA_LAYOUT_WIDE", "KDA_LAYOUT_QUARTER", "KDA_LAYOUT_SPLIT", "kda_status_string", "decode_args",
-    "KDA_FLAG_VTILE", "KDA_FLAG_STATE_BF16", "KDA_FLAG_VALIDATE", "KDA_DEVICE_STATUS",
+    "KDA_LAYOUT_WIDE", "KDA_LAYOUT_QUARTER", "KDA_LAYOUT_SPLIT", "kda_status_string",
+    "decode_args", "KDA_FLAG_VTILE", "KDA_FLAG_KERNEL", "KDA_FLAG_ORDER", "KDA_FLAG_STATE_BF16",
+    "KDA_FLAG_VALIDATE", "KDA_DEVICE_STATUS",
+    "KDA_KERNEL_WIDE", "KDA_KERNEL_QUARTER2", "KDA_KERNEL_QUARTER4", "KDA_KERNEL_QUARTER8", "KDA_KERNEL_SPLIT",
+    "KDA_ORDER_TILE_FIRST", "KDA_ORDER_INPUTS_FIRST",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -39,12 +42,27 @@ KDA_FLAG_VALIDATE = 1 << 1
 KDA_DEVICE_STATUS = {0: "KDA_DEVICE_OK", 1: "KDA_DEVICE_ERR_SLOT_RANGE", 2: "KDA_DEVICE_ERR_SLOT_DUP",
                      3: "KDA_DEVICE_ERR_CU_SEQLENS"}
 KDA_FLAG_VTILE_SHIFT = 8
+KDA_FLAG_KERNEL_SHIFT = 12
+KDA_FLAG_ORDER_SHIFT = 16
+KDA_KERNEL_WIDE, KDA_KERNEL_QUARTER2, KDA_KERNEL_QUARTER4, KDA_KERNEL_QUARTER8 = 1, 2, 3, 4
+KDA_KERNEL_SPLIT = 5
+KDA_ORDER_TILE_FIRST, KDA_ORDER_INPUTS_FIRST = 1, 2
 
 
 def KDA_FLAG_VTILE(width: int) -> int:
     """Flag bits forcing a value-tile width of 32, 64 or 128 columns."""
     code = {32: 1, 64: 2, 128: 3}[width]
     return code << KDA_FLAG_VTILE_SHIFT
+
+
+def KDA_FLAG_KERNEL(code: int) -> int:
+    """Flag bits forcing a kernel (a KDA_KERNEL_* code)."""
+    return (int(code) & 15) << KDA_FLAG_KERNEL_SHIFT
+
+
+def KDA_FLAG_ORDER(code: int) -> int:
+    """Flag bits forcing a load order (KDA_ORDER_TILE_FIRST or KDA_ORDER_INPUTS_FIRST)."""
+    return (int(code) & 3) << KDA_FLAG_ORDER_SHIFT
 
 
 class KdaError(RuntimeError):
@@ -82,14 +100,9 @@ class KdaDecodeArgs(ctypes.Structure):
 _lib = None
 
 
-def library() -> ctypes.CDLL:
-    """Load libkda.so (built in place by ``build.py``); raise if it is missing."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(library_path):
-        raise RuntimeError(f"{library_path} is not built: run linear_attention_recurrent_decode_amd.build.build()")
-    lib = ctypes.CDLL(library_path)
+def _open(path: str) -> ctypes.CDLL:
+    """Load a build of the C ABI from ``path`` and declare its signatures."""
+    lib = ctypes.CDLL(path)
     P = ctypes.POINTER(KdaDecodeArgs)
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [P, ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p]
@@ -101,8 +114,18 @@ def library() -> ctypes.CDLL:
     lib.kda_decode_plan.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [ctypes.c_int]
-    _lib = lib
     return lib
+
+
+def library() -> ctypes.CDLL:
+    """Load libkda.so (built in place by ``build.py``); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise RuntimeError(f"{library_path} is not built: run linear_attention_recurrent_decode_amd.build.build()")
+    _lib = _open(library_path)
+    return _lib
 
 
 def kda_status_string(status: int) -> str:

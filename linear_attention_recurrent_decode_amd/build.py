@@ -1,4 +1,6 @@
-"""Build libkda.so (gfx950) in place with hipcc.
+"""Build libkda.so (gfx950) in place: the kernel layer (csrc/kda_decode.hip)
+with hipcc, the host layer (csrc/kda_host.cpp: C ABI, validation, launch
+plan) with the host C++ compiler, linked into one shared library.
 
     python -m linear_attention_recurrent_decode_amd.build
 """
@@ -8,10 +10,13 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "kda_decode.hip")
+CSRC = os.path.join(PKG, "csrc")
+SRC = os.path.join(CSRC, "kda_decode.hip")
+HOST_SRC = os.path.join(CSRC, "kda_host.cpp")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkda.so")
 
@@ -20,7 +25,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     # every fused multiply-add in the kernels is an explicit fmaf: no implicit
     # contraction, so inlined copies of the same code round the same way
@@ -32,6 +36,9 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
+# the host layer: plain C++17
+HOST_CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
+
 
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -40,19 +47,36 @@ def hipcc() -> str:
     return path
 
 
-def build(verbose: bool = False) -> str:
-    """Compile libkda.so next to this file (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-o", tmp, SRC]
+def host_cxx() -> str:
+    path = shutil.which("g++") or shutil.which("c++")
+    if not path:
+        raise RuntimeError("no host C++ compiler")
+    return path
+
+
+def _run(cmd, what):
     res = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 feature and says so: harmless
     noise = "'-packed-fp32-ops' is not a recognized feature"
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+        raise RuntimeError(f"{what} failed:\n" + "\n".join(msgs))
+    return msgs
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libkda.so next to this file (always recompiles)."""
+    with tempfile.TemporaryDirectory(prefix="kda_build_") as tmp:
+        host_o = os.path.join(tmp, "kda_host.o")
+        dev_o = os.path.join(tmp, "kda_decode.o")
+        msgs = _run([host_cxx(), *HOST_CXX_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", HOST_SRC, "-o", host_o],
+                    "host layer")
+        msgs += _run([hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", SRC, "-o", dev_o], "kernel layer")
+        tmp_lib = LIB + ".tmp"
+        msgs += _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp_lib, dev_o, host_o], "link")
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp_lib, LIB)
     return LIB
 
 

@@ -50,7 +50,7 @@
 #include <string.h>
 #include <type_traits>
 
-#include "kda.h"
+#include "kda_launch.h"
 
 namespace {
 
@@ -1526,7 +1526,10 @@ __global__ __launch_bounds__(256) void kda_gated_rmsnorm_kernel(const uint16_t *
     }
 }
 
-// ------------------------------------------------------------------ host
+// ------------------------------------------------------------------ launches
+//
+// The kernel layer's side of kda_launch.h: the device check, and the
+// launch of the kernel instance a call's plan names.
 
 std::atomic<int> g_device_kind[MAX_DEVICES];   // 0 unknown, 1 gfx950, 2 other
 
@@ -1562,7 +1565,181 @@ bool raise_q8_lds_limit()
     return true;
 }
 
-kda_status check_device()
+DecodeParams make_params(const kda_internal::DecodeCall &c)
+{
+    const kda_decode_args *a = c.args;
+    DecodeParams p;
+    p.q = static_cast<const uint16_t *>(a->q);
+    p.k = static_cast<const uint16_t *>(a->k);
+    p.v = static_cast<const uint16_t *>(a->v);
+    p.g = a->g;
+    p.beta = a->beta;
+    p.raw_gate = static_cast<const uint16_t *>(a->raw_gate);
+    p.raw_beta = static_cast<const uint16_t *>(a->raw_beta);
+    p.A_log = a->A_log;
+    p.dt_bias = a->dt_bias;
+    p.q_stride = a->q_stride;
+    p.k_stride = a->k_stride;
+    p.v_stride = a->v_stride;
+    p.g_stride = a->g_stride;
+    p.beta_stride = a->beta_stride;
+    p.raw_gate_stride = a->raw_gate_stride;
+    p.raw_beta_stride = a->raw_beta_stride;
+    p.HV = a->HV;
+    p.T = c.T;
+    p.qk_magic = c.qk_magic;
+    p.qk_magic_hi = c.qk_magic_hi;
+    p.scale = a->scale;
+    p.eps = a->norm_eps;
+    p.state = a->state;
+    p.slot_idx = a->slot_idx;
+    p.cu_seqlens = c.cu_seqlens;
+    p.out = static_cast<uint16_t *>(a->out);
+    p.gate = static_cast<const uint16_t *>(a->gate);
+    p.norm_weight = static_cast<const uint16_t *>(a->norm_weight);
+    p.out_stride = a->out_stride;
+    p.gate_stride = a->gate_stride;
+    p.num_slots = a->num_slots;
+    p.slot_stride = a->slot_stride;
+    p.status = c.validate ? a->device_status : nullptr;
+    p.inter_state = a->inter_state;
+    p.inter_stride = a->inter_stride;
+    return p;
+}
+
+// One launch of `kernel` over `blocks` workgroups: the preloaded scalars,
+// then the parameter block.  The split-key kernel takes no cu_seqlens.
+template <bool WITH_CU>
+kda_status launch(const void *kernel, const DecodeParams &p, int64_t blocks, int threads, size_t lds,
+                  hipStream_t stream)
+{
+    if (blocks > 0x7FFFFFFF)
+        return KDA_ERR_SHAPE;
+    const int32_t *slot_idx = p.slot_idx, *cu_seqlens = p.cu_seqlens;
+    void *state = p.state;
+    int64_t slot_stride = p.slot_stride, num_slots = p.num_slots;
+    int32_t HV = p.HV, T = p.T;
+    const int32_t *status = p.status;
+    DecodeParams params = p;
+    void *with_cu[] = {&slot_idx, &cu_seqlens, &state, &slot_stride, &num_slots, &HV, &T, &status, &params};
+    void *without_cu[] = {&slot_idx, &state, &slot_stride, &num_slots, &HV, &T, &status, &params};
+    const hipError_t e = hipLaunchKernel(kernel, dim3((uint32_t)blocks), dim3(threads), WITH_CU ? with_cu : without_cu,
+                                         lds, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+// ---- the 32-column kernel: the body and the width of the plan
+template <int NW, bool NORM, bool BF16S, bool RAWG>
+kda_status launch_wide(const DecodeParams &p, int64_t units, int body, hipStream_t s)
+{
+    // the loop body serves only fp32 pools with activated gates (the plan's
+    // rule); it is not instantiated for the other forms
+    const void *fn = body == kda_internal::BODY_STAGED
+                         ? reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_STAGED, BF16S, RAWG>)
+                         : reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_PEELED, BF16S, RAWG>);
+    if constexpr (!BF16S && !RAWG) {
+        if (body == kda_internal::BODY_LOOP)
+            fn = reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_LOOP, BF16S, RAWG>);
+    }
+    return launch<true>(fn, p, units * (4 / NW), 64 * NW, 0, s);
+}
+
+template <bool RAWG, bool BF16S>
+kda_status dispatch_wide(const DecodeParams &p, int64_t units, const kda_internal::Plan &pl, bool norm,
+                         hipStream_t s)
+{
+    if (norm)
+        return pl.waves == 4 ? launch_wide<4, true, BF16S, RAWG>(p, units, pl.body, s) : KDA_ERR_UNSUPPORTED;
+    switch (pl.waves) {
+    case 1: return launch_wide<1, false, BF16S, RAWG>(p, units, pl.body, s);
+    case 2: return launch_wide<2, false, BF16S, RAWG>(p, units, pl.body, s);
+    default: return launch_wide<4, false, BF16S, RAWG>(p, units, pl.body, s);
+    }
+}
+
+// ---- 16-column waves: waves per workgroup, tokens loaded ahead (PF), order
+template <int NQ, int PF, bool NORM, bool RAWG, bool BF16S>
+kda_status launch_quarter(const DecodeParams &p, int64_t units, bool early, hipStream_t s)
+{
+    const void *fn = reinterpret_cast<const void *>(&kda_decode_q_kernel<NQ, PF, NORM, RAWG, BF16S, false>);
+    if constexpr (PF >= 2 && !BF16S) {
+        if (early)
+            fn = reinterpret_cast<const void *>(&kda_decode_q_kernel<NQ, PF, NORM, RAWG, BF16S, true>);
+    }
+    return launch<true>(fn, p, units * (8 / NQ), 64 * NQ, q_lds_bytes(NQ), s);
+}
+
+template <int NQ, bool NORM, bool RAWG, bool BF16S>
+kda_status dispatch_quarter_tokens(const DecodeParams &p, int64_t units, bool early, hipStream_t s)
+{
+    switch (p.cu_seqlens ? 4 : p.T) {
+    case 1: return launch_quarter<NQ, 1, NORM, RAWG, BF16S>(p, units, early, s);
+    case 2: return launch_quarter<NQ, 2, NORM, RAWG, BF16S>(p, units, early, s);
+    case 3: return launch_quarter<NQ, 3, NORM, RAWG, BF16S>(p, units, early, s);
+    default: return launch_quarter<NQ, 4, NORM, RAWG, BF16S>(p, units, early, s);
+    }
+}
+
+template <bool RAWG, bool BF16S>
+kda_status dispatch_quarter(const DecodeParams &p, int64_t units, const kda_internal::Plan &pl, bool norm,
+                            hipStream_t s)
+{
+    if (norm)
+        return pl.waves == 8 ? dispatch_quarter_tokens<8, true, RAWG, BF16S>(p, units, pl.early, s)
+                             : KDA_ERR_UNSUPPORTED;
+    if (pl.waves == 2) {
+        // two waves serve only one-token fp32 calls with the fused gate
+        if constexpr (RAWG && !BF16S) {
+            if (p.T == 1 && !p.cu_seqlens)
+                return launch_quarter<2, 1, false, true, false>(p, units, false, s);
+        }
+        return KDA_ERR_UNSUPPORTED;
+    }
+    return pl.waves == 8 ? dispatch_quarter_tokens<8, false, RAWG, BF16S>(p, units, pl.early, s)
+                         : dispatch_quarter_tokens<4, false, RAWG, BF16S>(p, units, pl.early, s);
+}
+
+// ---- split-key waves (step calls only)
+template <int PF, bool RAWG, bool BF16S>
+kda_status launch_split(const DecodeParams &p, int64_t units, bool early, hipStream_t s)
+{
+    const void *fn = reinterpret_cast<const void *>(&kda_decode_split_kernel<PF, RAWG, BF16S, false>);
+    if constexpr (PF >= 2 && !BF16S) {
+        if (early)
+            fn = reinterpret_cast<const void *>(&kda_decode_split_kernel<PF, RAWG, BF16S, true>);
+    }
+    return launch<false>(fn, p, units * (VD / S_COLS), 256, split_lds_bytes(), s);
+}
+
+template <bool RAWG, bool BF16S>
+kda_status dispatch_split(const DecodeParams &p, int64_t units, bool early, hipStream_t s)
+{
+    if (p.cu_seqlens)
+        return KDA_ERR_UNSUPPORTED;
+    switch (p.T) {
+    case 1: return launch_split<1, RAWG, BF16S>(p, units, false, s);
+    case 2: return launch_split<2, RAWG, BF16S>(p, units, early, s);
+    case 3: return launch_split<3, RAWG, BF16S>(p, units, early, s);
+    default: return launch_split<4, RAWG, BF16S>(p, units, early, s);
+    }
+}
+
+template <bool RAWG, bool BF16S>
+kda_status dispatch(const DecodeParams &p, int64_t units, const kda_internal::Plan &pl, bool norm, hipStream_t s)
+{
+    switch (pl.kernel) {
+    case kda_internal::KERNEL_WIDE: return dispatch_wide<RAWG, BF16S>(p, units, pl, norm, s);
+    case kda_internal::KERNEL_QUARTER: return dispatch_quarter<RAWG, BF16S>(p, units, pl, norm, s);
+    case kda_internal::KERNEL_SPLIT: return norm ? KDA_ERR_UNSUPPORTED : dispatch_split<RAWG, BF16S>(p, units, pl.early, s);
+    }
+    return KDA_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+namespace kda_internal {
+
+kda_status device_ready()
 {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES)
@@ -1586,509 +1763,34 @@ kda_status check_device()
     return kind == 1 ? KDA_OK : KDA_ERR_DEVICE;
 }
 
-struct ByteRange {
-    uintptr_t lo = 0, hi = 0;   // [lo, hi), empty when lo == hi
-};
-
-// Bounding byte range of a strided [rows][inner] tensor.
-ByteRange span(const void *ptr, int64_t rows, int64_t stride, int64_t inner, int64_t elem)
+kda_status launch_decode(const DecodeCall &c)
 {
-    ByteRange r;
-    if (!ptr || rows <= 0 || inner <= 0)
-        return r;
-    r.lo = reinterpret_cast<uintptr_t>(ptr);
-    r.hi = r.lo + (uintptr_t)(((rows - 1) * stride + inner) * elem);
-    return r;
-}
-
-bool overlaps(ByteRange a, ByteRange b)
-{
-    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
-}
-
-bool aligned(const void *p, uintptr_t bytes)
-{
-    return (reinterpret_cast<uintptr_t>(p) & (bytes - 1)) == 0;
-}
-
-int vtile_from_flags(uint32_t flags)
-{
-    switch ((flags & KDA_FLAG_VTILE_MASK) >> KDA_FLAG_VTILE_SHIFT) {
-    case 1: return 32;
-    case 2: return 64;
-    case 3: return 128;
-    default: return 0;
-    }
-}
-
-kda_status validate(const kda_decode_args *a, int64_t tokens, const int32_t *cu_seqlens, uint32_t flags)
-{
-    if (flags & ~(KDA_FLAG_VTILE_MASK | KDA_FLAG_STATE_BF16 | KDA_FLAG_VALIDATE))
-        return KDA_ERR_UNSUPPORTED;
-    const int64_t state_elem = (flags & KDA_FLAG_STATE_BF16) ? 2 : 4;
-    if (a->N < 0 || a->H < 1 || a->HV < 1 || a->HV > 65535 || a->HV % a->H != 0 || tokens < 0)
-        return KDA_ERR_SHAPE;
-    if (a->K != KD || a->V != VD)
-        return KDA_ERR_SHAPE;
-    // the gate inputs come in one form: activated (g, beta) or raw
-    const bool raw = a->raw_gate != nullptr;
-    if (raw ? (a->g || a->beta) : (a->raw_beta || a->A_log || a->dt_bias))
-        return KDA_ERR_UNSUPPORTED;
-    if (a->N == 0)
-        return KDA_OK;
-    // per-token tensors may be NULL only when the call holds no token rows
-    if (tokens > 0 && (!a->q || !a->k || !a->v || !a->out || (!raw && (!a->g || !a->beta))))
-        return KDA_ERR_NULL;
-    if (raw && (!a->raw_beta || !a->A_log || !a->dt_bias))
-        return KDA_ERR_NULL;
-    if (!a->state || !a->slot_idx)
-        return KDA_ERR_NULL;
-    if (!a->norm_weight && a->gate)
-        return KDA_ERR_NULL;
-    const int64_t hk = (int64_t)a->H * a->K, hvk = (int64_t)a->HV * a->K, hvv = (int64_t)a->HV * a->V;
-    if (a->num_slots < 0 || a->slot_stride < hvk * a->V)
-        return KDA_ERR_SHAPE;
-    if (a->q_stride < hk || a->k_stride < hk || a->v_stride < hvv || a->out_stride < hvv ||
-        (a->gate && a->gate_stride < hvv))
-        return KDA_ERR_SHAPE;
-    if (raw ? (a->raw_gate_stride < hvk || a->raw_beta_stride < a->HV)
-            : (a->g_stride < hvk || a->beta_stride < a->HV))
-        return KDA_ERR_SHAPE;
-    if (!(a->norm_eps >= 0.0f))
-        return KDA_ERR_SHAPE;
-    if (!aligned(a->q, 16) || !aligned(a->k, 16) || a->q_stride % 8 || a->k_stride % 8 ||
-        !aligned(a->v, 8) || a->v_stride % 4 ||
-        (raw ? (!aligned(a->raw_gate, 16) || a->raw_gate_stride % 8 || !aligned(a->raw_beta, 2) ||
-                !aligned(a->A_log, 4) || !aligned(a->dt_bias, 16))
-             : (!aligned(a->g, 16) || a->g_stride % 4 || !aligned(a->beta, 4))) ||
-        !aligned(a->state, 4 * state_elem) || a->slot_stride % 4 ||
-        !aligned(a->out, 8) || a->out_stride % 4 || !aligned(a->slot_idx, 4) ||
-        (cu_seqlens && !aligned(cu_seqlens, 4)) ||
-        (a->gate && (!aligned(a->gate, 8) || a->gate_stride % 4 || !aligned(a->norm_weight, 8))))
-        return KDA_ERR_ALIGN;
-
-    const ByteRange out = span(a->out, tokens, a->out_stride, hvv, 2);
-    const ByteRange state = span(a->state, a->num_slots, a->slot_stride, hvk * a->V, state_elem);
-    const ByteRange inputs[] = {
-        span(a->q, tokens, a->q_stride, hk, 2),
-        span(a->k, tokens, a->k_stride, hk, 2),
-        span(a->v, tokens, a->v_stride, hvv, 2),
-        span(a->g, tokens, a->g_stride, hvk, 4),
-        span(a->beta, tokens, a->beta_stride, a->HV, 4),
-        span(a->slot_idx, 1, 0, a->N, 4),
-        span(cu_seqlens, 1, 0, (int64_t)a->N + 1, 4),
-        span(a->gate, tokens, a->gate_stride, hvv, 2),
-        span(a->norm_weight, 1, 0, a->V, 2),
-        span(a->raw_gate, tokens, a->raw_gate_stride, hvk, 2),
-        span(a->raw_beta, tokens, a->raw_beta_stride, a->HV, 2),
-        span(a->A_log, 1, 0, a->HV, 4),
-        span(a->dt_bias, 1, 0, hvk, 4),
-    };
-    if (overlaps(out, state))
-        return KDA_ERR_ALIAS;
-    for (const ByteRange &in : inputs)
-        if (overlaps(out, in) || overlaps(state, in))
-            return KDA_ERR_ALIAS;
-    ByteRange inter;
-    if (a->inter_state) {
-        if (!aligned(a->inter_state, 4 * state_elem) || a->inter_stride % 4)
-            return KDA_ERR_ALIGN;
-        if (a->inter_stride < hvk * a->V)
-            return KDA_ERR_SHAPE;
-        inter = span(a->inter_state, tokens, a->inter_stride, hvk * a->V, state_elem);
-        if (overlaps(inter, out) || overlaps(inter, state))
-            return KDA_ERR_ALIAS;
-        for (const ByteRange &in : inputs)
-            if (overlaps(inter, in))
-                return KDA_ERR_ALIAS;
-    }
-    if (flags & KDA_FLAG_VALIDATE) {
-        if (!a->device_status)
-            return KDA_ERR_NULL;
-        if (!aligned(a->device_status, 4))
-            return KDA_ERR_ALIGN;
-        const ByteRange st = span(a->device_status, 1, 0, 1, 4);
-        if (overlaps(st, out) || overlaps(st, state) || overlaps(st, inter))
-            return KDA_ERR_ALIAS;
-        for (const ByteRange &in : inputs)
-            if (overlaps(st, in))
-                return KDA_ERR_ALIAS;
-    }
-    return KDA_OK;
-}
-
-// Value-tile width from the number of (request, value head) tiles, tuned on
-// MI355X with cold caches (256 compute units):
-//   fewer tiles than compute units: 32 columns, one wave per workgroup, the
-//     most workgroups in flight for a latency-bound call;
-//   one token per request, 256 .. 1023 tiles: 64 columns;
-//   several tokens per request, or 1024 tiles and up: 128 columns.
-// The norm epilogue needs all 128 columns in one workgroup.
-int32_t plan_vtile(int64_t units, int32_t T, bool norm)
-{
-    if (norm)
-        return 128;
-    if (units < 256)
-        return 32;
-    if (T == 1 && units < 1024)
-        return 64;
-    return 128;
-}
-
-// 16-column waves: 0 = not used (the 32-column kernel), PLAN_SPLIT = the
-// split-key kernel (32 columns per workgroup), else kda_decode_q_kernel's
-// waves per workgroup (2, 4 or 8: 32, 64 or 128 columns).  Measured on
-// MI355X with cold caches against the 32-column kernel (us per call, H = 8
-// unless noted):
-//   fp32 pool, no norm, one token: the split-key kernel wins up to 128
-//     tiles (N1 3.05 vs 3.42, N8 3.74 vs 4.00, N16 4.68 vs 4.75) and loses
-//     from 192 (N24 5.68 vs 5.50); with the fused gate activation two waves
-//     of kda_decode_q_kernel win up to 64 tiles instead (N1 3.32, split-key
-//     3.41, 32-column 3.53; N8 3.98, 4.06, 4.09); from 512 tiles eight
-//     waves (full 512-byte rows of the staged tile; N64: 12.14 vs 12.94,
-//     N128: 26.8 vs 27.7, N256/H12: 76.1 vs 78.3), which lose below (N48:
-//     10.2 vs 9.6);
-//   fp32 pool, no norm, two or more tokens: the split-key kernel up to 192
-//     tiles (T = 4: N1 4.59 vs 4.73 with four waves, N8 5.13 vs 5.27, N24
-//     7.8 vs 8.3), and with two or three tokens up to 256 (N32/T2 7.1 vs
-//     7.8, N32/T3 7.9 vs 8.2); four waves beyond that, up to 512 tiles (T =
-//     4: N48 11.5-12.0 vs 12.4, N64 13.9-14.1 vs 17.3 split-key and 16.4
-//     32-column), which lose above (N96/T4: 24.7 vs 21.2 with the
-//     32-column kernel);
-//   fp32 pool, packed: eight waves from 512 tiles (the H12 batch 68.0 vs
-//     69.7 us);
-//   bf16 pool, no norm: four waves (64 columns: full 128-byte row pieces of
-//     bf16) win at every size and token count, step or packed (T = 1: N32
-//     5.12 vs 5.89, N128 15.8 vs 20.6; T = 4: N32 7.46 vs 9.98; the packed
-//     H12 batch 40.9 vs 50.7), where the 32-column kernel moves half lines;
-//     only the split-key kernel beats them, with two or more tokens up to
-//     32 tiles (T = 4: N1 4.85 vs 5.05, N4 5.02 vs 5.07; one token ties or
-//     loses: N4 3.59 vs 3.46);
-//   with the norm epilogue (eight waves: the head's 128 columns in one
-//     workgroup): every bf16-pool call (normed N64/H16 T=1 17.4 vs 20.1, N8
-//     T=4 9.3 vs 10.8) and fp32 step calls with two or more tokens up to
-//     512 tiles (N8/H16 T=4 10.0 vs 10.7, N32 17.8 vs 19.3); one-token fp32
-//     calls gain nothing (N32/H16 12.8-13.0 both) or lose (N16: 8.9 vs 7.8).
-// T = 0 stands for a packed call; raw = the fused gate activation.
-constexpr int32_t PLAN_SPLIT = 1;
-
-int32_t plan_quarter_waves(int64_t units, int32_t T, bool bf16, bool norm, bool raw)
-{
-    if (norm)
-        return (bf16 || (T >= 2 && units <= 512)) ? 8 : 0;
-    if (bf16)
-        return (T >= 2 && units <= 32) ? PLAN_SPLIT : 4;
-    if (T == 0)
-        return units >= 512 ? 8 : 0;
-    if (T == 1) {
-        if (units >= 512)
-            return 8;
-        if (raw)
-            return units <= 64 ? 2 : 0;
-        return units <= 128 ? PLAN_SPLIT : 0;
-    }
-    if (units <= 192 || (units <= 256 && T <= 3))
-        return PLAN_SPLIT;
-    return units > 512 ? 0 : 4;
-}
-
-template <int PF, bool RAWG, bool BF16S, bool EARLY>
-kda_status launch_split(const DecodeParams &p, int64_t units, hipStream_t stream)
-{
-    const int64_t blocks = units * (VD / S_COLS);
-    if (blocks > 0x7FFFFFFF)
-        return KDA_ERR_SHAPE;
-    const int32_t *slot_idx = p.slot_idx;
-    void *state = p.state;
-    int64_t slot_stride = p.slot_stride, num_slots = p.num_slots;
-    int32_t HV = p.HV, T = p.T;
-    const int32_t *status = p.status;
-    void *args[] = {&slot_idx, &state, &slot_stride, &num_slots, &HV, &T, &status, const_cast<DecodeParams *>(&p)};
-    const void *fn = reinterpret_cast<const void *>(&kda_decode_split_kernel<PF, RAWG, BF16S, EARLY>);
-    const hipError_t e = hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(256), args, split_lds_bytes(), stream);
-    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
-}
-
-template <bool RAWG, bool BF16S>
-kda_status dispatch_split(const DecodeParams &p, int64_t units, bool early, hipStream_t s)
-{
-    constexpr bool E = !BF16S;   // bf16 pools load the tile first
-    switch (p.T) {
-    case 1: return launch_split<1, RAWG, BF16S, false>(p, units, s);
-    case 2: return E && early ? launch_split<2, RAWG, BF16S, E>(p, units, s) : launch_split<2, RAWG, BF16S, false>(p, units, s);
-    case 3: return E && early ? launch_split<3, RAWG, BF16S, E>(p, units, s) : launch_split<3, RAWG, BF16S, false>(p, units, s);
-    default: return E && early ? launch_split<4, RAWG, BF16S, E>(p, units, s) : launch_split<4, RAWG, BF16S, false>(p, units, s);
-    }
-}
-
-template <int NQ, int PF, bool NORM, bool RAWG, bool BF16S, bool EARLY>
-kda_status launch_q(const DecodeParams &p, int64_t units, hipStream_t stream)
-{
-    const int64_t blocks = units * (8 / NQ);
-    if (blocks > 0x7FFFFFFF)
-        return KDA_ERR_SHAPE;
-    const int32_t *slot_idx = p.slot_idx, *cu_seqlens = p.cu_seqlens;
-    void *state = p.state;
-    int64_t slot_stride = p.slot_stride, num_slots = p.num_slots;
-    int32_t HV = p.HV, T = p.T;
-    const int32_t *status = p.status;
-    void *args[] = {&slot_idx, &cu_seqlens, &state, &slot_stride, &num_slots, &HV, &T, &status,
-                    const_cast<DecodeParams *>(&p)};
-    const void *fn = reinterpret_cast<const void *>(&kda_decode_q_kernel<NQ, PF, NORM, RAWG, BF16S, EARLY>);
-    const hipError_t e = hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(64 * NQ), args, q_lds_bytes(NQ), stream);
-    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
-}
-
-template <int NQ, int PF, bool NORM, bool RAWG, bool BF16S>
-kda_status launch_q_order(const DecodeParams &p, int64_t units, bool early, hipStream_t s)
-{
-    if constexpr (PF == 1 || BF16S)
-        return launch_q<NQ, PF, NORM, RAWG, BF16S, false>(p, units, s);
-    else
-        return early ? launch_q<NQ, PF, NORM, RAWG, BF16S, true>(p, units, s)
-                     : launch_q<NQ, PF, NORM, RAWG, BF16S, false>(p, units, s);
-}
-
-template <int NQ, bool NORM, bool RAWG, bool BF16S>
-kda_status dispatch_q_tokens(const DecodeParams &p, int64_t units, bool early, hipStream_t s)
-{
-    switch (p.cu_seqlens ? 4 : p.T) {
-    case 1: return launch_q_order<NQ, 1, NORM, RAWG, BF16S>(p, units, early, s);
-    case 2: return launch_q_order<NQ, 2, NORM, RAWG, BF16S>(p, units, early, s);
-    case 3: return launch_q_order<NQ, 3, NORM, RAWG, BF16S>(p, units, early, s);
-    default: return launch_q_order<NQ, 4, NORM, RAWG, BF16S>(p, units, early, s);
-    }
-}
-
-// The load order of a 16-column-wave launch (nq: waves per workgroup, or
-// PLAN_SPLIT): the first token's inputs before the state tile (the
-// kernels' EARLY order) for fp32-pool calls with two or more tokens per
-// request, or packed, from 192 tiles; with fewer than eight waves only up
-// to 256 tiles, or 384 with three or more tokens; otherwise the tile first.
-// Measured on MI355X with cold caches (us per call, H = 8, tile first vs
-// inputs first): N8/T4 5.22 vs 5.46, N16/T4 6.56 vs 6.61, N24/T4 8.03 vs
-// 7.77, N32/T3 8.56 vs 8.03, N32/T4 9.47 vs 9.06; four waves at 384 tiles
-// N48/T2 9.96 vs 10.60, N48/T3 11.07 vs 10.75, N48/T4 12.45 vs 11.86, and
-// at 512 N64/T2 12.53 vs 13.58, N64/T3 12.78 vs 13.72, N64/T4 14.61 vs
-// 14.98; eight waves: the packed H12 batch 69.2 vs 68.0, normed
-// N32/H16/T4 (512 tiles) 18.7 vs 17.8.  With one token the tile first wins
-// at every size (N1 3.04 vs 3.54, N64 12.2 vs 12.9), and with a bf16 pool,
-// whose tiles are half the bytes (N32/T4 7.48 vs 7.59).
-bool plan_early(int64_t units, int32_t T, bool bf16, int nq)
-{
-    if (bf16 || T == 1 || units < 192)
-        return false;
-    if (nq == 8)
-        return true;
-    return units <= 256 || (T >= 3 && units <= 384);
-}
-
-template <bool RAWG, bool BF16S>
-kda_status dispatch_q(const DecodeParams &p, int64_t units, int nq, bool norm, hipStream_t s)
-{
-    const bool early = plan_early(units, p.cu_seqlens ? 0 : p.T, BF16S, norm ? 8 : nq);
-    if (norm)
-        return dispatch_q_tokens<8, true, RAWG, BF16S>(p, units, early, s);
-    if (nq == PLAN_SPLIT)
-        return dispatch_split<RAWG, BF16S>(p, units, early, s);
-    // two waves serve only one-token fp32 calls with the fused gate
-    if constexpr (RAWG && !BF16S) {
-        if (nq == 2) {
-            if (p.T != 1 || p.cu_seqlens)
-                return KDA_ERR_UNSUPPORTED;
-            return launch_q<2, 1, false, true, false, false>(p, units, s);
-        }
-    }
-    return nq == 8 ? dispatch_q_tokens<8, false, RAWG, BF16S>(p, units, early, s)
-                   : dispatch_q_tokens<4, false, RAWG, BF16S>(p, units, early, s);
-}
-
-template <int NW, bool NORM, bool BF16S, bool RAWG>
-kda_status launch_decode(const DecodeParams &p, int64_t units, int body, hipStream_t stream)
-{
-    const int64_t blocks = units * (4 / NW);
-    if (blocks > 0x7FFFFFFF)
-        return KDA_ERR_SHAPE;
-    const int32_t *slot_idx = p.slot_idx, *cu_seqlens = p.cu_seqlens;
-    void *state = p.state;
-    int64_t slot_stride = p.slot_stride, num_slots = p.num_slots;
-    int32_t HV = p.HV, T = p.T;
-    const int32_t *status = p.status;
-    void *args[] = {&slot_idx, &cu_seqlens, &state, &slot_stride, &num_slots, &HV, &T, &status,
-                    const_cast<DecodeParams *>(&p)};
-    // the loop body serves only fp32 pools with activated gates (run_decode's
-    // plan); it is not instantiated for the other forms
-    const void *fn = body == BODY_STAGED
-                         ? reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_STAGED, BF16S, RAWG>)
-                         : reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_PEELED, BF16S, RAWG>);
-    if constexpr (!BF16S && !RAWG) {
-        if (body == BODY_LOOP)
-            fn = reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_LOOP, BF16S, RAWG>);
-    }
-    const hipError_t e = hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(64 * NW), args, 0, stream);
-    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
-}
-
-template <bool BF16S, bool RAWG>
-kda_status dispatch_width(const DecodeParams &p, int64_t units, int body, bool norm, int vtile, hipStream_t s)
-{
-    if (norm)
-        return launch_decode<4, true, BF16S, RAWG>(p, units, body, s);
-    switch (vtile) {
-    case 32: return launch_decode<1, false, BF16S, RAWG>(p, units, body, s);
-    case 64: return launch_decode<2, false, BF16S, RAWG>(p, units, body, s);
-    default: return launch_decode<4, false, BF16S, RAWG>(p, units, body, s);
-    }
-}
-
-template <bool BF16S>
-kda_status dispatch_gate(const DecodeParams &p, int64_t units, int body, bool norm, int vtile, hipStream_t s)
-{
-    if (p.raw_gate)
-        return dispatch_width<BF16S, true>(p, units, body, norm, vtile, s);
-    return dispatch_width<BF16S, false>(p, units, body, norm, vtile, s);
-}
-
-kda_status run_decode(const kda_decode_args *a, int32_t T, const int32_t *cu_seqlens, int64_t tokens,
-                      uint32_t flags, void *stream)
-{
-    if (!a)
-        return KDA_ERR_NULL;
-    kda_status st = validate(a, tokens, cu_seqlens, flags);
-    if (st != KDA_OK)
-        return st;
-    if (a->N == 0)
-        return KDA_OK;
-    const bool norm = a->gate != nullptr;
-    const bool bf16_pool = (flags & KDA_FLAG_STATE_BF16) != 0;
-    const int64_t units = (int64_t)a->N * a->HV;
-    int vtile = vtile_from_flags(flags);
-    // a forced width keeps the 32-column waves; otherwise the plan may pick
-    // the 16-column waves
-    const int nq =
-        vtile == 0 ? plan_quarter_waves(units, cu_seqlens ? 0 : T, bf16_pool, norm, a->raw_gate != nullptr) : 0;
-    if (vtile == 0)
-        vtile = plan_vtile(units, cu_seqlens ? 1 : T, norm);
-    if (norm && vtile != 128)
-        return KDA_ERR_UNSUPPORTED;
-    st = check_device();
-    if (st != KDA_OK)
-        return st;
-
-    DecodeParams p;
-    p.q = static_cast<const uint16_t *>(a->q);
-    p.k = static_cast<const uint16_t *>(a->k);
-    p.v = static_cast<const uint16_t *>(a->v);
-    p.g = a->g;
-    p.beta = a->beta;
-    p.state = a->state;
-    p.slot_idx = a->slot_idx;
-    p.cu_seqlens = cu_seqlens;
-    p.out = static_cast<uint16_t *>(a->out);
-    p.gate = static_cast<const uint16_t *>(a->gate);
-    p.norm_weight = static_cast<const uint16_t *>(a->norm_weight);
-    p.q_stride = a->q_stride;
-    p.k_stride = a->k_stride;
-    p.v_stride = a->v_stride;
-    p.g_stride = a->g_stride;
-    p.beta_stride = a->beta_stride;
-    p.out_stride = a->out_stride;
-    p.gate_stride = a->gate_stride;
-    p.num_slots = a->num_slots;
-    p.slot_stride = a->slot_stride;
-    p.HV = a->HV;
-    p.T = T;
-    const uint64_t qk_magic = (uint64_t(1) << 32) / (uint64_t)(a->HV / a->H) + 1;
-    p.qk_magic = (uint32_t)qk_magic;
-    p.qk_magic_hi = (uint32_t)(qk_magic >> 32);
-    p.scale = a->scale;
-    p.eps = a->norm_eps;
-    p.status = nullptr;
-    p.inter_state = a->inter_state;
-    p.inter_stride = a->inter_stride;
-    p.raw_gate = static_cast<const uint16_t *>(a->raw_gate);
-    p.raw_beta = static_cast<const uint16_t *>(a->raw_beta);
-    p.A_log = a->A_log;
-    p.dt_bias = a->dt_bias;
-    p.raw_gate_stride = a->raw_gate_stride;
-    p.raw_beta_stride = a->raw_beta_stride;
-
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (flags & KDA_FLAG_VALIDATE) {
-        p.status = a->device_status;
+    const DecodeParams p = make_params(c);
+    const kda_decode_args *a = c.args;
+    hipStream_t s = static_cast<hipStream_t>(c.stream);
+    if (c.validate) {
         const int32_t *slots = a->slot_idx;
+        const int32_t *cu = c.cu_seqlens;
         int32_t n = a->N;
-        int64_t num_slots = a->num_slots;
+        int64_t num_slots = a->num_slots, tokens = c.tokens;
         int32_t *status = a->device_status;
-        void *vargs[] = {&slots, &cu_seqlens, &n, &num_slots, &tokens, &status};
+        void *vargs[] = {&slots, &cu, &n, &num_slots, &tokens, &status};
         if (hipLaunchKernel(reinterpret_cast<const void *>(&kda_validate_kernel), dim3(1), dim3(VALIDATE_THREADS),
                             vargs, 0, s) != hipSuccess)
             return KDA_ERR_LAUNCH;
     }
-    if (nq) {
-        if (bf16_pool)
-            return a->raw_gate ? dispatch_q<true, true>(p, units, nq, norm, s)
-                               : dispatch_q<false, true>(p, units, nq, norm, s);
-        return a->raw_gate ? dispatch_q<true, false>(p, units, nq, norm, s)
-                           : dispatch_q<false, false>(p, units, nq, norm, s);
-    }
-    // 32-column waves.  Packed batches: the staged body; step calls with
-    // several tokens per request, fewer than 512 tiles (two per compute
-    // unit), the fused gate activation or a bf16 pool: the peeled body (its
-    // straight-line first token also lets the activation run while the tile
-    // is in flight, and at 144 VGPRs it runs three waves per SIMD, which the
-    // half-size bf16 tiles need); otherwise the prefetching loop (all
-    // measured on MI355X, cold caches)
-    const int body = cu_seqlens != nullptr ? BODY_STAGED
-                     : (T > 1 || units < 512 || a->raw_gate || bf16_pool) ? BODY_PEELED : BODY_LOOP;
-    if (flags & KDA_FLAG_STATE_BF16)
-        return dispatch_gate<true>(p, units, body, norm, vtile, s);
-    return dispatch_gate<false>(p, units, body, norm, vtile, s);
+    const int64_t units = (int64_t)a->N * a->HV;
+    const bool norm = a->gate != nullptr;
+    const bool raw = a->raw_gate != nullptr;
+    if (c.bf16_state)
+        return raw ? dispatch<true, true>(p, units, c.plan, norm, s) : dispatch<false, true>(p, units, c.plan, norm, s);
+    return raw ? dispatch<true, false>(p, units, c.plan, norm, s) : dispatch<false, false>(p, units, c.plan, norm, s);
 }
 
-}  // namespace
-
-extern "C" {
-
-kda_status kda_decode_step(const kda_decode_args *args, int32_t T, uint32_t flags, void *stream)
+kda_status launch_gated_rmsnorm(const void *x, const void *gate, const void *weight, void *y, int64_t rows,
+                                int32_t V, float eps, void *stream)
 {
-    if (!args)
-        return KDA_ERR_NULL;
-    if (T < 1)
-        return KDA_ERR_SHAPE;
-    return run_decode(args, T, nullptr, (int64_t)args->N * T, flags, stream);
-}
-
-kda_status kda_decode_packed(const kda_decode_args *args, const int32_t *cu_seqlens, int64_t total_tokens,
-                             uint32_t flags, void *stream)
-{
-    if (!args || !cu_seqlens)
-        return KDA_ERR_NULL;
-    return run_decode(args, 0, cu_seqlens, total_tokens, flags, stream);
-}
-
-kda_status kda_gated_rmsnorm(const void *x, const void *gate, const void *weight, void *y, int64_t rows,
-                             int32_t V, float eps, void *stream)
-{
-    if (!x || !gate || !weight || !y)
-        return KDA_ERR_NULL;
-    if (rows < 0 || V < 2 || V > 8192 || V % 2 || !(eps >= 0.0f))
-        return KDA_ERR_SHAPE;
-    if (!aligned(x, 4) || !aligned(gate, 4) || !aligned(weight, 4) || !aligned(y, 4))
-        return KDA_ERR_ALIGN;
-    const ByteRange yr = span(y, rows, V, V, 2);
-    if (y != x && overlaps(yr, span(x, rows, V, V, 2)))
-        return KDA_ERR_ALIAS;
-    if (overlaps(yr, span(gate, rows, V, V, 2)) || overlaps(yr, span(weight, 1, 0, V, 2)))
-        return KDA_ERR_ALIAS;
-    if (rows == 0)
-        return KDA_OK;
-    kda_status st = check_device();
-    if (st != KDA_OK)
-        return st;
     const int64_t blocks = (rows + 3) / 4;
-    if (blocks > 0x7FFFFFFF)
-        return KDA_ERR_SHAPE;
     const uint16_t *xp = static_cast<const uint16_t *>(x);
     const uint16_t *zp = static_cast<const uint16_t *>(gate);
     const uint16_t *wp = static_cast<const uint16_t *>(weight);
@@ -2096,34 +1798,8 @@ kda_status kda_gated_rmsnorm(const void *x, const void *gate, const void *weight
     int Vi = V;
     void *args[] = {&xp, &zp, &wp, &yp, &rows, &Vi, &eps};
     const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&kda_gated_rmsnorm_kernel),
-                                         dim3((uint32_t)blocks), dim3(256), args, 0,
-                                         static_cast<hipStream_t>(stream));
+                                         dim3((uint32_t)blocks), dim3(256), args, 0, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
-int32_t kda_decode_plan(int64_t units, int32_t T, uint32_t options)
-{
-    const bool norm = (options & KDA_PLAN_NORM) != 0, packed = (options & KDA_PLAN_PACKED) != 0;
-    const int32_t nq = plan_quarter_waves(units, packed ? 0 : T, (options & KDA_PLAN_STATE_BF16) != 0, norm,
-                                          (options & KDA_PLAN_RAW_GATE) != 0);
-    if (options & KDA_PLAN_LAYOUT)
-        return nq == 0 ? KDA_LAYOUT_WIDE : nq == PLAN_SPLIT ? KDA_LAYOUT_SPLIT : KDA_LAYOUT_QUARTER;
-    return nq == PLAN_SPLIT ? S_COLS : nq ? 16 * nq : plan_vtile(units, packed ? 1 : T, norm);
-}
-
-const char *kda_status_string(kda_status status)
-{
-    switch (status) {
-    case KDA_OK: return "ok";
-    case KDA_ERR_NULL: return "a required pointer is NULL";
-    case KDA_ERR_SHAPE: return "a size is out of range or unsupported";
-    case KDA_ERR_ALIGN: return "a pointer or stride breaks the alignment rules";
-    case KDA_ERR_ALIAS: return "a written buffer overlaps another buffer of the call";
-    case KDA_ERR_UNSUPPORTED: return "unsupported flag or mode";
-    case KDA_ERR_DEVICE: return "the current device is not gfx950, or a HIP query failed";
-    case KDA_ERR_LAUNCH: return "kernel launch failed";
-    }
-    return "unknown status";
-}
-
-}  // extern "C"
+}  // namespace kda_internal

@@ -20,8 +20,15 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(_HERE, "kda_oracle.c")
-LIB = os.path.join(_HERE, "liboracle.so")
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall", "-Wextra"]
+# KDA_ORACLE_SANITIZE=1 (the test suite's sanitizer tier, in a process that
+# preloads the sanitizer runtimes): the oracle is built and loaded with
+# AddressSanitizer and UndefinedBehaviorSanitizer, any finding fatal
+SANITIZE = os.environ.get("KDA_ORACLE_SANITIZE") == "1"
+SANITIZE_FLAGS = ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+if SANITIZE:
+    CFLAGS = CFLAGS + SANITIZE_FLAGS
+LIB = os.path.join(_HERE, "liboracle_san.so" if SANITIZE else "liboracle.so")
 
 _lib = None
 

@@ -10,6 +10,13 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    # The sanitizer tier (test_sanitizers.py) runs the host-side ABI tests
+    # against a host-only build of the library's host layer made with
+    # AddressSanitizer and UndefinedBehaviorSanitizer: it names that build here.
+    host_lib = os.environ.get("KDA_TEST_HOST_LIBRARY")
+    if host_lib:
+        import linear_attention_recurrent_decode_amd as kda
+        kda._lib = kda._open(host_lib)
 
 
 def pytest_collection_modifyitems(config, items):

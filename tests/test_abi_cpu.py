@@ -319,13 +319,54 @@ def test_aliasing():
 
 
 def test_unknown_flags():
-    a, _ = _valid_args()
-    assert _step(a, flags=4) == UNSUP
-    a, _ = _valid_args()
-    assert _step(a, flags=1 << 12) == UNSUP
+    for flags in (4, 1 << 10, 1 << 20, 1 << 31, kda.KDA_FLAG_KERNEL(6), kda.KDA_FLAG_KERNEL(15),
+                  kda.KDA_FLAG_ORDER(3)):
+        a, _ = _valid_args()
+        assert _step(a, T=2, flags=flags) == UNSUP, hex(flags)
     a, _ = _valid_args()
     a.gate, a.gate_stride, a.norm_weight = BASE + 40 * (1 << 26), 4 * 128, BASE + 41 * (1 << 26)
     assert _step(a, flags=kda.KDA_FLAG_VTILE(32)) == UNSUP      # the norm needs 128 columns
+
+
+def _norm_args():
+    a, cu = _valid_args()
+    a.gate, a.gate_stride, a.norm_weight = BASE + 40 * (1 << 26), 4 * 128, BASE + 41 * (1 << 26)
+    return a, cu
+
+
+K, O = kda.KDA_FLAG_KERNEL, kda.KDA_FLAG_ORDER
+
+
+@pytest.mark.parametrize("make,T,flags,expect", [
+    # forced kernels the library provides: validation passes, the device check stops the call
+    (_valid_args, 1, K(kda.KDA_KERNEL_WIDE), DEVICE),
+    (_valid_args, 2, K(kda.KDA_KERNEL_WIDE) | kda.KDA_FLAG_VTILE(64), DEVICE),
+    (_valid_args, 1, K(kda.KDA_KERNEL_QUARTER4), DEVICE),
+    (_valid_args, 3, K(kda.KDA_KERNEL_QUARTER8) | O(kda.KDA_ORDER_INPUTS_FIRST), DEVICE),
+    (_valid_args, 4, K(kda.KDA_KERNEL_SPLIT) | O(kda.KDA_ORDER_TILE_FIRST), DEVICE),
+    (_valid_args, 2, O(kda.KDA_ORDER_INPUTS_FIRST), DEVICE),    # the library's kernel, forced order
+    (_norm_args, 2, K(kda.KDA_KERNEL_QUARTER8), DEVICE),
+    (_norm_args, 1, K(kda.KDA_KERNEL_WIDE), DEVICE),
+    # combinations no kernel provides
+    (_valid_args, 2, K(kda.KDA_KERNEL_QUARTER4) | kda.KDA_FLAG_VTILE(64), UNSUP),   # a width is for WIDE only
+    (_norm_args, 2, K(kda.KDA_KERNEL_QUARTER4), UNSUP),         # the norm: 128 columns per workgroup
+    (_norm_args, 2, K(kda.KDA_KERNEL_SPLIT), UNSUP),
+    (_norm_args, 1, K(kda.KDA_KERNEL_WIDE) | kda.KDA_FLAG_VTILE(64), UNSUP),
+    (_valid_args, 1, K(kda.KDA_KERNEL_QUARTER2), UNSUP),        # two waves: one-token fused-gate calls only
+    (_valid_args, 1, K(kda.KDA_KERNEL_WIDE) | O(kda.KDA_ORDER_TILE_FIRST), UNSUP),   # the body fixes the order
+    (_valid_args, 1, K(kda.KDA_KERNEL_SPLIT) | O(kda.KDA_ORDER_INPUTS_FIRST), UNSUP),   # one token: tile first
+    (_valid_args, 2, K(kda.KDA_KERNEL_SPLIT) | O(kda.KDA_ORDER_INPUTS_FIRST) | kda.KDA_FLAG_STATE_BF16, UNSUP),
+])
+def test_forced_kernels(make, T, flags, expect):
+    a, _ = make()
+    a.N = 2 if T > 2 else a.N
+    assert _step(a, T=T, flags=flags) == expect
+
+
+def test_forced_split_kernel_refuses_packed_calls():
+    a, cu = _valid_args()
+    assert _packed(a, cu, 4, flags=K(kda.KDA_KERNEL_SPLIT)) == UNSUP
+    assert _packed(a, cu, 4, flags=K(kda.KDA_KERNEL_QUARTER4)) == DEVICE
 
 
 def test_zero_requests_is_a_no_op():
