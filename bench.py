@@ -155,6 +155,18 @@ def traffic_for(workload: str):
         return None
 
 
+def shape_problem(ki, spec: str):
+    """A problem of the shape ``spec`` ("N=24,T=4,H=8"; T=0 packed) drawn from
+    the serving workloads' distributions."""
+    kv = dict(item.split("=") for item in spec.split(",") if item)
+    N, T, H = int(kv.get("N", 32)), int(kv.get("T", 1)), int(kv.get("H", 8))
+    HV = int(kv.get("HV", H))
+    slots = int(kv.get("slots", max(512, 2 * N)))
+    name = "shape_" + "_".join(f"{k}{v}" for k, v in kv.items())
+    return ki.make_problem(name, ki.SEED_BASE + 100 + N, N=N, H=H, HV=HV, K=128, V=128, num_slots=slots,
+                           T=T or None, raw_gates=kv.get("raw") == "1", norm=kv.get("norm") == "1")
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -278,6 +290,10 @@ def main():
     ap.add_argument("--warmup-ms", type=float, default=100.0, help="minimum wall time of graph-replayed warmup")
     ap.add_argument("--blocks", type=int, default=5, help="timed blocks (at least 3)")
     ap.add_argument("--workload", default="n32_t1_h8")
+    ap.add_argument("--shape", default=None,
+                    help="a workload of another shape with the same value distributions instead of --workload: "
+                         "comma-separated N=, T= (0: packed, 1..4 tokens per request), H=, HV=, slots=, "
+                         "raw=1 (fused gate), norm=1")
     ap.add_argument("--cpu-budget", type=float, default=8.0, help="seconds of oracle work per cpu_baseline run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the copy reference and the enqueue cost")
@@ -310,7 +326,7 @@ def main():
     torch.cuda.set_device(dev)
     lib = kda.library()
 
-    p = ki.workload(args.workload)
+    p = ki.workload(args.workload) if args.shape is None else shape_problem(ki, args.shape)
     bf16_state = args.state == "bf16"
     state_dtype = torch.bfloat16 if bf16_state else torch.float32
     state_elem = 2 if bf16_state else 4

@@ -214,8 +214,15 @@ typedef struct kda_decode_args {
  * token rows n*T .. n*T+T-1.  The tokens of one request are recurred in
  * order within the call with the state held on chip; the state is written
  * back once, after the last token.  One-token decode (T = 1) is the common
- * serving case and takes the same kernel.  Equivalent to kda_decode_packed
- * with cu_seqlens[n] = n*T.
+ * serving case and takes the same entry point.  Equivalent to
+ * kda_decode_packed with cu_seqlens[n] = n*T.
+ *
+ * Source: vLLM PR 57585, "Microbenchmark and earlier serving limits": the
+ * decode call over N requests of T = 1 or 4 tokens, 8 or 16 heads,
+ * K = V = 128, bf16 inputs and fp32 state; b12x PR 249, "Purpose": ordinary
+ * decode, where every live request brings exactly one token, is the hot
+ * case, and its maintainer's review keeps it an internal route of the one
+ * public call rather than a second entry point.
  */
 kda_status kda_decode_step(const kda_decode_args *args, int32_t T, uint32_t flags, void *stream);
 
@@ -227,6 +234,13 @@ kda_status kda_decode_step(const kda_decode_args *args, int32_t T, uint32_t flag
  * per-token tensors hold; it bounds the overlap checks only.  The device
  * metadata (slot_idx, cu_seqlens) is trusted as the serving scheduler wrote
  * it; slots outside the pool are skipped, never dereferenced.
+ *
+ * Source: FlashInfer PR 4562, description: packed decode that keeps
+ * caller-stream execution, row-strided beta, an indexed (noncompact)
+ * recurrent state, inactive graph-padding rows, a caller-owned output and
+ * graph replay; b12x PR 249, "Purpose": packed, padded, speculative and
+ * multi-token requests take the general route, which validates the device
+ * metadata (KDA_FLAG_VALIDATE here).
  */
 kda_status kda_decode_packed(const kda_decode_args *args, const int32_t *cu_seqlens,
                              int64_t total_tokens, uint32_t flags, void *stream);
@@ -266,7 +280,11 @@ kda_status kda_gated_rmsnorm(const void *x, const void *gate, const void *weight
  * (description); the thresholds here are this chip's measurements. */
 int32_t kda_decode_plan(int64_t units, int32_t T, uint32_t options);
 
-/* Static description of a status code. */
+/* Static description of a status code.  Source: b12x PR 249, inline review
+ * of the overlap checks: a call whose written buffers overlap its inputs is
+ * rejected with an error before any launch; FlashInfer PR 4562,
+ * description: inputs outside the supported bands are routed fail-closed.
+ * Every such refusal is a kda_status here; this returns its text. */
 const char *kda_status_string(kda_status status);
 
 #ifdef __cplusplus

@@ -191,66 +191,87 @@ int32_t plan_body(const CallShape &c)
     return (c.T > 1 || c.units < 512 || c.raw || c.bf16) ? BODY_PEELED : BODY_LOOP;
 }
 
-// The per-token 16-column layouts: 0 = the 32-column kernel, PLAN_SPLIT =
-// the split-key kernel, else kda_decode_q_kernel's waves per workgroup (2,
-// 4 or 8).  Measured on MI355X with cold caches (us per call, H = 8 unless
-// noted):
-//   fp32 pool, no norm, one token: the split-key kernel wins up to 128
-//     tiles (N1 3.05 vs 3.42 on the 32-column kernel, N8 3.74 vs 4.00, N16
-//     4.68 vs 4.75) and loses from 192 (N24 5.68 vs 5.50); with the fused
-//     gate activation two waves of kda_decode_q_kernel win up to 64 tiles
-//     instead; from 512 tiles eight waves (full 512-byte rows of the staged
-//     tile; N64 12.14 vs 12.94, N128 26.8 vs 27.7);
-//   fp32 pool, no norm, two or more tokens: the split-key kernel up to 192
-//     tiles, or 256 with two or three tokens (N32/T2 7.1 vs 7.8); four
-//     waves beyond that up to 512;
-//   fp32 pool, packed: eight waves from 512 tiles (the H12 batch 68.0 vs
-//     69.7 us);
-//   bf16 pool, no norm: four waves (64 columns: full 128-byte row pieces of
-//     bf16) at every size (T = 1: N32 5.12 vs 5.89, N128 15.8 vs 20.6; the
-//     packed H12 batch 40.9 vs 50.7), the split-key kernel with two or more
-//     tokens up to 32 tiles;
-//   with the norm epilogue (eight waves: the head's 128 columns in one
-//     workgroup): every bf16-pool call (normed N64/H16 T=1 17.4 vs 20.1)
-//     and fp32 step calls with two or more tokens up to 512 tiles (N8/H16
-//     T=4 10.0 vs 10.7, N32 17.8 vs 19.3); one-token fp32 calls gain
-//     nothing (N32/H16 12.8-13.0 both) or lose (N16: 8.9 vs 7.8).
+// The 16-column layouts: 0 = the 32-column kernel, PLAN_SPLIT = the
+// split-key kernel, else kda_decode_q_kernel's waves per workgroup (2, 4 or
+// 8).  Every boundary below is an A/B measurement on MI355X (bench.py
+// --flags-b: the two choices in alternating A B B A blocks of 200 cold
+// calls in one process; H = 8 unless noted; us per call, block spread
+// +-0.2 to 0.5%):
+//   fp32, one token: split-key waves up to 128 tiles (N16: 4.54 vs 4.75 on
+//     the 32-column kernel), the 32-column kernel from there (N20 5.12 vs
+//     5.21, N24 5.44 vs 5.93) to 384 tiles (N48 9.67 vs 9.95 on eight
+//     16-column waves), eight 16-column waves from 400 (N50 10.12 vs 11.34,
+//     N56 10.77 vs 12.50, N64 11.91 vs 12.86); with the fused gate two
+//     16-column waves up to 64 tiles (N8 3.80 vs 3.91 split-key, 4.06
+//     32-column; N9 4.24 on the 32-column kernel vs 4.36);
+//   fp32, two or more tokens: split-key waves up to 256 tiles (N32/T4 8.46
+//     vs 8.76 on four 16-column waves), and with two or three tokens up to
+//     320 (N40/T2 8.49 vs 8.59, N40/T3 8.81 vs 8.98; N36/T4 10.03 vs 9.81
+//     the other way); four 16-column waves to 576 tiles (N65/T4 16.33 vs
+//     17.79 on the 32-column kernel, N80/T4 19.32 vs 19.02, N96/T4 23.9 vs
+//     20.3);
+//   fp32, packed (1 to 4 tokens per request): four 16-column waves up to
+//     1024 tiles (N8: 5.63 vs 7.64 on the 32-column kernel, N24 7.69 vs
+//     9.28 and 8.75 on eight waves, N32 8.14 vs 9.40, N48 10.20 vs 12.48,
+//     N96 22.7 vs 24.4, N128 29.25 vs 29.17), eight beyond (N256 51.3 vs
+//     54.8, the H12 batch 67.6 vs 73.3 and 69.7 on the 32-column kernel);
+//   bf16 pool, no norm: four 16-column waves (full 128-byte row pieces of
+//     bf16) at every size (N32/T1 5.15 vs 5.81 on the 32-column kernel and
+//     5.68 on eight waves, N128/T1 15.3 vs 16.3 on eight), the split-key
+//     waves with two or more tokens up to 32 tiles (N4/T4 4.85 vs 5.00);
+//   the norm epilogue (the head's 128 columns in one workgroup: eight
+//     16-column waves or the 32-column kernel at 128 columns): eight waves
+//     for every bf16-pool call, fp32 calls of two or more tokens up to 512
+//     tiles (N8/H16/T4 9.72 vs 10.58) and fp32 one-token calls from 512
+//     (N32/H16 12.35 vs 12.61, N48/H16 20.3 vs 21.5; N16/H16 8.56 vs 7.83
+//     the other way).
 constexpr int32_t PLAN_SPLIT = 1;
 
 int32_t plan_quarter_waves(const CallShape &c)
 {
-    if (c.norm)
-        return (c.bf16 || (c.T >= 2 && c.units <= 512)) ? 8 : 0;
+    if (c.norm) {
+        if (c.bf16)
+            return 8;
+        return (c.T >= 2 ? c.units <= 512 : c.T == 1 && c.units >= 512) ? 8 : 0;
+    }
     if (c.bf16)
         return (c.T >= 2 && c.units <= 32) ? PLAN_SPLIT : 4;
     if (c.T == 0)
-        return c.units >= 512 ? 8 : 0;
+        return c.units <= 1024 ? 4 : 8;
     if (c.T == 1) {
-        if (c.units >= 512)
+        if (c.units > 384)
             return 8;
         if (c.raw)
             return c.units <= 64 ? 2 : 0;
         return c.units <= 128 ? PLAN_SPLIT : 0;
     }
-    if (c.units <= 192 || (c.units <= 256 && c.T <= 3))
+    if (c.units <= 256 || (c.T <= 3 && c.units <= 320))
         return PLAN_SPLIT;
-    return c.units > 512 ? 0 : 4;
+    return c.units <= 576 ? 4 : 0;
 }
 
-// The load order of a per-token 16-column launch: the first token's inputs
+// The load order of a 16-column-wave launch: the first token's inputs
 // before the state tile (so that their state-free part runs while the tile
-// is in flight) for fp32-pool calls with two or more tokens per request, or
-// packed, from 192 tiles: with eight waves at any size, with fewer up to
-// 256 tiles (384 with three or more tokens); otherwise the tile first.
-// With one token the tile first wins at every size (N1 3.04 vs 3.54 us,
-// N64 12.2 vs 12.9), and with a bf16 pool, whose tiles are half the bytes.
-bool plan_early(const CallShape &c, int32_t waves)
+// is in flight) for fp32-pool calls from 192 tiles with two or more tokens
+// per request, or packed on eight waves: eight waves always, split-key
+// waves up to 256 tiles, four waves with three or more tokens; otherwise
+// the tile first.  Measured as above: split-key N24/T4 7.49 vs 7.62 tile
+// first, N33/T2 7.33 tile first vs 7.72 on four waves, N36/T2 7.52 tile
+// first vs 8.24 inputs first; four waves N32/T4 8.78 vs 8.95 tile first,
+// N48/T4 10.31 vs 10.72, N64/T4 12.76 vs 13.09, N70/T4 17.18 vs 17.78;
+// packed, eight waves: the H12 batch 67.7 vs 68.8 tile first; four waves:
+// N24 7.58 tile first vs 7.69, N64 13.43 vs 13.53.  With one token the tile
+// first wins at every size (N1 3.04 vs 3.54 us, N64 12.2 vs 12.9), and with
+// a bf16 pool, whose tiles are half the bytes.
+bool plan_early(const CallShape &c, int32_t waves, bool split)
 {
     if (c.bf16 || c.T == 1 || c.units < 192)
         return false;
-    if (waves == 8)
-        return true;
-    return c.units <= 256 || (c.T >= 3 && c.units <= 384);
+    if (c.T == 0 || waves == 8)
+        return waves == 8;
+    if (split)
+        return c.units <= 256;
+    return c.T >= 3;
 }
 
 // The library's plan for a call.
@@ -261,11 +282,11 @@ Plan library_plan(const CallShape &c)
     if (nq == PLAN_SPLIT) {
         p.kernel = KERNEL_SPLIT;
         p.waves = 4;
-        p.early = plan_early(c, 4);
+        p.early = plan_early(c, 4, true);
     } else if (nq) {
         p.kernel = KERNEL_QUARTER;
         p.waves = c.norm ? 8 : nq;
-        p.early = plan_early(c, p.waves);
+        p.early = plan_early(c, p.waves, false);
     } else {
         p.kernel = KERNEL_WIDE;
         p.waves = plan_vtile(c.units, c.T, c.norm) / 32;
@@ -306,13 +327,13 @@ kda_status call_plan(const CallShape &c, uint32_t flags, Plan &out)
         p = Plan();
         p.kernel = KERNEL_QUARTER;
         p.waves = code == KDA_KERNEL_QUARTER2 ? 2 : code == KDA_KERNEL_QUARTER4 ? 4 : 8;
-        p.early = plan_early(c, p.waves);
+        p.early = plan_early(c, p.waves, false);
         break;
     case KDA_KERNEL_SPLIT:
         p = Plan();
         p.kernel = KERNEL_SPLIT;
         p.waves = 4;
-        p.early = plan_early(c, 4);
+        p.early = plan_early(c, 4, true);
         break;
     default:
         return KDA_ERR_UNSUPPORTED;

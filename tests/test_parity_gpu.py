@@ -115,7 +115,7 @@ def test_loop_body_shapes(N):
     with the oracle."""
     p = ki.make_problem("loop", 60 + N, N=N, H=8, HV=8, K=128, V=128, num_slots=2 * N + 8, T=1)
     assert kda.kda_decode_plan(N * 8, 1, False) == 128
-    assert kda.kda_decode_plan(N * 8, 1, packed=True) == 128
+    assert kda.kda_decode_plan(N * 8, 1, packed=True) == 64     # packed: four 16-column waves to 1024 tiles
     _log(f"one token, {N * 8} tiles", parity(p))
     width = 64 if N * 8 < 1024 else 128
     runs = []
@@ -756,17 +756,19 @@ QUARTER_CASES = [
     (1, 8, 8, 4, False, SPLIT),       # 8 tiles
     (5, 1, 3, 2, False, SPLIT),       # three value heads per q/k head
     (9, 4, 8, 3, True, SPLIT),        # fused gate activation
-    (24, 4, 8, 4, False, SPLIT),      # 192 tiles: the split-key layout's last size at four tokens
+    (24, 4, 8, 4, False, SPLIT),      # 192 tiles, four tokens, inputs first
     (7, 2, 4, 6, True, SPLIT),        # tokens past the four whose inputs load with the tile
     (8, 8, 8, 1, False, SPLIT),       # one token, 64 tiles
     (16, 2, 8, 1, False, SPLIT),      # one token, 128 tiles
     (8, 2, 8, 1, True, QUARTER),      # one token, 64 tiles, fused gate: two waves per workgroup
-    (32, 8, 8, 3, False, SPLIT),      # 256 tiles, three tokens
+    (32, 8, 8, 4, False, SPLIT),      # 256 tiles: the split-key layout's last size at four tokens
+    (40, 8, 8, 3, False, SPLIT),      # 320 tiles, three tokens, tile first: its last size at three
     (24, 2, 8, 2, True, SPLIT),       # 192 tiles, two tokens, fused gate, inputs first
-    (25, 4, 8, 4, False, QUARTER),    # 200 tiles: four waves per workgroup
-    (33, 8, 8, 2, True, QUARTER),     # 264 tiles, two tokens, fused gate
-    (40, 2, 6, 5, False, QUARTER),    # 240 tiles, five tokens
+    (36, 4, 8, 4, False, QUARTER),    # 288 tiles: four waves per workgroup, inputs first
+    (41, 8, 8, 2, True, QUARTER),     # 328 tiles, two tokens, fused gate, tile first
+    (44, 2, 6, 5, False, QUARTER),    # 264 tiles, five tokens
     (60, 8, 8, 2, False, QUARTER),    # 480 tiles, two tokens
+    (70, 8, 8, 4, False, QUARTER),    # 560 tiles, four tokens, tile first
 ]
 
 
@@ -869,18 +871,21 @@ def test_quarter_waves_norm_match_wide_waves_bitwise(case):
     assert torch.equal(o, results[0][0]) and torch.equal(st, results[0][1]) and torch.equal(it, results[0][2])
 
 
-@pytest.mark.parametrize("case", [(64, 8, 8, 1, True), (130, 4, 4, None, False), (130, 4, 4, None, True)])
+@pytest.mark.parametrize("case", [(64, 8, 8, 1, True, 128), (130, 4, 4, None, False, 64),
+                                  (130, 4, 4, None, True, 64), (260, 4, 4, None, False, 128),
+                                  (40, 4, 4, None, True, 64)])
 def test_eight_quarter_waves_match_wide_waves_bitwise(case):
-    """Eight 16-column waves per workgroup (one-token and packed fp32 calls
-    from 512 tiles) against the forced 32-column kernel, bit for bit with
-    per-token states, fused gate or not; the final state against the
+    """16-column waves of fp32 one-token calls from 400 tiles and packed
+    calls (four waves per workgroup up to 1024 tiles, eight beyond; eight
+    forced at every size) against the forced 32-column kernel, bit for bit
+    with per-token states, fused gate or not; the final state against the
     oracle."""
-    N, H, HV, T, raw = case
+    N, H, HV, T, raw, width = case
     p = ki.make_problem("eightq", 800 + N, N=N, H=H, HV=HV, K=128, V=128, num_slots=N + 9, T=T, t_max=3,
                         n_pad=N // 8, raw_gates=raw)
-    assert kda.kda_decode_plan(N * HV, T or 1, packed=T is None) == 128
+    assert kda.kda_decode_plan(N * HV, T or 1, packed=T is None) == width
     results = []
-    for flags in (0, kda.KDA_FLAG_VTILE(128)):
+    for flags in (0, kda.KDA_FLAG_VTILE(128), kda.KDA_FLAG_KERNEL(kda.KDA_KERNEL_QUARTER8)):
         d = _fresh(p)
         inter = guarded_full(d, (p.tokens, p.HV, p.K, p.V), 1232.0, torch.float32)
         run_gpu(d, flags=flags, inter_state=inter)
@@ -889,8 +894,8 @@ def test_eight_quarter_waves_match_wide_waves_bitwise(case):
         if flags == 0:
             _log(f"eight quarter waves {case}", compare(d, *run_oracle(p)))
         results.append((d.out.view(torch.int16).clone(), d.state.clone(), inter))
-    o, st, it = results[1]
-    assert torch.equal(o, results[0][0]) and torch.equal(st, results[0][1]) and torch.equal(it, results[0][2])
+    for o, st, it in results[1:]:
+        assert torch.equal(o, results[0][0]) and torch.equal(st, results[0][1]) and torch.equal(it, results[0][2])
 
 
 def test_quarter_waves_full_t4_sweep_match_wide_waves():
