@@ -63,7 +63,9 @@ COLD_BYTES = 1 << 30            # state traffic between two uses of the same slo
 HOST_ENQUEUE_US_BOUND = 8.0     # above the host's time per enqueue (about 4 us from Python)
 GAP_MIN_US = 2000.0             # the untimed replay before a block keeps the GPU busy at least this long
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "linear_attention_recurrent_decode_amd", "csrc", "kda_decode.hip")
+CSRC = os.path.join(ROOT, "linear_attention_recurrent_decode_amd", "csrc")
+# the kernels, and the host layer whose launch plan picks one for a workload
+CODE_SOURCES = (os.path.join(CSRC, "kda_decode.hip"), os.path.join(CSRC, "kda_host.cpp"))
 # kda_decode_plan(..., layout=True) values
 LAYOUT_NAMES = {0: "32-column waves", 1: "16-column waves", 2: "16-column waves, split key rows"}
 
@@ -130,16 +132,20 @@ def spread(values) -> dict:
     return {"median": float(np.median(v)), "p10": float(np.percentile(v, 10)), "p90": float(np.percentile(v, 90))}
 
 
-def kernel_code_sha256(path: str = KERNEL_SRC) -> str:
-    """SHA-256 of the kernel source's code: comments and whitespace removed,
-    so that editing a comment does not void the recorded counters (the
-    source has no string literal that holds a comment marker)."""
-    with open(path) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", "", text)
-    text = re.sub(r"\s+", "", text)
-    return hashlib.sha256(text.encode()).hexdigest()
+def kernel_code_sha256(paths=CODE_SOURCES) -> str:
+    """SHA-256 of the code of the kernels and of the launch plan: comments
+    and whitespace removed, so that editing a comment does not void the
+    recorded counters (the sources hold no string literal with a comment
+    marker)."""
+    h = hashlib.sha256()
+    for path in ([paths] if isinstance(paths, str) else paths):
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        text = re.sub(r"\s+", "", text)
+        h.update(text.encode())
+    return h.hexdigest()
 
 
 def traffic_for(workload: str):

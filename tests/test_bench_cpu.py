@@ -52,13 +52,18 @@ def test_slot_sets_are_disjoint_and_keep_padding():
 
 
 def test_kernel_code_fingerprint_ignores_comments(tmp_path):
-    src = open(bench.KERNEL_SRC).read()
+    kern, host = bench.CODE_SOURCES
+    src = open(kern).read()
     commented = tmp_path / "a.hip"
     commented.write_text("// a new comment\n" + src.replace("\n", "\n  ", 3) + "\n/* trailing */\n")
-    assert bench.kernel_code_sha256(str(commented)) == bench.kernel_code_sha256()
+    assert bench.kernel_code_sha256((str(commented), host)) == bench.kernel_code_sha256()
     changed = tmp_path / "b.hip"
     changed.write_text(src.replace("constexpr int STAGE_TOKENS = 4;", "constexpr int STAGE_TOKENS = 5;"))
-    assert bench.kernel_code_sha256(str(changed)) != bench.kernel_code_sha256()
+    assert bench.kernel_code_sha256((str(changed), host)) != bench.kernel_code_sha256()
+    # a change of the launch plan voids the counters too
+    plan = tmp_path / "h.cpp"
+    plan.write_text(open(host).read().replace("c.units <= 1024 ? 4 : 8", "c.units <= 512 ? 4 : 8"))
+    assert bench.kernel_code_sha256((kern, str(plan))) != bench.kernel_code_sha256()
 
 
 def test_more_than_one_gpu_is_refused():
