@@ -2,10 +2,15 @@
 with hipcc, the host layer (csrc/kda_host.cpp: C ABI, validation, launch
 plan) with the host C++ compiler, linked into one shared library.
 
-    python -m linear_attention_recurrent_decode_amd.build
+    python -m linear_attention_recurrent_decode_amd.build [--kernarg-preload N]
+
+--kernarg-preload sets how many leading kernel arguments arrive in SGPRs at
+wave launch (default 8; 0 turns preloading off, which is slower but is what
+a kernel-tracing profiler's dispatch path sees: see the notes on tracing).
 """
 from __future__ import annotations
 
+import argparse
 import os
 import shutil
 import subprocess
@@ -64,14 +69,21 @@ def _run(cmd, what):
     return msgs
 
 
-def build(verbose: bool = False) -> str:
+KERNARG_PRELOAD = 8
+
+
+def build(verbose: bool = False, kernarg_preload: int = KERNARG_PRELOAD) -> str:
     """Compile libkda.so next to this file (always recompiles)."""
+    if not 0 <= kernarg_preload <= 16:
+        raise ValueError("kernarg_preload must be in 0..16")
+    flags = [f"-amdgpu-kernarg-preload-count={kernarg_preload}" if f.startswith("-amdgpu-kernarg-preload-count=")
+             else f for f in HIPCC_FLAGS]
     with tempfile.TemporaryDirectory(prefix="kda_build_") as tmp:
         host_o = os.path.join(tmp, "kda_host.o")
         dev_o = os.path.join(tmp, "kda_decode.o")
         msgs = _run([host_cxx(), *HOST_CXX_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", HOST_SRC, "-o", host_o],
                     "host layer")
-        msgs += _run([hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", SRC, "-o", dev_o], "kernel layer")
+        msgs += _run([hipcc(), *flags, "-I", INCLUDE, "-I", CSRC, "-c", SRC, "-o", dev_o], "kernel layer")
         tmp_lib = LIB + ".tmp"
         msgs += _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp_lib, dev_o, host_o], "link")
     if verbose and msgs:
@@ -81,4 +93,7 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    ap = argparse.ArgumentParser(description="build libkda.so (gfx950) in place")
+    ap.add_argument("--kernarg-preload", type=int, default=KERNARG_PRELOAD,
+                    help="leading kernel arguments preloaded into SGPRs (0: off)")
+    print(build(verbose=True, kernarg_preload=ap.parse_args().kernarg_preload))
