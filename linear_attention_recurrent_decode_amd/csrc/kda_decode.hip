@@ -1,4 +1,6 @@
-// kda_decode.hip -- gfx950 kernels and the C ABI of libkda.so (declared in kda.h).
+// kda_decode.hip -- the kernel layer of libkda.so: the gfx950 kernels and
+// their launches, reached from the host layer (kda_host.cpp: the C ABI of
+// kda.h, argument validation, the launch plan) through kda_launch.h.
 //
 // Recurrent KDA decode is a bandwidth-bound stream over the state pool: per
 // (request, value head) and call, a 64 KiB fp32 state tile is read once and
@@ -17,9 +19,11 @@
 // (request, value head, value tile).  Columns never interact in the
 // recurrence, so the tiling cannot change a single result bit: every wave runs
 // the same per-column arithmetic in the same order whatever the tile width.
-// Calls with several tokens per request or few tiles take a second layout
-// of the same arithmetic, with the same result bits (16-column waves, one
-// column of 32 key rows per lane; see kda_decode_q_kernel).
+// Calls with several tokens per request or few tiles take two more layouts
+// of the same arithmetic, with the same result bits: 16-column waves, one
+// column of 32 key rows per lane (kda_decode_q_kernel), and split-key
+// 16-column waves, one column of 16 key rows per lane, two waves per column
+// set (kda_decode_split_kernel).
 //
 // Per token (vLLM PR 57585 names the op; the gated delta rule of Kimi Delta
 // Attention is the recurrence):
