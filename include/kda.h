@@ -119,6 +119,19 @@ typedef enum kda_status {
 #define KDA_ORDER_TILE_FIRST 1
 #define KDA_ORDER_INPUTS_FIRST 2
 
+/* flags: bits 18..19 force the placement of a call's workgroups over the
+ * chip's 8 XCDs (each with its own L2), for measuring one placement against
+ * the other.  0 = the library's: consecutive workgroups hold one head's
+ * value tiles, so the hardware's round-robin hand-out spreads a head over
+ * several XCDs.  KDA_PLACEMENT_HEAD_XCD: the value tiles of a head run on one
+ * XCD, which then fetches the head's token inputs once instead of once per
+ * tile (split-key waves with two or more tokens per request and an fp32 pool
+ * only; elsewhere KDA_ERR_UNSUPPORTED).  Results are bitwise the same. */
+#define KDA_FLAG_PLACEMENT_SHIFT 18u
+#define KDA_FLAG_PLACEMENT_MASK (3u << KDA_FLAG_PLACEMENT_SHIFT)
+#define KDA_FLAG_PLACEMENT(code) (((uint32_t)(code) & 3u) << KDA_FLAG_PLACEMENT_SHIFT)
+#define KDA_PLACEMENT_HEAD_XCD 1
+
 /*
  * One decode call.  Token t of the call is row t of every per-token tensor.
  *

@@ -27,7 +27,7 @@ __all__ = [
     "decode_args", "KDA_FLAG_VTILE", "KDA_FLAG_KERNEL", "KDA_FLAG_ORDER", "KDA_FLAG_STATE_BF16",
     "KDA_FLAG_VALIDATE", "KDA_DEVICE_STATUS",
     "KDA_KERNEL_WIDE", "KDA_KERNEL_QUARTER2", "KDA_KERNEL_QUARTER4", "KDA_KERNEL_QUARTER8", "KDA_KERNEL_SPLIT",
-    "KDA_ORDER_TILE_FIRST", "KDA_ORDER_INPUTS_FIRST",
+    "KDA_ORDER_TILE_FIRST", "KDA_ORDER_INPUTS_FIRST", "KDA_FLAG_PLACEMENT", "KDA_PLACEMENT_HEAD_XCD",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -44,9 +44,11 @@ KDA_DEVICE_STATUS = {0: "KDA_DEVICE_OK", 1: "KDA_DEVICE_ERR_SLOT_RANGE", 2: "KDA
 KDA_FLAG_VTILE_SHIFT = 8
 KDA_FLAG_KERNEL_SHIFT = 12
 KDA_FLAG_ORDER_SHIFT = 16
+KDA_FLAG_PLACEMENT_SHIFT = 18
 KDA_KERNEL_WIDE, KDA_KERNEL_QUARTER2, KDA_KERNEL_QUARTER4, KDA_KERNEL_QUARTER8 = 1, 2, 3, 4
 KDA_KERNEL_SPLIT = 5
 KDA_ORDER_TILE_FIRST, KDA_ORDER_INPUTS_FIRST = 1, 2
+KDA_PLACEMENT_HEAD_XCD = 1
 
 
 def KDA_FLAG_VTILE(width: int) -> int:
@@ -63,6 +65,11 @@ def KDA_FLAG_KERNEL(code: int) -> int:
 def KDA_FLAG_ORDER(code: int) -> int:
     """Flag bits forcing a load order (KDA_ORDER_TILE_FIRST or KDA_ORDER_INPUTS_FIRST)."""
     return (int(code) & 3) << KDA_FLAG_ORDER_SHIFT
+
+
+def KDA_FLAG_PLACEMENT(code: int) -> int:
+    """Flag bits forcing a workgroup placement (KDA_PLACEMENT_HEAD_XCD)."""
+    return (int(code) & 3) << KDA_FLAG_PLACEMENT_SHIFT
 
 
 class KdaError(RuntimeError):

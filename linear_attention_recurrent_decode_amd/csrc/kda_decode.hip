@@ -1315,10 +1315,20 @@ __device__ __forceinline__ void advance_split(float (&s)[S_ROWS], const PairPre 
 // as in kda_decode_q_kernel (here with rows 16 apart padded to other
 // banks), followed there by the exchange buffers; it goes back the same
 // way, or with an fp32 pool and the tile first straight from the lanes.
-template <int PF, bool RAWG, bool BF16S, bool EARLY>
+//
+// Workgroup placement.  The hardware hands workgroups to the 8 XCDs in turn,
+// so by default (block = unit * 4 + value tile) a head's 4 value tiles run on
+// 4 XCDs, each of which fetches the head's token inputs into its own L2.
+// With HEAD_XCD the blocks of each group of 32 map to 8 heads x 4 tiles so
+// that blocks b, b + 8, b + 16, b + 24 (one XCD) hold one head's tiles; the
+// last group holds the remaining n < 8 heads.  Same results; measured slower
+// (the re-fetched input rows come from the memory-side cache, not HBM), so
+// the library never picks it and KDA_FLAG_PLACEMENT forces it.
+template <int PF, bool RAWG, bool BF16S, bool EARLY, bool HEAD_XCD = false>
 __global__ __launch_bounds__(256) void kda_decode_split_kernel(const int32_t *slot_idx, void *state,
                                                                int64_t slot_stride, int64_t num_slots, int32_t HV,
-                                                               int32_t T, const int32_t *status, DecodeParams p)
+                                                               int32_t T, const int32_t *status, int32_t units,
+                                                               DecodeParams p)
 {
     static_assert(PF >= 1 && PF <= 4, "up to 4 tokens' inputs ahead");
     static_assert(!EARLY || PF >= 2, "one-token calls load the tile first");
@@ -1327,8 +1337,25 @@ __global__ __launch_bounds__(256) void kda_decode_split_kernel(const int32_t *sl
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t block = blockIdx.x;
-    const int vt = (int)(block % NVT);
-    const int64_t unit = block / NVT;
+    int vt;
+    int64_t unit;
+    if constexpr (HEAD_XCD) {
+        static_assert(NVT == 4, "a group of 32 blocks is 8 heads x 4 value tiles");
+        const int64_t group = block >> 5;
+        const int r = (int)(block & 31);
+        const int64_t heads = (int64_t)units - group * 8;   // heads in this group: 8, or fewer in the last
+        if (heads >= 8) {
+            unit = group * 8 + (r & 7);
+            vt = r >> 3;
+        } else {
+            const int n = (int)heads;
+            unit = group * 8 + r % n;
+            vt = r / n;
+        }
+    } else {
+        vt = (int)(block % NVT);
+        unit = block / NVT;
+    }
     const int64_t req = unit / HV;
     const int hv = (int)(unit - req * HV);
 
@@ -1611,9 +1638,8 @@ DecodeParams make_params(const kda_internal::DecodeCall &c)
     return p;
 }
 
-// One launch of `kernel` over `blocks` workgroups: the preloaded scalars,
-// then the parameter block.  The split-key kernel takes no cu_seqlens.
-template <bool WITH_CU>
+// One launch of `kernel` (32-column or 16-column waves) over `blocks`
+// workgroups: the preloaded scalars, then the parameter block.
 kda_status launch(const void *kernel, const DecodeParams &p, int64_t blocks, int threads, size_t lds,
                   hipStream_t stream)
 {
@@ -1625,10 +1651,8 @@ kda_status launch(const void *kernel, const DecodeParams &p, int64_t blocks, int
     int32_t HV = p.HV, T = p.T;
     const int32_t *status = p.status;
     DecodeParams params = p;
-    void *with_cu[] = {&slot_idx, &cu_seqlens, &state, &slot_stride, &num_slots, &HV, &T, &status, &params};
-    void *without_cu[] = {&slot_idx, &state, &slot_stride, &num_slots, &HV, &T, &status, &params};
-    const hipError_t e = hipLaunchKernel(kernel, dim3((uint32_t)blocks), dim3(threads), WITH_CU ? with_cu : without_cu,
-                                         lds, stream);
+    void *args[] = {&slot_idx, &cu_seqlens, &state, &slot_stride, &num_slots, &HV, &T, &status, &params};
+    const hipError_t e = hipLaunchKernel(kernel, dim3((uint32_t)blocks), dim3(threads), args, lds, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
@@ -1645,7 +1669,7 @@ kda_status launch_wide(const DecodeParams &p, int64_t units, int body, hipStream
         if (body == kda_internal::BODY_LOOP)
             fn = reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_LOOP, BF16S, RAWG>);
     }
-    return launch<true>(fn, p, units * (4 / NW), 64 * NW, 0, s);
+    return launch(fn, p, units * (4 / NW), 64 * NW, 0, s);
 }
 
 template <bool RAWG, bool BF16S>
@@ -1670,7 +1694,7 @@ kda_status launch_quarter(const DecodeParams &p, int64_t units, bool early, hipS
         if (early)
             fn = reinterpret_cast<const void *>(&kda_decode_q_kernel<NQ, PF, NORM, RAWG, BF16S, true>);
     }
-    return launch<true>(fn, p, units * (8 / NQ), 64 * NQ, q_lds_bytes(NQ), s);
+    return launch(fn, p, units * (8 / NQ), 64 * NQ, q_lds_bytes(NQ), s);
 }
 
 template <int NQ, bool NORM, bool RAWG, bool BF16S>
@@ -1705,26 +1729,42 @@ kda_status dispatch_quarter(const DecodeParams &p, int64_t units, const kda_inte
 
 // ---- split-key waves (step calls only)
 template <int PF, bool RAWG, bool BF16S>
-kda_status launch_split(const DecodeParams &p, int64_t units, bool early, hipStream_t s)
+kda_status launch_split(const DecodeParams &p, int64_t units, bool early, bool head_xcd, hipStream_t s)
 {
     const void *fn = reinterpret_cast<const void *>(&kda_decode_split_kernel<PF, RAWG, BF16S, false>);
     if constexpr (PF >= 2 && !BF16S) {
         if (early)
             fn = reinterpret_cast<const void *>(&kda_decode_split_kernel<PF, RAWG, BF16S, true>);
+        if (head_xcd)
+            fn = early ? reinterpret_cast<const void *>(&kda_decode_split_kernel<PF, RAWG, BF16S, true, true>)
+                       : reinterpret_cast<const void *>(&kda_decode_split_kernel<PF, RAWG, BF16S, false, true>);
     }
-    return launch<false>(fn, p, units * (VD / S_COLS), 256, split_lds_bytes(), s);
+    const int64_t blocks = units * (VD / S_COLS);
+    if (blocks > 0x7FFFFFFF)
+        return KDA_ERR_SHAPE;
+    // the preloaded scalars (no cu_seqlens: step calls only), the head count,
+    // then the parameter block
+    const int32_t *slot_idx = p.slot_idx;
+    void *state = p.state;
+    int64_t slot_stride = p.slot_stride, num_slots = p.num_slots;
+    int32_t HV = p.HV, T = p.T, units32 = (int32_t)units;
+    const int32_t *status = p.status;
+    DecodeParams params = p;
+    void *args[] = {&slot_idx, &state, &slot_stride, &num_slots, &HV, &T, &status, &units32, &params};
+    const hipError_t e = hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(256), args, split_lds_bytes(), s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 template <bool RAWG, bool BF16S>
-kda_status dispatch_split(const DecodeParams &p, int64_t units, bool early, hipStream_t s)
+kda_status dispatch_split(const DecodeParams &p, int64_t units, bool early, bool head_xcd, hipStream_t s)
 {
-    if (p.cu_seqlens)
+    if (p.cu_seqlens || (head_xcd && (p.T < 2 || BF16S)))
         return KDA_ERR_UNSUPPORTED;
     switch (p.T) {
-    case 1: return launch_split<1, RAWG, BF16S>(p, units, false, s);
-    case 2: return launch_split<2, RAWG, BF16S>(p, units, early, s);
-    case 3: return launch_split<3, RAWG, BF16S>(p, units, early, s);
-    default: return launch_split<4, RAWG, BF16S>(p, units, early, s);
+    case 1: return launch_split<1, RAWG, BF16S>(p, units, false, false, s);
+    case 2: return launch_split<2, RAWG, BF16S>(p, units, early, head_xcd, s);
+    case 3: return launch_split<3, RAWG, BF16S>(p, units, early, head_xcd, s);
+    default: return launch_split<4, RAWG, BF16S>(p, units, early, head_xcd, s);
     }
 }
 
@@ -1734,7 +1774,7 @@ kda_status dispatch(const DecodeParams &p, int64_t units, const kda_internal::Pl
     switch (pl.kernel) {
     case kda_internal::KERNEL_WIDE: return dispatch_wide<RAWG, BF16S>(p, units, pl, norm, s);
     case kda_internal::KERNEL_QUARTER: return dispatch_quarter<RAWG, BF16S>(p, units, pl, norm, s);
-    case kda_internal::KERNEL_SPLIT: return norm ? KDA_ERR_UNSUPPORTED : dispatch_split<RAWG, BF16S>(p, units, pl.early, s);
+    case kda_internal::KERNEL_SPLIT: return norm ? KDA_ERR_UNSUPPORTED : dispatch_split<RAWG, BF16S>(p, units, pl.early, pl.head_xcd, s);
     }
     return KDA_ERR_UNSUPPORTED;
 }

@@ -48,7 +48,7 @@ int vtile_from_flags(uint32_t flags)
 }
 
 constexpr uint32_t KNOWN_FLAGS = KDA_FLAG_STATE_BF16 | KDA_FLAG_VALIDATE | KDA_FLAG_VTILE_MASK |
-                                 KDA_FLAG_KERNEL_MASK | KDA_FLAG_ORDER_MASK;
+                                 KDA_FLAG_KERNEL_MASK | KDA_FLAG_ORDER_MASK | KDA_FLAG_PLACEMENT_MASK;
 
 // Sizes, null pointers, alignment and overlap of a decode call (the rules of
 // kda.h, "One decode call").
@@ -303,12 +303,15 @@ kda_status call_plan(const CallShape &c, uint32_t flags, Plan &out)
     const int vtile = vtile_from_flags(flags);
     int code = (int)((flags & KDA_FLAG_KERNEL_MASK) >> KDA_FLAG_KERNEL_SHIFT);
     const int order = (int)((flags & KDA_FLAG_ORDER_MASK) >> KDA_FLAG_ORDER_SHIFT);
+    const int placement = (int)((flags & KDA_FLAG_PLACEMENT_MASK) >> KDA_FLAG_PLACEMENT_SHIFT);
     if (code == 0 && vtile)
         code = KDA_KERNEL_WIDE;
     if (vtile && code != KDA_KERNEL_WIDE)
         return KDA_ERR_UNSUPPORTED;
+    if (placement > KDA_PLACEMENT_HEAD_XCD)
+        return KDA_ERR_UNSUPPORTED;
     Plan p = library_plan(c);
-    if (code == 0 && order == 0) {
+    if (code == 0 && order == 0 && placement == 0) {
         out = p;
         return KDA_OK;
     }
@@ -352,6 +355,12 @@ kda_status call_plan(const CallShape &c, uint32_t flags, Plan &out)
         return KDA_ERR_UNSUPPORTED;
     if (p.early && (c.bf16 || c.T == 1))
         return KDA_ERR_UNSUPPORTED;
+    if (placement) {
+        // the head-per-XCD order exists for the multi-token fp32 split-key kernels
+        if (p.kernel != KERNEL_SPLIT || c.T < 2 || c.bf16)
+            return KDA_ERR_UNSUPPORTED;
+        p.head_xcd = true;
+    }
     out = p;
     return KDA_OK;
 }

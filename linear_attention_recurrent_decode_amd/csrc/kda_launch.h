@@ -34,6 +34,7 @@ struct Plan {
                              // SPLIT: 4 (two column waves x two row halves)
     int32_t body = BODY_PEELED;   // WIDE only
     bool early = false;      // QUARTER, SPLIT: the first token's inputs before the state tile
+    bool head_xcd = false;   // SPLIT: a head's value tiles on one XCD (KDA_PLACEMENT_HEAD_XCD)
 
     // value columns one workgroup holds
     int32_t columns() const

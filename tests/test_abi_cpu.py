@@ -321,7 +321,7 @@ def test_aliasing():
 
 def test_unknown_flags():
     for flags in (4, 1 << 10, 1 << 20, 1 << 31, kda.KDA_FLAG_KERNEL(6), kda.KDA_FLAG_KERNEL(15),
-                  kda.KDA_FLAG_ORDER(3)):
+                  kda.KDA_FLAG_ORDER(3), kda.KDA_FLAG_PLACEMENT(2), kda.KDA_FLAG_PLACEMENT(3)):
         a, _ = _valid_args()
         assert _step(a, T=2, flags=flags) == UNSUP, hex(flags)
     a, _ = _valid_args()
@@ -335,7 +335,8 @@ def _norm_args():
     return a, cu
 
 
-K, O = kda.KDA_FLAG_KERNEL, kda.KDA_FLAG_ORDER
+K, O, P = kda.KDA_FLAG_KERNEL, kda.KDA_FLAG_ORDER, kda.KDA_FLAG_PLACEMENT
+XCD = P(kda.KDA_PLACEMENT_HEAD_XCD)
 
 
 @pytest.mark.parametrize("make,T,flags,expect", [
@@ -348,6 +349,9 @@ K, O = kda.KDA_FLAG_KERNEL, kda.KDA_FLAG_ORDER
     (_valid_args, 2, O(kda.KDA_ORDER_INPUTS_FIRST), DEVICE),    # the library's kernel, forced order
     (_norm_args, 2, K(kda.KDA_KERNEL_QUARTER8), DEVICE),
     (_norm_args, 1, K(kda.KDA_KERNEL_WIDE), DEVICE),
+    (_valid_args, 4, K(kda.KDA_KERNEL_SPLIT) | XCD, DEVICE),   # a head's value tiles on one XCD
+    (_valid_args, 2, XCD, DEVICE),                             # the library's split-key kernel, placed so
+    (_valid_args, 3, K(kda.KDA_KERNEL_SPLIT) | O(kda.KDA_ORDER_INPUTS_FIRST) | XCD, DEVICE),
     # combinations no kernel provides
     (_valid_args, 2, K(kda.KDA_KERNEL_QUARTER4) | kda.KDA_FLAG_VTILE(64), UNSUP),   # a width is for WIDE only
     (_norm_args, 2, K(kda.KDA_KERNEL_QUARTER4), UNSUP),         # the norm: 128 columns per workgroup
@@ -357,6 +361,9 @@ K, O = kda.KDA_FLAG_KERNEL, kda.KDA_FLAG_ORDER
     (_valid_args, 1, K(kda.KDA_KERNEL_WIDE) | O(kda.KDA_ORDER_TILE_FIRST), UNSUP),   # the body fixes the order
     (_valid_args, 1, K(kda.KDA_KERNEL_SPLIT) | O(kda.KDA_ORDER_INPUTS_FIRST), UNSUP),   # one token: tile first
     (_valid_args, 2, K(kda.KDA_KERNEL_SPLIT) | O(kda.KDA_ORDER_INPUTS_FIRST) | kda.KDA_FLAG_STATE_BF16, UNSUP),
+    (_valid_args, 1, K(kda.KDA_KERNEL_SPLIT) | XCD, UNSUP),    # placement: multi-token split-key calls only
+    (_valid_args, 2, K(kda.KDA_KERNEL_QUARTER4) | XCD, UNSUP),
+    (_valid_args, 2, K(kda.KDA_KERNEL_SPLIT) | XCD | kda.KDA_FLAG_STATE_BF16, UNSUP),
 ])
 def test_forced_kernels(make, T, flags, expect):
     a, _ = make()
@@ -367,6 +374,7 @@ def test_forced_kernels(make, T, flags, expect):
 def test_forced_split_kernel_refuses_packed_calls():
     a, cu = _valid_args()
     assert _packed(a, cu, 4, flags=K(kda.KDA_KERNEL_SPLIT)) == UNSUP
+    assert _packed(a, cu, 4, flags=XCD) == UNSUP
     assert _packed(a, cu, 4, flags=K(kda.KDA_KERNEL_QUARTER4)) == DEVICE
 
 

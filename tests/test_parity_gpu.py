@@ -898,6 +898,35 @@ def test_eight_quarter_waves_match_wide_waves_bitwise(case):
         assert torch.equal(o, results[0][0]) and torch.equal(st, results[0][1]) and torch.equal(it, results[0][2])
 
 
+@pytest.mark.parametrize("case", [(1, 8, 8, 4), (8, 8, 8, 4), (5, 2, 6, 3), (7, 1, 3, 2), (33, 8, 8, 2),
+                                  (11, 4, 12, 4), (3, 1, 5, 6)])
+def test_head_per_xcd_placement_bitwise(case):
+    """Split-key calls with a head's value tiles placed on one XCD
+    (KDA_PLACEMENT_HEAD_XCD: groups of 8 heads x 4 tiles, a partial last
+    group when the head count is not a multiple of 8) against the default
+    placement, bit for bit with per-token states, both load orders, with
+    and without the fused gate; the placed call against the oracle."""
+    N, H, HV, T = case
+    split = kda.KDA_FLAG_KERNEL(kda.KDA_KERNEL_SPLIT)
+    xcd = kda.KDA_FLAG_PLACEMENT(kda.KDA_PLACEMENT_HEAD_XCD)
+    for raw in (False, True):
+        p = ki.make_problem("xcd", 900 + N, N=N, H=H, HV=HV, K=128, V=128, num_slots=N + 5, T=T, n_pad=N // 5,
+                            raw_gates=raw)
+        for order in (kda.KDA_ORDER_TILE_FIRST, kda.KDA_ORDER_INPUTS_FIRST):
+            results = []
+            for placement in (0, xcd):
+                d = _fresh(p)
+                inter = guarded_full(d, (p.tokens, p.HV, p.K, p.V), 1232.0, torch.float32)
+                run_gpu(d, flags=split | kda.KDA_FLAG_ORDER(order) | placement, inter_state=inter)
+                torch.cuda.synchronize()
+                assert_guards(d)
+                if placement and order == kda.KDA_ORDER_INPUTS_FIRST:
+                    _log(f"head per XCD {case} raw={raw}", compare(d, *run_oracle(p)))
+                results.append((d.out.view(torch.int16).clone(), d.state.clone(), inter))
+            (o0, s0, i0), (o1, s1, i1) = results
+            assert torch.equal(o0, o1) and torch.equal(s0, s1) and torch.equal(i0, i1), (case, raw, order)
+
+
 def test_quarter_waves_full_t4_sweep_match_wide_waves():
     """The T = 4 serving sweep: the library's choice against the forced
     32-column kernel, bit for bit."""
