@@ -160,11 +160,16 @@ struct CallShape {
 };
 
 // Value-tile width of the 32-column kernel from the tile count, tuned on
-// MI355X with cold caches (256 compute units):
+// MI355X with cold caches (256 compute units; A/B blocks as below):
 //   fewer tiles than compute units: 32 columns, one wave per workgroup, the
-//     most workgroups in flight for a latency-bound call;
-//   one token per request, 256 .. 1023 tiles: 64 columns;
-//   several tokens per request, or 1024 tiles and up: 128 columns.
+//     most workgroups in flight for a latency-bound call (N20/T1 5.08 vs
+//     5.63 us at 64 columns, N24/T1 5.39 vs 5.80);
+//   one token per request, 256 .. 1023 tiles: 64 columns (N32/T1 6.69 vs
+//     6.95 at 32 and 7.06 at 128, N40/T1 8.26 vs 8.62 and 11.07);
+//   two tokens per request (the kernel serves them at 513 .. 768 tiles): 64
+//     columns (N80/T2 15.10 vs 16.18, N96/T2 18.65 vs 20.16 at 128);
+//   three or more tokens, or 1024 tiles and up: 128 columns (N80/T4 18.28
+//     vs 19.37, N88/T3 16.94 vs 17.79 at 64).
 // The norm epilogue needs all 128 columns in one workgroup.
 int32_t plan_vtile(int64_t units, int32_t T, bool norm)
 {
@@ -172,7 +177,7 @@ int32_t plan_vtile(int64_t units, int32_t T, bool norm)
         return 128;
     if (units < 256)
         return 32;
-    if (T <= 1 && units < 1024)
+    if ((T <= 1 && units < 1024) || T == 2)
         return 64;
     return 128;
 }
@@ -207,9 +212,15 @@ int32_t plan_body(const CallShape &c)
 //   fp32, two or more tokens: split-key waves up to 256 tiles (N32/T4 8.46
 //     vs 8.76 on four 16-column waves), and with two or three tokens up to
 //     320 (N40/T2 8.49 vs 8.59, N40/T3 8.81 vs 8.98; N36/T4 10.03 vs 9.81
-//     the other way); four 16-column waves to 576 tiles (N65/T4 16.33 vs
-//     17.79 on the 32-column kernel, N80/T4 19.32 vs 19.02, N96/T4 23.9 vs
-//     20.3);
+//     the other way); four 16-column waves to 576 tiles, 512 with two tokens
+//     (N64/T2 12.30 vs 13.27 on the 32-column kernel, N72/T4 17.51 vs 19.70;
+//     but N72/T2 17.21 vs 14.90); the 32-column kernel to 768 (N80/T4 18.65
+//     vs 18.89, N96/T4 20.33 vs 22.33, N88/T3 16.93 vs 20.83, N96/T2 18.65
+//     vs 21.55); four 16-column waves again to 1536 (N104/T4 24.70 vs 27.70,
+//     N112/T2 24.35 vs 25.57, N104/T3 23.65 vs 25.34, N128/T2 26.84 vs
+//     29.04, N160/T4 35.67 vs 37.10 and 37.20 on eight), eight beyond
+//     (N256/T4 54.41 vs 55.37 on four and 57.45 on the 32-column kernel,
+//     N256/T2 53.22 vs 54.20);
 //   fp32, packed (1 to 4 tokens per request): four 16-column waves up to
 //     1024 tiles (N8: 5.63 vs 7.64 on the 32-column kernel, N24 7.69 vs
 //     9.28 and 8.75 on eight waves, N32 8.14 vs 9.40, N48 10.20 vs 12.48,
@@ -247,7 +258,11 @@ int32_t plan_quarter_waves(const CallShape &c)
     }
     if (c.units <= 256 || (c.T <= 3 && c.units <= 320))
         return PLAN_SPLIT;
-    return c.units <= 576 ? 4 : 0;
+    if (c.units <= (c.T == 2 ? 512 : 576))
+        return 4;
+    if (c.units <= 768)
+        return 0;
+    return c.units <= 1536 ? 4 : 8;
 }
 
 // The load order of a 16-column-wave launch: the first token's inputs

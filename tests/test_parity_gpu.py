@@ -768,8 +768,42 @@ QUARTER_CASES = [
     (41, 8, 8, 2, True, QUARTER),     # 328 tiles, two tokens, fused gate, tile first
     (44, 2, 6, 5, False, QUARTER),    # 264 tiles, five tokens
     (60, 8, 8, 2, False, QUARTER),    # 480 tiles, two tokens
-    (70, 8, 8, 4, False, QUARTER),    # 560 tiles, four tokens, tile first
+    (70, 8, 8, 4, False, QUARTER),    # 560 tiles, four tokens, inputs first
 ]
+
+
+LARGE_MULTI_TOKEN_CASES = [
+    # (N, T, fused gate, columns per workgroup, layout): fp32 step calls past
+    # the split-key range, H = HV = 8
+    (72, 2, False, 64, kda.KDA_LAYOUT_WIDE),      # 576 tiles, two tokens: 32-column waves, 64 columns
+    (90, 3, True, 128, kda.KDA_LAYOUT_WIDE),      # 720 tiles, three tokens: 32-column waves, 128 columns
+    (100, 2, False, 64, QUARTER),                 # 800 tiles: four 16-column waves again, tile first
+    (100, 4, True, 64, QUARTER),                  # 800 tiles, four tokens: inputs first
+    (200, 2, False, 128, QUARTER),                # 1600 tiles: eight 16-column waves, inputs first
+]
+
+
+@pytest.mark.parametrize("case", LARGE_MULTI_TOKEN_CASES)
+def test_large_multi_token_calls(case):
+    """The plan's kernels for many tiles and several tokens per request
+    against the oracle, and bit for bit against the 32-column kernel at a
+    forced width and four forced 16-column waves."""
+    N, T, raw, width, layout = case
+    p = ki.make_problem("large", 500 + N, N=N, H=8, HV=8, K=128, V=128, num_slots=N + 11, T=T, n_pad=N // 10,
+                        raw_gates=raw)
+    assert kda.kda_decode_plan(N * 8, T, False, raw_gate=raw) == width
+    assert kda.kda_decode_plan(N * 8, T, False, raw_gate=raw, layout=True) == layout
+    results = []
+    for flags in (0, kda.KDA_FLAG_VTILE(128), kda.KDA_FLAG_KERNEL(kda.KDA_KERNEL_QUARTER4)):
+        d = _fresh(p)
+        run_gpu(d, flags=flags)
+        torch.cuda.synchronize()
+        assert_guards(d)
+        if flags == 0:
+            _log(f"large multi-token {case}", compare(d, *run_oracle(p)))
+        results.append((d.out.view(torch.int16).clone(), d.state.clone()))
+    for o, st in results[1:]:
+        assert torch.equal(o, results[0][0]) and torch.equal(st, results[0][1]), case
 
 
 @pytest.mark.parametrize("case", QUARTER_CASES)
