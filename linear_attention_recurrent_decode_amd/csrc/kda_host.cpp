@@ -204,10 +204,12 @@ int32_t plan_body(const CallShape &c)
 // +-0.2 to 0.5%):
 //   fp32, one token: split-key waves up to 128 tiles (N16: 4.54 vs 4.75 on
 //     the 32-column kernel), the 32-column kernel from there (N20 5.12 vs
-//     5.21, N24 5.44 vs 5.93) to 384 tiles (N48 9.67 vs 9.95 on eight
-//     16-column waves), eight 16-column waves from 400 (N50 10.12 vs 11.34,
-//     N56 10.77 vs 12.50, N64 11.91 vs 12.86); with the fused gate two
-//     16-column waves up to 64 tiles (N8 3.80 vs 3.91 split-key, 4.06
+//     5.21, N24 5.42 vs 5.96 on four 16-column waves) to 256 tiles (N32 6.53
+//     vs 7.12), four 16-column waves to 384 (N33 7.38 vs 7.67, N36 7.49 vs
+//     7.92, N48 9.13 vs 9.62 and 9.95 on eight; fused gate N33 7.60 vs 7.98,
+//     N48 9.20 vs 9.70), eight 16-column waves beyond (N50 10.12 vs 11.34,
+//     N52 10.32 vs 12.20 on four, N64 11.91 vs 12.86); with the fused gate
+//     two 16-column waves up to 64 tiles (N8 3.80 vs 3.91 split-key, 4.06
 //     32-column; N9 4.24 on the 32-column kernel vs 4.36);
 //   fp32, two or more tokens: split-key waves up to 256 tiles (N32/T4 8.46
 //     vs 8.76 on four 16-column waves), and with two or three tokens up to
@@ -252,6 +254,8 @@ int32_t plan_quarter_waves(const CallShape &c)
     if (c.T == 1) {
         if (c.units > 384)
             return 8;
+        if (c.units > 256)
+            return 4;
         if (c.raw)
             return c.units <= 64 ? 2 : 0;
         return c.units <= 128 ? PLAN_SPLIT : 0;

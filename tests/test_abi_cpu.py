@@ -68,14 +68,16 @@ def test_status_strings_and_plan():
             assert kda.kda_decode_plan(units, T, True) == 128
     # the launch table of fp32 step calls without the norm: with one token,
     # split-key 16-column waves (32 columns) up to 128 tiles, 32-column waves
-    # (32 or 64 columns) to 384, eight 16-column waves (128 columns) beyond;
+    # (32 or 64 columns) to 256, four 16-column waves (64 columns) to 384,
+    # eight (128 columns) beyond;
     # with two or more tokens split-key waves up to 256 tiles (320 with two
     # or three tokens), four 16-column waves (64 columns) to 576 (512 with
     # two tokens), 32-column waves to 768 (64 columns with two tokens, else
     # 128), four 16-column waves to 1536, eight beyond
     W, Q, S = kda.KDA_LAYOUT_WIDE, kda.KDA_LAYOUT_QUARTER, kda.KDA_LAYOUT_SPLIT
     expect = {(1, 1): (32, S), (8, 1): (32, S), (64, 1): (32, S), (128, 1): (32, S), (129, 1): (32, W),
-              (192, 1): (32, W), (255, 1): (32, W), (256, 1): (64, W), (384, 1): (64, W), (385, 1): (128, Q),
+              (192, 1): (32, W), (255, 1): (32, W), (256, 1): (64, W), (257, 1): (64, Q), (384, 1): (64, Q),
+              (385, 1): (128, Q),
               (512, 1): (128, Q), (1024, 1): (128, Q),
               (128, 2): (32, S), (256, 2): (32, S), (320, 2): (32, S), (321, 2): (64, Q), (512, 2): (64, Q),
               (513, 2): (64, W), (576, 2): (64, W), (768, 2): (64, W), (769, 2): (64, Q), (1536, 2): (64, Q),
@@ -91,7 +93,8 @@ def test_status_strings_and_plan():
     # the fused gate activation: one-token calls take two 16-column waves
     # (32 columns) up to 64 tiles instead of the split-key waves; the rest of
     # the table is the same
-    raw = {(1, 1): (32, Q), (64, 1): (32, Q), (65, 1): (32, W), (128, 1): (32, W), (384, 1): (64, W),
+    raw = {(1, 1): (32, Q), (64, 1): (32, Q), (65, 1): (32, W), (128, 1): (32, W), (256, 1): (64, W),
+           (300, 1): (64, Q), (384, 1): (64, Q),
            (385, 1): (128, Q), (512, 1): (128, Q), (8, 4): (32, S), (192, 2): (32, S), (300, 4): (64, Q)}
     for (units, T), (width, layout) in raw.items():
         assert kda.kda_decode_plan(units, T, raw_gate=True) == width, (units, T)

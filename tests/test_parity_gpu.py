@@ -769,6 +769,9 @@ QUARTER_CASES = [
     (44, 2, 6, 5, False, QUARTER),    # 264 tiles, five tokens
     (60, 8, 8, 2, False, QUARTER),    # 480 tiles, two tokens
     (70, 8, 8, 4, False, QUARTER),    # 560 tiles, four tokens, inputs first
+    (36, 8, 8, 1, False, QUARTER),    # one token, 288 tiles: four waves per workgroup
+    (48, 2, 8, 1, False, QUARTER),    # one token, 384 tiles: the last size on four waves
+    (34, 4, 8, 1, True, QUARTER),     # one token, 272 tiles, fused gate: four waves
 ]
 
 
@@ -817,7 +820,7 @@ def test_quarter_waves_match_wide_waves_bitwise(case):
     p = ki.make_problem("quarter", 300 + N, N=N, H=H, HV=HV, K=128, V=128, num_slots=2 * N + 3, T=T,
                         n_pad=N // 4, raw_gates=raw)
     assert kda.kda_decode_plan(N * HV, T, False, layout=True, raw_gate=raw) == layout
-    two_waves = raw and T == 1                  # 32 columns per workgroup
+    two_waves = raw and T == 1 and N * HV <= 64  # 32 columns per workgroup
     assert kda.kda_decode_plan(N * HV, T, False, raw_gate=raw) == (64 if layout == QUARTER and not two_waves else 32)
     results = []
     for flags in (0, kda.KDA_FLAG_VTILE(32), kda.KDA_FLAG_VTILE(64), kda.KDA_FLAG_VTILE(128)):
