@@ -669,11 +669,11 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t block = blockIdx.x;
-    const int vt = (int)(block % NVT);
-    const int64_t unit = block / NVT;
-    const int64_t req = unit / HV;
-    const int hv = (int)(unit - req * HV);
+    // grid: x = value head x value tile, y = request (no division on the way
+    // to the slot index)
+    const int vt = (int)(blockIdx.x % NVT);
+    const int hv = (int)(blockIdx.x / NVT);
+    const int64_t req = blockIdx.y;
 
     // slot gather: padding rows and slots outside the pool are skipped; with
     // validation, every block stops here unless the metadata check passed
@@ -1121,11 +1121,9 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t block = blockIdx.x;
-    const int vt = (int)(block % NVT);
-    const int64_t unit = block / NVT;
-    const int64_t req = unit / HV;
-    const int hv = (int)(unit - req * HV);
+    const int vt = (int)(blockIdx.x % NVT);   // grid: x = value head x value tile, y = request
+    const int hv = (int)(blockIdx.x / NVT);
+    const int64_t req = blockIdx.y;
 
     const int64_t slot = slot_idx[req];
     if constexpr (EARLY)
@@ -1316,9 +1314,10 @@ __device__ __forceinline__ void advance_split(float (&s)[S_ROWS], const PairPre 
 // banks), followed there by the exchange buffers; it goes back the same
 // way, or with an fp32 pool and the tile first straight from the lanes.
 //
-// Workgroup placement.  The hardware hands workgroups to the 8 XCDs in turn,
-// so by default (block = unit * 4 + value tile) a head's 4 value tiles run on
-// 4 XCDs, each of which fetches the head's token inputs into its own L2.
+// Workgroup placement.  The hardware hands workgroups to the 8 XCDs in turn
+// (x fastest), so by default (x = value head * 4 + value tile) a head's 4
+// value tiles run on 4 XCDs, each of which fetches the head's token inputs
+// into its own L2.
 // With HEAD_XCD the blocks of each group of 32 map to 8 heads x 4 tiles so
 // that blocks b, b + 8, b + 16, b + 24 (one XCD) hold one head's tiles; the
 // last group holds the remaining n < 8 heads.  Same results; measured slower
@@ -1336,14 +1335,16 @@ __global__ __launch_bounds__(256) void kda_decode_split_kernel(const int32_t *sl
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t block = blockIdx.x;
-    int vt;
-    int64_t unit;
+    // grid: x = value head x value tile, y = request
+    int vt, hv;
+    int64_t req;
     if constexpr (HEAD_XCD) {
         static_assert(NVT == 4, "a group of 32 blocks is 8 heads x 4 value tiles");
+        const int64_t block = (int64_t)blockIdx.y * (HV * NVT) + blockIdx.x;   // the order of hand-out
         const int64_t group = block >> 5;
         const int r = (int)(block & 31);
         const int64_t heads = (int64_t)units - group * 8;   // heads in this group: 8, or fewer in the last
+        int64_t unit;
         if (heads >= 8) {
             unit = group * 8 + (r & 7);
             vt = r >> 3;
@@ -1352,12 +1353,13 @@ __global__ __launch_bounds__(256) void kda_decode_split_kernel(const int32_t *sl
             unit = group * 8 + r % n;
             vt = r / n;
         }
+        req = unit / HV;
+        hv = (int)(unit - req * HV);
     } else {
-        vt = (int)(block % NVT);
-        unit = block / NVT;
+        vt = (int)(blockIdx.x % NVT);
+        hv = (int)(blockIdx.x / NVT);
+        req = blockIdx.y;
     }
-    const int64_t req = unit / HV;
-    const int hv = (int)(unit - req * HV);
 
     const int64_t slot = slot_idx[req];
     if constexpr (EARLY)
@@ -1638,22 +1640,65 @@ DecodeParams make_params(const kda_internal::DecodeCall &c)
     return p;
 }
 
-// One launch of `kernel` (32-column or 16-column waves) over `blocks`
-// workgroups: the preloaded scalars, then the parameter block.
-kda_status launch(const void *kernel, const DecodeParams &p, int64_t blocks, int threads, size_t lds,
-                  hipStream_t stream)
+// The grid of a decode launch: x = value head x value tile, y = request.  A
+// call with more requests than the y dimension holds is launched in ranges
+// of requests, each as a call of its own.
+constexpr int64_t MAX_REQUESTS_PER_LAUNCH = 65535;
+
+// The parameter block of the requests from r0 on: the slot indices (and
+// cu_seqlens, whose token offsets stay absolute) from r0, and for step calls
+// every per-token tensor from token row r0 * T.  `elem` is the pool's element
+// size (per-token states).
+DecodeParams request_range(const DecodeParams &p, int64_t r0, int64_t elem)
 {
-    if (blocks > 0x7FFFFFFF)
-        return KDA_ERR_SHAPE;
-    const int32_t *slot_idx = p.slot_idx, *cu_seqlens = p.cu_seqlens;
-    void *state = p.state;
-    int64_t slot_stride = p.slot_stride, num_slots = p.num_slots;
-    int32_t HV = p.HV, T = p.T;
-    const int32_t *status = p.status;
-    DecodeParams params = p;
-    void *args[] = {&slot_idx, &cu_seqlens, &state, &slot_stride, &num_slots, &HV, &T, &status, &params};
-    const hipError_t e = hipLaunchKernel(kernel, dim3((uint32_t)blocks), dim3(threads), args, lds, stream);
-    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+    DecodeParams c = p;
+    c.slot_idx += r0;
+    if (p.cu_seqlens) {
+        c.cu_seqlens += r0;
+        return c;
+    }
+    const int64_t t0 = r0 * p.T;
+    if (t0 == 0)
+        return c;
+    c.q += t0 * p.q_stride;
+    c.k += t0 * p.k_stride;
+    c.v += t0 * p.v_stride;
+    if (c.g)
+        c.g += t0 * p.g_stride;
+    if (c.beta)
+        c.beta += t0 * p.beta_stride;
+    if (c.raw_gate)
+        c.raw_gate += t0 * p.raw_gate_stride;
+    if (c.raw_beta)
+        c.raw_beta += t0 * p.raw_beta_stride;
+    c.out += t0 * p.out_stride;
+    if (c.gate)
+        c.gate += t0 * p.gate_stride;
+    if (c.inter_state)
+        c.inter_state = static_cast<char *>(c.inter_state) + t0 * p.inter_stride * elem;
+    return c;
+}
+
+// The launches of `kernel` (32-column or 16-column waves) over `requests`
+// requests of `tiles` value tiles per head: the preloaded scalars, then the
+// parameter block.
+kda_status launch(const void *kernel, const DecodeParams &p, int64_t requests, int tiles, int threads, size_t lds,
+                  int64_t elem, hipStream_t stream)
+{
+    for (int64_t r0 = 0; r0 < requests; r0 += MAX_REQUESTS_PER_LAUNCH) {
+        const int64_t n = requests - r0 < MAX_REQUESTS_PER_LAUNCH ? requests - r0 : MAX_REQUESTS_PER_LAUNCH;
+        DecodeParams params = r0 ? request_range(p, r0, elem) : p;
+        const int32_t *slot_idx = params.slot_idx, *cu_seqlens = params.cu_seqlens;
+        void *state = params.state;
+        int64_t slot_stride = params.slot_stride, num_slots = params.num_slots;
+        int32_t HV = params.HV, T = params.T;
+        const int32_t *status = params.status;
+        void *args[] = {&slot_idx, &cu_seqlens, &state, &slot_stride, &num_slots, &HV, &T, &status, &params};
+        if (hipLaunchKernel(kernel, dim3((uint32_t)(HV * tiles), (uint32_t)n), dim3(threads), args, lds, stream) !=
+            hipSuccess)
+            return KDA_ERR_LAUNCH;
+    }
+    return KDA_OK;
 }
 
 // ---- the 32-column kernel: the body and the width of the plan
@@ -1669,7 +1714,7 @@ kda_status launch_wide(const DecodeParams &p, int64_t units, int body, hipStream
         if (body == kda_internal::BODY_LOOP)
             fn = reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_LOOP, BF16S, RAWG>);
     }
-    return launch(fn, p, units * (4 / NW), 64 * NW, 0, s);
+    return launch(fn, p, units / p.HV, 4 / NW, 64 * NW, 0, BF16S ? 2 : 4, s);
 }
 
 template <bool RAWG, bool BF16S>
@@ -1694,7 +1739,7 @@ kda_status launch_quarter(const DecodeParams &p, int64_t units, bool early, hipS
         if (early)
             fn = reinterpret_cast<const void *>(&kda_decode_q_kernel<NQ, PF, NORM, RAWG, BF16S, true>);
     }
-    return launch(fn, p, units * (8 / NQ), 64 * NQ, q_lds_bytes(NQ), s);
+    return launch(fn, p, units / p.HV, 8 / NQ, 64 * NQ, q_lds_bytes(NQ), BF16S ? 2 : 4, s);
 }
 
 template <int NQ, bool NORM, bool RAWG, bool BF16S>
@@ -1739,20 +1784,23 @@ kda_status launch_split(const DecodeParams &p, int64_t units, bool early, bool h
             fn = early ? reinterpret_cast<const void *>(&kda_decode_split_kernel<PF, RAWG, BF16S, true, true>)
                        : reinterpret_cast<const void *>(&kda_decode_split_kernel<PF, RAWG, BF16S, false, true>);
     }
-    const int64_t blocks = units * (VD / S_COLS);
-    if (blocks > 0x7FFFFFFF)
-        return KDA_ERR_SHAPE;
-    // the preloaded scalars (no cu_seqlens: step calls only), the head count,
-    // then the parameter block
-    const int32_t *slot_idx = p.slot_idx;
-    void *state = p.state;
-    int64_t slot_stride = p.slot_stride, num_slots = p.num_slots;
-    int32_t HV = p.HV, T = p.T, units32 = (int32_t)units;
-    const int32_t *status = p.status;
-    DecodeParams params = p;
-    void *args[] = {&slot_idx, &state, &slot_stride, &num_slots, &HV, &T, &status, &units32, &params};
-    const hipError_t e = hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(256), args, split_lds_bytes(), s);
-    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+    // the preloaded scalars (no cu_seqlens: step calls only), the launch's
+    // head count, then the parameter block; requests in ranges as in launch()
+    const int64_t requests = units / p.HV;
+    for (int64_t r0 = 0; r0 < requests; r0 += MAX_REQUESTS_PER_LAUNCH) {
+        const int64_t n = requests - r0 < MAX_REQUESTS_PER_LAUNCH ? requests - r0 : MAX_REQUESTS_PER_LAUNCH;
+        DecodeParams params = r0 ? request_range(p, r0, BF16S ? 2 : 4) : p;
+        const int32_t *slot_idx = params.slot_idx;
+        void *state = params.state;
+        int64_t slot_stride = params.slot_stride, num_slots = params.num_slots;
+        int32_t HV = params.HV, T = params.T, heads = (int32_t)(n * HV);
+        const int32_t *status = params.status;
+        void *args[] = {&slot_idx, &state, &slot_stride, &num_slots, &HV, &T, &status, &heads, &params};
+        if (hipLaunchKernel(fn, dim3((uint32_t)(HV * (VD / S_COLS)), (uint32_t)n), dim3(256), args,
+                            split_lds_bytes(), s) != hipSuccess)
+            return KDA_ERR_LAUNCH;
+    }
+    return KDA_OK;
 }
 
 template <bool RAWG, bool BF16S>

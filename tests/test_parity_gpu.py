@@ -642,6 +642,24 @@ def test_out_of_range_slots_are_skipped():
     parity(p)
 
 
+@pytest.mark.parametrize("packed", [False, True])
+def test_more_requests_than_one_grid_holds(packed):
+    """A call with more requests than a launch grid's request dimension
+    (65535) runs as launches over request ranges: live requests on both
+    sides of each range boundary, in every kernel family, against the
+    oracle; padding rows untouched."""
+    N = 65535 + 300
+    p = ki.make_problem("ranges", 8, N=N, H=1, HV=1, K=128, V=128, num_slots=32, T=None if packed else 2,
+                        t_max=2, n_pad=N - 16)
+    live = [0, 1, 65533, 65534, 65535, 65536, 65537, N - 2, N - 1]
+    p.slot_idx[:] = -1
+    p.slot_idx[live] = np.arange(len(live), dtype=p.slot_idx.dtype) * 3
+    K_ = kda.KDA_FLAG_KERNEL
+    kinds = [0, K_(kda.KDA_KERNEL_QUARTER4)] if packed else [0, K_(kda.KDA_KERNEL_WIDE), K_(kda.KDA_KERNEL_SPLIT)]
+    for flags in kinds:
+        _log(f"request ranges packed={packed} flags={flags:#x}", parity(p, packed=packed, flags=flags))
+
+
 def test_zero_length_requests_leave_state_alone():
     p = ki.make_problem("zlen", 7, N=5, H=1, HV=2, K=128, V=128, num_slots=8, T=None)
     lens = np.array([2, 0, 1, 0, 3])
