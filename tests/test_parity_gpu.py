@@ -995,6 +995,38 @@ def test_quarter_waves_full_t4_sweep_match_wide_waves():
         assert torch.equal(a.state, b.state) and torch.equal(a.out.view(torch.int16), b.out.view(torch.int16)), n
 
 
+def _one_request(p, i):
+    """Request i of problem p as a call of its own (same inputs, same slot)."""
+    import dataclasses
+    lo, hi = int(p.cu_seqlens[i]), int(p.cu_seqlens[i + 1])
+    cut = lambda a: None if a is None else a[lo:hi].copy()
+    return dataclasses.replace(p, N=1, cu_seqlens=np.array([0, hi - lo], dtype=np.int32),
+                               slot_idx=p.slot_idx[i:i + 1].copy(), q=cut(p.q), k=cut(p.k), v=cut(p.v),
+                               g=cut(p.g), beta=cut(p.beta), gate=cut(p.gate), raw_gate=cut(p.raw_gate),
+                               raw_beta=cut(p.raw_beta))
+
+
+@pytest.mark.parametrize("T,raw", [(1, False), (1, True), (2, True), (4, False)])
+def test_results_do_not_depend_on_the_batch(T, raw):
+    """A request decoded inside a batch of 64 (512 tiles: eight or four
+    16-column waves) and alone (8 tiles: split-key or two 16-column waves)
+    gives the same output and state bits."""
+    N = 64
+    p = ki.make_problem("batch", 40 + T, N=N, H=8, HV=8, K=128, V=128, num_slots=N + 4, T=T, raw_gates=raw)
+    whole = _fresh(p)
+    run_gpu(whole)
+    torch.cuda.synchronize()
+    assert kda.kda_decode_plan(8, T, False, raw_gate=raw, layout=True) != \
+        kda.kda_decode_plan(N * 8, T, False, raw_gate=raw, layout=True) or T == 1
+    for i in (0, 17, N - 1):
+        alone = _fresh(_one_request(p, i))
+        run_gpu(alone)
+        torch.cuda.synchronize()
+        lo, hi, slot = int(p.cu_seqlens[i]), int(p.cu_seqlens[i + 1]), int(p.slot_idx[i])
+        assert torch.equal(alone.out.view(torch.int16), whole.out[lo:hi].view(torch.int16)), i
+        assert torch.equal(alone.state[slot], whole.state[slot]), i
+
+
 def test_chained_single_tokens_bit_identical():
     p = ki.workload("n32_t4_h8")
     d_multi = _fresh(p)
