@@ -36,7 +36,8 @@ write, the same rotation and protocol), the host cost of one enqueue through
 the C ABI, the cache-resident time (--warm), and the CPU oracle on all host
 cores and on one.  With --flags-b the blocks alternate A B B A ... between the
 library's choice (A) and a call with extra flag bits (B), and the line
-carries both medians.  Prints one JSON line.
+carries both medians (--flags-b 0x2: validated calls, KDA_FLAG_VALIDATE, against
+trusted ones).  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -376,10 +377,14 @@ def main():
     pool_live = pools[0][torch.from_numpy(p.slot_idx[p.live_requests()].astype(np.int64)).to(dev)].float().cpu().numpy()
     set_t = [torch.from_numpy(s).to(dev) for s in sets]
 
+    # a verdict word for calls with KDA_FLAG_VALIDATE (--flags-b 0x2: the
+    # metadata check's cost); calls without the flag ignore it
+    verdict = torch.zeros(1, dtype=torch.int32, device=dev)
     combos = []
     for r in range(R):
         for s in set_t:
-            combos.append(kda.decode_args(q, k, v, g, beta, pools[r], s, out, p.scale, gate, w, p.eps, **raw))
+            combos.append(kda.decode_args(q, k, v, g, beta, pools[r], s, out, p.scale, gate, w, p.eps,
+                                          device_status=verdict, **raw))
     T = p.T if p.T is not None else 0
     packed = p.T is None
     base_flags = kda.KDA_FLAG_STATE_BF16 if bf16_state else 0

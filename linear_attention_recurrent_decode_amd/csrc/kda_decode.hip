@@ -650,6 +650,16 @@ __device__ __forceinline__ void slot_and_token_args(const DecodeParams &p, int64
                      "s"(p.qk_magic_hi));
 }
 
+// The validation verdict for a workgroup's entry check, fetched together
+// with the slot index: without validation (status == nullptr) the load goes
+// to the slot array's first word instead, so that no branch separates the
+// two loads and one wait covers both; the value is then ignored.
+__device__ __forceinline__ int32_t entry_verdict(const int32_t *status, const int32_t *slot_idx)
+{
+    const int32_t v = *(status ? status : slot_idx);
+    return status ? v : KDA_DEVICE_OK;
+}
+
 constexpr int BODY_LOOP = 0, BODY_PEELED = 1, BODY_STAGED = 2;
 
 // The scalars on the critical path (slot lookup -> tile address, and the
@@ -677,12 +687,11 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot
 
     // slot gather: padding rows and slots outside the pool are skipped; with
     // validation, every block stops here unless the metadata check passed
+    const int32_t verdict = entry_verdict(status, slot_idx);
     const int64_t slot = slot_idx[req];
     if constexpr (BODY == BODY_LOOP)
         slot_and_token_args<RAWG>(p, slot);   // the loop body loads its first token before the tile
-    if (status && *status != KDA_DEVICE_OK)
-        return;
-    if (slot < 0 || slot >= num_slots)
+    if ((verdict != KDA_DEVICE_OK) | (slot < 0) | (slot >= num_slots))   // one branch: both loads first
         return;
     int64_t bos, eos;
     if (cu_seqlens) {
@@ -1125,12 +1134,11 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
     const int hv = (int)(blockIdx.x / NVT);
     const int64_t req = blockIdx.y;
 
+    const int32_t verdict = entry_verdict(status, slot_idx);
     const int64_t slot = slot_idx[req];
     if constexpr (EARLY)
         slot_and_token_args<RAWG>(p, slot);
-    if (status && *status != KDA_DEVICE_OK)
-        return;
-    if (slot < 0 || slot >= num_slots)
+    if ((verdict != KDA_DEVICE_OK) | (slot < 0) | (slot >= num_slots))   // one branch: both loads first
         return;
     int64_t bos, eos;
     if (cu_seqlens) {
@@ -1361,12 +1369,11 @@ __global__ __launch_bounds__(256) void kda_decode_split_kernel(const int32_t *sl
         req = blockIdx.y;
     }
 
+    const int32_t verdict = entry_verdict(status, slot_idx);
     const int64_t slot = slot_idx[req];
     if constexpr (EARLY)
         slot_and_token_args<RAWG>(p, slot);
-    if (status && *status != KDA_DEVICE_OK)
-        return;
-    if (slot < 0 || slot >= num_slots)
+    if ((verdict != KDA_DEVICE_OK) | (slot < 0) | (slot >= num_slots))   // one branch: both loads first
         return;
     const int64_t bos = req * T, eos = bos + T;
     const int h = qk_head(p, hv);
@@ -1473,40 +1480,74 @@ __global__ __launch_bounds__(256) void kda_decode_split_kernel(const int32_t *sl
     }
 }
 
-// Metadata check for KDA_FLAG_VALIDATE: one workgroup, lowest error code wins.
+// Metadata check for KDA_FLAG_VALIDATE: one workgroup, lowest error code
+// wins.  Duplicate live slots are found exactly with an open-addressing hash
+// table of slot values in LDS (linear probing, inserts by compare-and-swap):
+// inserting a value that is already there is a duplicate.  The table holds
+// VALIDATE_TABLE entries and takes at most half of that per pass; a call
+// with more live requests makes several passes over the slot indices, each
+// inserting only the slots whose hash selects that pass.
 constexpr int VALIDATE_THREADS = 1024;
-constexpr int VALIDATE_LDS_SLOTS = 8192;
+constexpr int VALIDATE_TABLE = 8192;                     // 32 KiB of LDS
+constexpr int VALIDATE_PER_PASS = VALIDATE_TABLE / 2;
+constexpr int32_t VALIDATE_EMPTY = -1;                   // never a live slot
+
+__device__ __forceinline__ uint32_t slot_hash(int32_t s)
+{
+    return (uint32_t)s * 2654435761u;   // Knuth's multiplicative hash; the table uses the top bits
+}
 
 __global__ __launch_bounds__(VALIDATE_THREADS) void kda_validate_kernel(const int32_t *slot_idx,
                                                                        const int32_t *cu_seqlens, int32_t N,
                                                                        int64_t num_slots, int64_t total_tokens,
                                                                        int32_t *status)
 {
-    __shared__ int32_t slots[VALIDATE_LDS_SLOTS];
+    __shared__ int32_t table[VALIDATE_TABLE];
     __shared__ int32_t verdict;
     const int tid = threadIdx.x;
-    const bool in_lds = N <= VALIDATE_LDS_SLOTS;
     if (tid == 0)
         verdict = 0x7FFFFFFF;
-    if (in_lds)
-        for (int i = tid; i < N; i += VALIDATE_THREADS)
-            slots[i] = slot_idx[i];
-    __syncthreads();
     int32_t found = 0x7FFFFFFF;
-    for (int i = tid; i < N; i += VALIDATE_THREADS) {
-        const int32_t s = in_lds ? slots[i] : slot_idx[i];
-        if (s == -1)
-            continue;
-        if (s < 0 || (int64_t)s >= num_slots) {
-            found = min(found, KDA_DEVICE_ERR_SLOT_RANGE);
-            continue;
-        }
-        for (int j = i + 1; j < N; ++j) {
-            if ((in_lds ? slots[j] : slot_idx[j]) == s) {
-                found = min(found, KDA_DEVICE_ERR_SLOT_DUP);
-                break;
+    const uint32_t passes = (uint32_t)((N + VALIDATE_PER_PASS - 1) / VALIDATE_PER_PASS);
+    for (uint32_t pass = 0; pass < passes; ++pass) {
+        for (int e = tid; e < VALIDATE_TABLE; e += VALIDATE_THREADS)
+            table[e] = VALIDATE_EMPTY;
+        __syncthreads();
+        for (int i = tid; i < N; i += VALIDATE_THREADS) {
+            const int32_t s = slot_idx[i];
+            if (s == -1)
+                continue;
+            if (s < 0 || (int64_t)s >= num_slots) {
+                if (pass == 0)
+                    found = min(found, KDA_DEVICE_ERR_SLOT_RANGE);
+                continue;
+            }
+            const uint32_t h = slot_hash(s);
+            if ((h & 0xFFFFu) % passes != pass)
+                continue;
+            // a pass holds about N / passes <= VALIDATE_PER_PASS values; the
+            // probe stops at an empty entry or at the value itself
+            uint32_t e = h >> 19;                                // 13 bits: VALIDATE_TABLE entries
+            bool settled = false;
+            for (int probe = 0; probe < VALIDATE_TABLE && !settled; ++probe) {
+                const int32_t prev = atomicCAS(&table[e], VALIDATE_EMPTY, s);
+                if (prev == s)
+                    found = min(found, KDA_DEVICE_ERR_SLOT_DUP);
+                settled = prev == VALIDATE_EMPTY || prev == s;
+                e = (e + 1) & (VALIDATE_TABLE - 1);
+            }
+            if (!settled) {
+                // a full table (slot values whose hashes crowd one pass):
+                // compare with every other slot index instead
+                for (int j = 0; j < N; ++j) {
+                    if (j != i && slot_idx[j] == s) {
+                        found = min(found, KDA_DEVICE_ERR_SLOT_DUP);
+                        break;
+                    }
+                }
             }
         }
+        __syncthreads();
     }
     if (cu_seqlens) {
         for (int i = tid; i <= N; i += VALIDATE_THREADS) {

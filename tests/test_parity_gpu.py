@@ -572,6 +572,37 @@ def test_validate_rejects_cu_seqlens_past_the_tokens():
     assert torch.equal(d.state, before)
 
 
+@pytest.mark.parametrize("case", ["valid", "duplicate", "past_pool", "cu_seqlens"])
+def test_validate_many_requests(case):
+    """10000 requests: the duplicate check's hash table takes 4096 values per
+    pass, so this call makes three passes; a duplicate of the first live
+    slot in the last live request is still found, valid metadata decodes."""
+    N = 10000
+    p = ki.make_problem("manyreq", 13, N=N, H=1, HV=1, K=128, V=128, num_slots=N + 16, T=None, t_max=2,
+                        n_pad=N // 10)
+    live = p.live_requests()
+    code = 0
+    if case == "duplicate":
+        p.slot_idx[live[-1]] = p.slot_idx[live[0]]
+        code = 2
+    elif case == "past_pool":
+        p.slot_idx[live[-1]] = p.num_slots
+        code = 1
+    elif case == "cu_seqlens":
+        p.cu_seqlens[N - 3] = p.cu_seqlens[N - 1]
+        code = 3
+    d = upload(p)
+    before = d.state.clone()
+    st = _status_word()
+    run_gpu(d, device_status=st)
+    torch.cuda.synchronize()
+    assert st.item() == code
+    if code:
+        assert torch.equal(d.state, before)
+    else:
+        _log("validated call, 10000 requests", compare(d, *run_oracle(p)))
+
+
 def test_validate_inside_a_graph():
     """A captured validated call: replays with valid metadata decode, a replay
     after the slot indices were corrupted in place touches nothing."""
