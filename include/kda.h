@@ -70,12 +70,14 @@ typedef enum kda_status {
 #define KDA_FLAG_STATE_BF16 (1u << 0)
 
 /* flags: bit 1 validates the device metadata before the decode, all or
- * nothing.  A one-workgroup check runs first on the call's stream and writes
- * `device_status`: KDA_DEVICE_OK, or the lowest-numbered KDA_DEVICE_ERR_* it
- * found.  The decode then runs only if the word is KDA_DEVICE_OK; otherwise
- * no state, output or other buffer is touched.  Costs one extra launch; the
- * duplicate check is O(N^2 / 1024) per call.  Without this flag the metadata
- * is trusted (slots outside the pool are skipped). */
+ * nothing, and writes `device_status`: KDA_DEVICE_OK, or the lowest-numbered
+ * KDA_DEVICE_ERR_* found.  The decode proceeds only if the metadata is valid;
+ * otherwise no state, output or other buffer is touched.  A call of at most
+ * 64 requests is checked by the decode kernel's own waves (no extra launch);
+ * a larger call runs a one-workgroup check kernel first on the call's stream
+ * (one extra launch; duplicates found through a hash table, O(N / 1024) per
+ * 4096 requests).  Without this flag the metadata is trusted (slots outside
+ * the pool are skipped). */
 #define KDA_FLAG_VALIDATE (1u << 1)
 #define KDA_DEVICE_OK 0
 #define KDA_DEVICE_ERR_SLOT_RANGE 1   /* a slot index outside [0, num_slots) other than -1 */

@@ -91,6 +91,9 @@ struct DecodeParams {
     int32_t *status;             // KDA_FLAG_VALIDATE: the metadata check's verdict
     void *inter_state;           // NULL, or the state after every token (pool element type)
     int64_t inter_stride;
+    int64_t tokens;              // token rows of the call (the check in the decode kernels)
+    int32_t requests;            // requests of the call (the check in the decode kernels)
+    int32_t check_in_kernel;     // host side: launch the instances that check the metadata (VCHECK)
 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -650,6 +653,46 @@ __device__ __forceinline__ void slot_and_token_args(const DecodeParams &p, int64
                      "s"(p.qk_magic_hi));
 }
 
+// The metadata check of a validated call of at most CHECK_IN_WAVE requests,
+// done by every wave of the decode itself instead of a kernel of its own:
+// lane l reads slot index l and cu_seqlens entries l, l + 1; a duplicate is
+// a live, in-range slot that another lane also holds (each slot compared with
+// every lane's, N scalar broadcasts); the codes and their order are those of
+// kda_validate_kernel.  Workgroup (0, 0) writes the verdict word.
+constexpr int CHECK_IN_WAVE = 64;
+
+__device__ __forceinline__ int32_t wave_verdict(int32_t *verdict_word, const int32_t *slot_idx,
+                                             const int32_t *cu_seqlens, int64_t num_slots, int32_t N,
+                                             int64_t tokens)
+{
+    const int lane = threadIdx.x & 63;
+    const bool mine = lane < N;
+    const int32_t s = mine ? slot_idx[lane] : -1;
+    bool cu_bad = false;
+    if (cu_seqlens && mine) {
+        const int32_t c0 = cu_seqlens[lane], c1 = cu_seqlens[lane + 1];
+        cu_bad = c0 > c1 || (int64_t)c1 > tokens || (lane == 0 && (c0 < 0 || (int64_t)c0 > tokens));
+    }
+    const bool live = s != -1;
+    const bool range_bad = live && (s < 0 || (int64_t)s >= num_slots);
+    const bool checked = live && !range_bad;
+    bool dup = false;
+    for (int j = 0; j < N; ++j) {
+        const int32_t sj = __builtin_amdgcn_readlane(s, j);
+        dup |= checked && j != lane && sj == s;
+    }
+    int32_t code = KDA_DEVICE_OK;
+    if (__builtin_amdgcn_ballot_w64(cu_bad))
+        code = KDA_DEVICE_ERR_CU_SEQLENS;
+    if (__builtin_amdgcn_ballot_w64(dup))
+        code = KDA_DEVICE_ERR_SLOT_DUP;
+    if (__builtin_amdgcn_ballot_w64(range_bad))
+        code = KDA_DEVICE_ERR_SLOT_RANGE;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+        *verdict_word = code;
+    return code;
+}
+
 // The validation verdict for a workgroup's entry check, fetched together
 // with the slot index: without validation (status == nullptr) the load goes
 // to the slot array's first word instead, so that no branch separates the
@@ -660,6 +703,20 @@ __device__ __forceinline__ int32_t entry_verdict(const int32_t *status, const in
     return status ? v : KDA_DEVICE_OK;
 }
 
+// The entry verdict of a kernel instance: its own check of the metadata
+// (VCHECK: the instances for validated calls of at most CHECK_IN_WAVE
+// requests, `status` the verdict word to write), or the word a
+// kda_validate_kernel run wrote (or no validation).
+template <bool VCHECK>
+__device__ __forceinline__ int32_t kernel_verdict(const int32_t *status, const int32_t *slot_idx,
+                                                  const int32_t *cu_seqlens, int64_t num_slots, const DecodeParams &p)
+{
+    if constexpr (VCHECK)
+        return wave_verdict(const_cast<int32_t *>(status), slot_idx, cu_seqlens, num_slots, p.requests, p.tokens);
+    else
+        return entry_verdict(status, slot_idx);
+}
+
 constexpr int BODY_LOOP = 0, BODY_PEELED = 1, BODY_STAGED = 2;
 
 // The scalars on the critical path (slot lookup -> tile address, and the
@@ -667,7 +724,7 @@ constexpr int BODY_LOOP = 0, BODY_PEELED = 1, BODY_STAGED = 2;
 // with kernarg preloading, so they arrive in SGPRs at wave launch and the slot
 // index load issues without waiting for a kernel-argument fetch.  The rest
 // travels in DecodeParams.
-template <int NW, bool NORM, int BODY, bool BF16S, bool RAWG>
+template <int NW, bool NORM, int BODY, bool BF16S, bool RAWG, bool VCHECK = false>
 __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot_idx, const int32_t *cu_seqlens,
                                                              void *state, int64_t slot_stride, int64_t num_slots,
                                                              int32_t HV, int32_t T, const int32_t *status,
@@ -687,7 +744,7 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot
 
     // slot gather: padding rows and slots outside the pool are skipped; with
     // validation, every block stops here unless the metadata check passed
-    const int32_t verdict = entry_verdict(status, slot_idx);
+    const int32_t verdict = kernel_verdict<VCHECK>(status, slot_idx, cu_seqlens, num_slots, p);
     const int64_t slot = slot_idx[req];
     if constexpr (BODY == BODY_LOOP)
         slot_and_token_args<RAWG>(p, slot);   // the loop body loads its first token before the tile
@@ -1116,7 +1173,7 @@ struct SlabIO {
 // kernel arguments requested with the slot index), so that its state-free
 // part runs while the tile is in flight.  LDS is dynamic: the staged tile
 // (C = 16 NQ columns) plus 64 floats for the norm's group sums.
-template <int NQ, int PF, bool NORM, bool RAWG, bool BF16S, bool EARLY>
+template <int NQ, int PF, bool NORM, bool RAWG, bool BF16S, bool EARLY, bool VCHECK = false>
 __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *slot_idx, const int32_t *cu_seqlens,
                                                                void *state, int64_t slot_stride, int64_t num_slots,
                                                                int32_t HV, int32_t T, const int32_t *status,
@@ -1134,7 +1191,7 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
     const int hv = (int)(blockIdx.x / NVT);
     const int64_t req = blockIdx.y;
 
-    const int32_t verdict = entry_verdict(status, slot_idx);
+    const int32_t verdict = kernel_verdict<VCHECK>(status, slot_idx, cu_seqlens, num_slots, p);
     const int64_t slot = slot_idx[req];
     if constexpr (EARLY)
         slot_and_token_args<RAWG>(p, slot);
@@ -1331,7 +1388,7 @@ __device__ __forceinline__ void advance_split(float (&s)[S_ROWS], const PairPre 
 // last group holds the remaining n < 8 heads.  Same results; measured slower
 // (the re-fetched input rows come from the memory-side cache, not HBM), so
 // the library never picks it and KDA_FLAG_PLACEMENT forces it.
-template <int PF, bool RAWG, bool BF16S, bool EARLY, bool HEAD_XCD = false>
+template <int PF, bool RAWG, bool BF16S, bool EARLY, bool HEAD_XCD = false, bool VCHECK = false>
 __global__ __launch_bounds__(256) void kda_decode_split_kernel(const int32_t *slot_idx, void *state,
                                                                int64_t slot_stride, int64_t num_slots, int32_t HV,
                                                                int32_t T, const int32_t *status, int32_t units,
@@ -1369,7 +1426,7 @@ __global__ __launch_bounds__(256) void kda_decode_split_kernel(const int32_t *sl
         req = blockIdx.y;
     }
 
-    const int32_t verdict = entry_verdict(status, slot_idx);
+    const int32_t verdict = kernel_verdict<VCHECK>(status, slot_idx, nullptr, num_slots, p);
     const int64_t slot = slot_idx[req];
     if constexpr (EARLY)
         slot_and_token_args<RAWG>(p, slot);
@@ -1508,13 +1565,25 @@ __global__ __launch_bounds__(VALIDATE_THREADS) void kda_validate_kernel(const in
     if (tid == 0)
         verdict = 0x7FFFFFFF;
     int32_t found = 0x7FFFFFFF;
+    // each thread's first slot index is fetched together with the cu_seqlens
+    // entries (one wait for both)
+    const int32_t s_first = tid < N ? slot_idx[tid] : -1;
+    if (cu_seqlens) {
+        for (int i = tid; i <= N; i += VALIDATE_THREADS) {
+            const int32_t c = cu_seqlens[i];
+            const int32_t prev = i == 0 ? 0 : cu_seqlens[i - 1];
+            const bool bad = (i == 0 ? c < 0 : prev > c) || (int64_t)c > total_tokens;
+            if (bad)
+                found = KDA_DEVICE_ERR_CU_SEQLENS;
+        }
+    }
     const uint32_t passes = (uint32_t)((N + VALIDATE_PER_PASS - 1) / VALIDATE_PER_PASS);
     for (uint32_t pass = 0; pass < passes; ++pass) {
         for (int e = tid; e < VALIDATE_TABLE; e += VALIDATE_THREADS)
             table[e] = VALIDATE_EMPTY;
         __syncthreads();
         for (int i = tid; i < N; i += VALIDATE_THREADS) {
-            const int32_t s = slot_idx[i];
+            const int32_t s = i == tid ? s_first : slot_idx[i];
             if (s == -1)
                 continue;
             if (s < 0 || (int64_t)s >= num_slots) {
@@ -1548,14 +1617,6 @@ __global__ __launch_bounds__(VALIDATE_THREADS) void kda_validate_kernel(const in
             }
         }
         __syncthreads();
-    }
-    if (cu_seqlens) {
-        for (int i = tid; i <= N; i += VALIDATE_THREADS) {
-            const int32_t c = cu_seqlens[i];
-            const bool bad = (i == 0 ? c < 0 : cu_seqlens[i - 1] > c) || (int64_t)c > total_tokens;
-            if (bad)
-                found = min(found, KDA_DEVICE_ERR_CU_SEQLENS);
-        }
     }
     atomicMin(&verdict, found);
     __syncthreads();
@@ -1618,25 +1679,32 @@ constexpr size_t q_lds_bytes(int nq) { return (size_t)(KD * 16 * nq + 128) * siz
 // and the two token parities' exchange buffers of both row halves.
 constexpr size_t split_lds_bytes() { return (size_t)(KD * S_COLS + (KD / 16) * 16 + 4 * S_XCH) * sizeof(float); }
 
-template <bool NORM, bool RAWG, bool BF16S>
-bool raise_q8_lds_limit()
+template <bool NORM, bool RAWG, bool BF16S, bool VCHECK>
+bool raise_q8_lds_limit_one()
 {
-    const void *fns[] = {reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 1, NORM, RAWG, BF16S, false>),
-                         reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 2, NORM, RAWG, BF16S, false>),
-                         reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 3, NORM, RAWG, BF16S, false>),
-                         reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 4, NORM, RAWG, BF16S, false>)};
+    const void *fns[] = {reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 1, NORM, RAWG, BF16S, false, VCHECK>),
+                         reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 2, NORM, RAWG, BF16S, false, VCHECK>),
+                         reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 3, NORM, RAWG, BF16S, false, VCHECK>),
+                         reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 4, NORM, RAWG, BF16S, false, VCHECK>)};
     for (const void *fn : fns)
         if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)q_lds_bytes(8)) != hipSuccess)
             return false;
     if constexpr (!BF16S) {   // the inputs-first order serves fp32 pools only
-        const void *early[] = {reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 2, NORM, RAWG, false, true>),
-                               reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 3, NORM, RAWG, false, true>),
-                               reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 4, NORM, RAWG, false, true>)};
+        const void *early[] = {
+            reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 2, NORM, RAWG, false, true, VCHECK>),
+            reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 3, NORM, RAWG, false, true, VCHECK>),
+            reinterpret_cast<const void *>(&kda_decode_q_kernel<8, 4, NORM, RAWG, false, true, VCHECK>)};
         for (const void *fn : early)
             if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)q_lds_bytes(8)) != hipSuccess)
                 return false;
     }
     return true;
+}
+
+template <bool NORM, bool RAWG, bool BF16S>
+bool raise_q8_lds_limit()
+{
+    return raise_q8_lds_limit_one<NORM, RAWG, BF16S, false>() && raise_q8_lds_limit_one<NORM, RAWG, BF16S, true>();
 }
 
 DecodeParams make_params(const kda_internal::DecodeCall &c)
@@ -1678,6 +1746,9 @@ DecodeParams make_params(const kda_internal::DecodeCall &c)
     p.status = c.validate ? a->device_status : nullptr;
     p.inter_state = a->inter_state;
     p.inter_stride = a->inter_stride;
+    p.tokens = c.tokens;
+    p.requests = a->N;
+    p.check_in_kernel = 0;
     return p;
 }
 
@@ -1743,18 +1814,26 @@ kda_status launch(const void *kernel, const DecodeParams &p, int64_t requests, i
 }
 
 // ---- the 32-column kernel: the body and the width of the plan
-template <int NW, bool NORM, bool BF16S, bool RAWG>
-kda_status launch_wide(const DecodeParams &p, int64_t units, int body, hipStream_t s)
+template <int NW, bool NORM, bool BF16S, bool RAWG, bool VCHECK>
+const void *launch_wide_fn(int body)
 {
     // the loop body serves only fp32 pools with activated gates (the plan's
     // rule); it is not instantiated for the other forms
-    const void *fn = body == kda_internal::BODY_STAGED
-                         ? reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_STAGED, BF16S, RAWG>)
-                         : reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_PEELED, BF16S, RAWG>);
     if constexpr (!BF16S && !RAWG) {
         if (body == kda_internal::BODY_LOOP)
-            fn = reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_LOOP, BF16S, RAWG>);
+            return reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_LOOP, BF16S, RAWG, VCHECK>);
     }
+    return body == kda_internal::BODY_STAGED
+               ? reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_STAGED, BF16S, RAWG, VCHECK>)
+               : reinterpret_cast<const void *>(&kda_decode_kernel<NW, NORM, BODY_PEELED, BF16S, RAWG, VCHECK>);
+}
+
+template <int NW, bool NORM, bool BF16S, bool RAWG>
+kda_status launch_wide(const DecodeParams &p, int64_t units, int body, hipStream_t s)
+{
+    const void *fn = launch_wide_fn<NW, NORM, BF16S, RAWG, false>(body);
+    if (p.check_in_kernel)
+        fn = launch_wide_fn<NW, NORM, BF16S, RAWG, true>(body);
     return launch(fn, p, units / p.HV, 4 / NW, 64 * NW, 0, BF16S ? 2 : 4, s);
 }
 
@@ -1775,10 +1854,13 @@ kda_status dispatch_wide(const DecodeParams &p, int64_t units, const kda_interna
 template <int NQ, int PF, bool NORM, bool RAWG, bool BF16S>
 kda_status launch_quarter(const DecodeParams &p, int64_t units, bool early, hipStream_t s)
 {
-    const void *fn = reinterpret_cast<const void *>(&kda_decode_q_kernel<NQ, PF, NORM, RAWG, BF16S, false>);
+    const bool check = p.check_in_kernel != 0;
+    const void *fn = check ? reinterpret_cast<const void *>(&kda_decode_q_kernel<NQ, PF, NORM, RAWG, BF16S, false, true>)
+                           : reinterpret_cast<const void *>(&kda_decode_q_kernel<NQ, PF, NORM, RAWG, BF16S, false>);
     if constexpr (PF >= 2 && !BF16S) {
         if (early)
-            fn = reinterpret_cast<const void *>(&kda_decode_q_kernel<NQ, PF, NORM, RAWG, BF16S, true>);
+            fn = check ? reinterpret_cast<const void *>(&kda_decode_q_kernel<NQ, PF, NORM, RAWG, BF16S, true, true>)
+                       : reinterpret_cast<const void *>(&kda_decode_q_kernel<NQ, PF, NORM, RAWG, BF16S, true>);
     }
     return launch(fn, p, units / p.HV, 8 / NQ, 64 * NQ, q_lds_bytes(NQ), BF16S ? 2 : 4, s);
 }
@@ -1817,10 +1899,15 @@ kda_status dispatch_quarter(const DecodeParams &p, int64_t units, const kda_inte
 template <int PF, bool RAWG, bool BF16S>
 kda_status launch_split(const DecodeParams &p, int64_t units, bool early, bool head_xcd, hipStream_t s)
 {
-    const void *fn = reinterpret_cast<const void *>(&kda_decode_split_kernel<PF, RAWG, BF16S, false>);
+    // (the head-per-XCD placement is not combined with the check in the
+    // kernel: launch_decode runs kda_validate_kernel for such calls)
+    const bool check = p.check_in_kernel != 0;
+    const void *fn = check ? reinterpret_cast<const void *>(&kda_decode_split_kernel<PF, RAWG, BF16S, false, false, true>)
+                           : reinterpret_cast<const void *>(&kda_decode_split_kernel<PF, RAWG, BF16S, false>);
     if constexpr (PF >= 2 && !BF16S) {
         if (early)
-            fn = reinterpret_cast<const void *>(&kda_decode_split_kernel<PF, RAWG, BF16S, true>);
+            fn = check ? reinterpret_cast<const void *>(&kda_decode_split_kernel<PF, RAWG, BF16S, true, false, true>)
+                       : reinterpret_cast<const void *>(&kda_decode_split_kernel<PF, RAWG, BF16S, true>);
         if (head_xcd)
             fn = early ? reinterpret_cast<const void *>(&kda_decode_split_kernel<PF, RAWG, BF16S, true, true>)
                        : reinterpret_cast<const void *>(&kda_decode_split_kernel<PF, RAWG, BF16S, false, true>);
@@ -1898,10 +1985,14 @@ kda_status device_ready()
 
 kda_status launch_decode(const DecodeCall &c)
 {
-    const DecodeParams p = make_params(c);
+    DecodeParams p = make_params(c);
     const kda_decode_args *a = c.args;
     hipStream_t s = static_cast<hipStream_t>(c.stream);
-    if (c.validate) {
+    if (c.validate && a->N <= CHECK_IN_WAVE && !c.plan.head_xcd) {
+        // the waves of the decode check the metadata themselves (the VCHECK
+        // instances, `status` the word they write): no second launch
+        p.check_in_kernel = 1;
+    } else if (c.validate) {
         const int32_t *slots = a->slot_idx;
         const int32_t *cu = c.cu_seqlens;
         int32_t n = a->N;

@@ -556,6 +556,68 @@ def test_validate_rejects_on_quarter_waves(case, dtype, name):
     assert torch.all(d.out.view(torch.int16) == np.int16(np.uint16(0xC640).view(np.int16)))
 
 
+SMALL_VALIDATED = [
+    # (N, H, HV, T (None: packed), bf16 pool, fused gate): calls of at most
+    # 64 requests, checked by the decode's own waves, on every kernel family
+    (32, 8, 8, 1, False, False),     # 32-column waves
+    (20, 4, 8, 1, False, True),      # 32-column waves, fused gate
+    (64, 8, 8, 1, False, False),     # 512 tiles: eight 16-column waves
+    (16, 2, 8, 2, False, False),     # split-key waves
+    (64, 8, 8, 4, False, False),     # four 16-column waves, inputs first
+    (32, 8, 8, 1, True, False),      # bf16 pool: four 16-column waves
+    (40, 8, 8, None, False, False),  # packed: four 16-column waves
+    (12, 2, 8, None, True, True),    # packed, bf16 pool, fused gate
+    (65, 1, 2, None, False, False),  # one request more: the check kernel
+]
+
+
+@pytest.mark.parametrize("case", ["valid", "duplicate", "past_pool", "negative", "both", "decreasing"])
+@pytest.mark.parametrize("shape", SMALL_VALIDATED)
+def test_validate_small_calls(shape, case):
+    """Validated calls of up to 64 requests are checked by the decode kernel's
+    own waves: the same codes as the check kernel, nothing written on a
+    rejection, the verdict word written either way, and valid metadata gives
+    the unvalidated call's bits."""
+    N, H, HV, T, bf16, raw = shape
+    if case == "decreasing" and T is not None:
+        pytest.skip("cu_seqlens: packed calls only")
+    p = ki.make_problem("vsmall", 70 + N, N=N, H=H, HV=HV, K=128, V=128, num_slots=N + 9, T=T, n_pad=N // 6,
+                        raw_gates=raw)
+    dtype = torch.bfloat16 if bf16 else torch.float32
+    code = 0 if case == "valid" else _corrupt(p, case)
+    d = upload(p, state_dtype=dtype)
+    before = d.state.clone()
+    st = _status_word()
+    run_gpu(d, device_status=st)
+    torch.cuda.synchronize()
+    assert st.item() == code
+    if code:
+        assert torch.equal(d.state, before)
+        assert torch.all(d.out.view(torch.int16) == np.int16(np.uint16(0xC640).view(np.int16)))
+    else:
+        ref = upload(p, state_dtype=dtype)
+        run_gpu(ref)
+        torch.cuda.synchronize()
+        assert torch.equal(d.state, ref.state) and torch.equal(d.out.view(torch.int16), ref.out.view(torch.int16))
+
+
+@pytest.mark.parametrize("N", [8, 64])
+def test_validate_small_packed_cu_seqlens_past_the_tokens(N):
+    """A packed call of at most 64 requests whose cu_seqlens ends past the
+    call's token rows: code 3 from the decode's own check."""
+    import ctypes
+    p = ki.make_problem("vpast", 90 + N, N=N, H=2, HV=4, K=128, V=128, num_slots=N + 3, T=None)
+    d = upload(p)
+    before = d.state.clone()
+    st = _status_word()
+    a = kda.decode_args(d.q, d.k, d.v, d.g, d.beta, d.state, d.slot_idx, d.out, p.scale, device_status=st)
+    rc = kda.library().kda_decode_packed(ctypes.byref(a), d.cu_seqlens.data_ptr(), p.tokens - 1,
+                                         kda.KDA_FLAG_VALIDATE, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0 and st.item() == 3
+    assert torch.equal(d.state, before)
+
+
 def test_validate_rejects_cu_seqlens_past_the_tokens():
     """cu_seqlens[N] beyond total_tokens: the call is given fewer token rows
     than the tensors hold, so even an unvalidated run would stay in bounds."""
