@@ -32,9 +32,9 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
  *     library allocates nothing, never synchronises and never copies to or
  *     from the host.  Each call enqueues one kernel on `stream` (two with
- *     KDA_FLAG_VALIDATE, and one more per further 65535 requests of a call
- *     with more; a hipStream_t, NULL = the default stream) and returns; it
- *     can be captured into a HIP graph.
+ *     KDA_FLAG_VALIDATE on a call of more than 64 requests, and one more per
+ *     further 65535 requests of a call with more; a hipStream_t, NULL = the
+ *     default stream) and returns; it can be captured into a HIP graph.
  *   - Arguments are validated on the host in O(1) before anything is
  *     launched.  On any error status nothing was launched and no buffer was
  *     touched, except KDA_ERR_LAUNCH (the runtime refused a launch): for a
