@@ -20,7 +20,8 @@ cold caches, untimed warmup, interleaved blocks; and FlashInfer PR 4562,
 description: a duration-calibrated graph warmup):
   1. --warmup eager calls, then graph replays of one full slot rotation until
      at least --warmup-ms of wall time have passed (untimed);
-  2. --blocks timed blocks of exactly --steps calls each.  A block's calls
+  2. --blocks timed blocks (by default enough for about 2000 timed calls:
+     5 blocks of 2000, 101 of 20) of exactly --steps calls each.  A block's calls
      are enqueued on one stream right behind an untimed HIP graph replay of
      the calls before them in the rotation (at least a full rotation and
      2 ms of GPU time, and long enough that the host has enqueued the whole
@@ -73,6 +74,13 @@ LAYOUT_NAMES = {0: "32-column waves", 1: "16-column waves", 2: "16-column waves,
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def default_blocks(steps: int) -> int:
+    """Timed blocks when --blocks is not given: enough for about 2000 timed
+    calls (a median over more blocks when each block is short), odd, 5 to 101."""
+    n = max(5, min(101, -(-2000 // max(1, steps))))
+    return n if n % 2 else n + 1
 
 
 def algorithmic_bytes(p, state_elem: int = 4) -> dict:
@@ -295,7 +303,8 @@ def main():
     ap.add_argument("--steps", type=int, default=2000, help="calls per timed block")
     ap.add_argument("--warmup", type=int, default=200, help="untimed eager calls before the calibrated warmup")
     ap.add_argument("--warmup-ms", type=float, default=100.0, help="minimum wall time of graph-replayed warmup")
-    ap.add_argument("--blocks", type=int, default=5, help="timed blocks (at least 3)")
+    ap.add_argument("--blocks", type=int, default=None,
+                    help="timed blocks (at least 3; default: enough blocks for about 2000 timed calls, 5 to 101)")
     ap.add_argument("--workload", default="n32_t1_h8")
     ap.add_argument("--shape", default=None,
                     help="a workload of another shape with the same value distributions instead of --workload: "
@@ -317,6 +326,8 @@ def main():
         print("bench.py measures one GPU only: recurrent KDA decode has no cross-GPU step here; "
               "run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.blocks is None and args.steps >= 1:
+        args.blocks = default_blocks(args.steps)
     if args.blocks < 3 or args.steps < 1:
         print("bench.py needs --blocks >= 3 and --steps >= 1", file=sys.stderr)
         sys.exit(2)

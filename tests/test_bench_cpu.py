@@ -113,3 +113,13 @@ def test_threaded_oracle_equals_one_thread():
                              np.ascontiguousarray(cu[a:b + 1]), p.scale, out=out)
     assert np.array_equal(split, one)
     assert np.array_equal(np.isnan(out), np.isnan(ref)) and np.array_equal(out[~np.isnan(ref)], ref[~np.isnan(ref)])
+
+
+def test_default_block_count():
+    """About 2000 timed calls by default, an odd count from 5 to 101."""
+    assert bench.default_blocks(2000) == 5
+    assert bench.default_blocks(400) == 5
+    assert bench.default_blocks(20) == 101
+    assert bench.default_blocks(100) == 21
+    assert bench.default_blocks(1) == 101
+    assert all(bench.default_blocks(k) % 2 == 1 for k in range(1, 3000, 7))
