@@ -91,8 +91,7 @@ struct DecodeParams {
     int32_t *status;             // KDA_FLAG_VALIDATE: the metadata check's verdict
     void *inter_state;           // NULL, or the state after every token (pool element type)
     int64_t inter_stride;
-    int64_t tokens;              // token rows of the call (the check in the decode kernels)
-    int32_t requests;            // requests of the call (the check in the decode kernels)
+    int64_t tokens;              // host side: token rows of the call
     int32_t check_in_kernel;     // host side: launch the instances that check the metadata (VCHECK)
 };
 
@@ -663,16 +662,22 @@ constexpr int CHECK_IN_WAVE = 64;
 
 __device__ __forceinline__ int32_t wave_verdict(int32_t *verdict_word, const int32_t *slot_idx,
                                              const int32_t *cu_seqlens, int64_t num_slots, int32_t N,
-                                             int64_t tokens)
+                                             int64_t tokens, int64_t req, int64_t &own_slot)
 {
     const int lane = threadIdx.x & 63;
     const bool mine = lane < N;
-    const int32_t s = mine ? slot_idx[lane] : -1;
-    bool cu_bad = false;
-    if (cu_seqlens && mine) {
-        const int32_t c0 = cu_seqlens[lane], c1 = cu_seqlens[lane + 1];
-        cu_bad = c0 > c1 || (int64_t)c1 > tokens || (lane == 0 && (c0 < 0 || (int64_t)c0 > tokens));
+    const int at = mine ? lane : 0;   // every lane loads (the words of request 0 past N), so that the
+                                      // loads issue together, without a branch between them
+    const int32_t s_at = slot_idx[at];
+    int32_t c0 = 0, c1 = 0;
+    if (cu_seqlens) {
+        c0 = cu_seqlens[at];
+        c1 = cu_seqlens[at + 1];
     }
+    const int32_t s = mine ? s_at : -1;
+    own_slot = __builtin_amdgcn_readlane(s, (int)req);   // the workgroup's own request (req < N)
+    const bool cu_bad = cu_seqlens && mine &&
+                        (c0 > c1 || (int64_t)c1 > tokens || (lane == 0 && (c0 < 0 || (int64_t)c0 > tokens)));
     const bool live = s != -1;
     const bool range_bad = live && (s < 0 || (int64_t)s >= num_slots);
     const bool checked = live && !range_bad;
@@ -703,18 +708,31 @@ __device__ __forceinline__ int32_t entry_verdict(const int32_t *status, const in
     return status ? v : KDA_DEVICE_OK;
 }
 
-// The entry verdict of a kernel instance: its own check of the metadata
-// (VCHECK: the instances for validated calls of at most CHECK_IN_WAVE
-// requests, `status` the verdict word to write), or the word a
-// kda_validate_kernel run wrote (or no validation).
+// A workgroup's entry: the validation verdict and its request's slot index.
+// VCHECK instances (validated calls of at most CHECK_IN_WAVE requests) check
+// the metadata themselves, with `status` the verdict word to write, the
+// launch's request count and (packed calls) token rows in preloaded
+// arguments, and take their slot index from the lanes' loads; the others
+// read the word a kda_validate_kernel run wrote (or none) beside the slot.
+struct Entry {
+    int32_t verdict;
+    int64_t slot;
+};
+
 template <bool VCHECK>
-__device__ __forceinline__ int32_t kernel_verdict(const int32_t *status, const int32_t *slot_idx,
-                                                  const int32_t *cu_seqlens, int64_t num_slots, const DecodeParams &p)
+__device__ __forceinline__ Entry entry_check(const int32_t *status, const int32_t *slot_idx,
+                                             const int32_t *cu_seqlens, int64_t num_slots, int32_t requests,
+                                             int64_t tokens, int64_t req)
 {
-    if constexpr (VCHECK)
-        return wave_verdict(const_cast<int32_t *>(status), slot_idx, cu_seqlens, num_slots, p.requests, p.tokens);
-    else
-        return entry_verdict(status, slot_idx);
+    Entry e;
+    if constexpr (VCHECK) {
+        e.verdict = wave_verdict(const_cast<int32_t *>(status), slot_idx, cu_seqlens, num_slots, requests, tokens,
+                                 req, e.slot);
+    } else {
+        e.verdict = entry_verdict(status, slot_idx);
+        e.slot = slot_idx[req];
+    }
+    return e;
 }
 
 constexpr int BODY_LOOP = 0, BODY_PEELED = 1, BODY_STAGED = 2;
@@ -727,7 +745,7 @@ constexpr int BODY_LOOP = 0, BODY_PEELED = 1, BODY_STAGED = 2;
 template <int NW, bool NORM, int BODY, bool BF16S, bool RAWG, bool VCHECK = false>
 __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot_idx, const int32_t *cu_seqlens,
                                                              void *state, int64_t slot_stride, int64_t num_slots,
-                                                             int32_t HV, int32_t T, const int32_t *status,
+                                                             int32_t requests, int32_t T, const int32_t *status,
                                                              DecodeParams p)
 {
     static_assert(NW == 1 || NW == 2 || NW == 4, "a workgroup is 1, 2 or 4 waves");
@@ -744,8 +762,10 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot
 
     // slot gather: padding rows and slots outside the pool are skipped; with
     // validation, every block stops here unless the metadata check passed
-    const int32_t verdict = kernel_verdict<VCHECK>(status, slot_idx, cu_seqlens, num_slots, p);
-    const int64_t slot = slot_idx[req];
+    // (VCHECK packed calls carry their token rows in T)
+    const Entry entry = entry_check<VCHECK>(status, slot_idx, cu_seqlens, num_slots, requests, T, req);
+    const int32_t verdict = entry.verdict;
+    const int64_t slot = entry.slot;
     if constexpr (BODY == BODY_LOOP)
         slot_and_token_args<RAWG>(p, slot);   // the loop body loads its first token before the tile
     if ((verdict != KDA_DEVICE_OK) | (slot < 0) | (slot >= num_slots))   // one branch: both loads first
@@ -1176,7 +1196,7 @@ struct SlabIO {
 template <int NQ, int PF, bool NORM, bool RAWG, bool BF16S, bool EARLY, bool VCHECK = false>
 __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *slot_idx, const int32_t *cu_seqlens,
                                                                void *state, int64_t slot_stride, int64_t num_slots,
-                                                               int32_t HV, int32_t T, const int32_t *status,
+                                                               int32_t requests, int32_t T, const int32_t *status,
                                                                DecodeParams p)
 {
     static_assert(NQ == 2 || NQ == 4 || NQ == 8, "a workgroup is 2, 4 or 8 waves of 16 columns");
@@ -1191,8 +1211,10 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
     const int hv = (int)(blockIdx.x / NVT);
     const int64_t req = blockIdx.y;
 
-    const int32_t verdict = kernel_verdict<VCHECK>(status, slot_idx, cu_seqlens, num_slots, p);
-    const int64_t slot = slot_idx[req];
+    // (VCHECK packed calls carry their token rows in T)
+    const Entry entry = entry_check<VCHECK>(status, slot_idx, cu_seqlens, num_slots, requests, T, req);
+    const int32_t verdict = entry.verdict;
+    const int64_t slot = entry.slot;
     if constexpr (EARLY)
         slot_and_token_args<RAWG>(p, slot);
     if ((verdict != KDA_DEVICE_OK) | (slot < 0) | (slot >= num_slots))   // one branch: both loads first
@@ -1426,8 +1448,10 @@ __global__ __launch_bounds__(256) void kda_decode_split_kernel(const int32_t *sl
         req = blockIdx.y;
     }
 
-    const int32_t verdict = kernel_verdict<VCHECK>(status, slot_idx, nullptr, num_slots, p);
-    const int64_t slot = slot_idx[req];
+    // (VCHECK: the launch's requests from its head count; step calls, no cu_seqlens)
+    const Entry entry = entry_check<VCHECK>(status, slot_idx, nullptr, num_slots, VCHECK ? units / HV : 0, 0, req);
+    const int32_t verdict = entry.verdict;
+    const int64_t slot = entry.slot;
     if constexpr (EARLY)
         slot_and_token_args<RAWG>(p, slot);
     if ((verdict != KDA_DEVICE_OK) | (slot < 0) | (slot >= num_slots))   // one branch: both loads first
@@ -1747,7 +1771,6 @@ DecodeParams make_params(const kda_internal::DecodeCall &c)
     p.inter_state = a->inter_state;
     p.inter_stride = a->inter_stride;
     p.tokens = c.tokens;
-    p.requests = a->N;
     p.check_in_kernel = 0;
     return p;
 }
@@ -1803,11 +1826,14 @@ kda_status launch(const void *kernel, const DecodeParams &p, int64_t requests, i
         const int32_t *slot_idx = params.slot_idx, *cu_seqlens = params.cu_seqlens;
         void *state = params.state;
         int64_t slot_stride = params.slot_stride, num_slots = params.num_slots;
-        int32_t HV = params.HV, T = params.T;
+        // the metadata check of VCHECK instances reads the launch's request
+        // count and, for a packed call (whose kernels do not use T), its token rows
+        int32_t requests = (int32_t)n;
+        int32_t T = params.check_in_kernel && cu_seqlens ? (int32_t)params.tokens : params.T;
         const int32_t *status = params.status;
-        void *args[] = {&slot_idx, &cu_seqlens, &state, &slot_stride, &num_slots, &HV, &T, &status, &params};
-        if (hipLaunchKernel(kernel, dim3((uint32_t)(HV * tiles), (uint32_t)n), dim3(threads), args, lds, stream) !=
-            hipSuccess)
+        void *args[] = {&slot_idx, &cu_seqlens, &state, &slot_stride, &num_slots, &requests, &T, &status, &params};
+        if (hipLaunchKernel(kernel, dim3((uint32_t)(params.HV * tiles), (uint32_t)n), dim3(threads), args, lds,
+                            stream) != hipSuccess)
             return KDA_ERR_LAUNCH;
     }
     return KDA_OK;
@@ -1988,7 +2014,7 @@ kda_status launch_decode(const DecodeCall &c)
     DecodeParams p = make_params(c);
     const kda_decode_args *a = c.args;
     hipStream_t s = static_cast<hipStream_t>(c.stream);
-    if (c.validate && a->N <= CHECK_IN_WAVE && !c.plan.head_xcd) {
+    if (c.validate && a->N <= CHECK_IN_WAVE && !c.plan.head_xcd && c.tokens <= 0x7FFFFFFF) {
         // the waves of the decode check the metadata themselves (the VCHECK
         // instances, `status` the word they write): no second launch
         p.check_in_kernel = 1;
