@@ -53,6 +53,7 @@
 #include <stdint.h>
 #include <string.h>
 #include <type_traits>
+#include <utility>
 
 #include "kda_launch.h"
 
@@ -655,14 +656,40 @@ __device__ __forceinline__ void slot_and_token_args(const DecodeParams &p, int64
 // The metadata check of a validated call of at most CHECK_IN_WAVE requests,
 // done by every wave of the decode itself instead of a kernel of its own:
 // lane l reads slot index l and cu_seqlens entries l, l + 1; a duplicate is
-// a live, in-range slot that another lane also holds (each slot compared with
-// every lane's, N scalar broadcasts); the codes and their order are those of
-// kda_validate_kernel.  Workgroup (0, 0) writes the verdict word.
+// a live, in-range slot that another lane also holds (every pair of lanes
+// compared through lane rotations, ds_bpermute); the codes and their order
+// are those of kda_validate_kernel.  Workgroup (0, 0) writes the verdict
+// word.
 constexpr int CHECK_IN_WAVE = 64;
+
+// x rotated right by R + first lanes within each 16-lane row (DPP row_ror;
+// a rotation by 0 is x itself), compared with s
+template <int R>
+__device__ __forceinline__ bool row_rotation_match(int32_t x, int32_t s)
+{
+    if constexpr (R == 0)
+        return x == s;
+    else
+        return __builtin_amdgcn_mov_dpp(x, 0x120 + R, 0xF, 0xF, true) == s;
+}
+
+// any of the row rotations FIRST .. FIRST + COUNT - 1 of x matches s
+template <int FIRST, int... R>
+__device__ __forceinline__ bool row_rotations_match(int32_t x, int32_t s, std::integer_sequence<int, R...>)
+{
+    return (false | ... | row_rotation_match<FIRST + R>(x, s));
+}
+
+template <int FIRST, int COUNT>
+__device__ __forceinline__ bool row_rotations_match(int32_t x, int32_t s)
+{
+    return row_rotations_match<FIRST>(x, s, std::make_integer_sequence<int, COUNT>{});
+}
 
 __device__ __forceinline__ int32_t wave_verdict(int32_t *verdict_word, const int32_t *slot_idx,
                                              const int32_t *cu_seqlens, int64_t num_slots, int32_t N,
-                                             int64_t tokens, int64_t req, int64_t &own_slot)
+                                             int64_t tokens, int64_t req, int64_t &own_slot, int64_t &bos,
+                                             int64_t &eos)
 {
     const int lane = threadIdx.x & 63;
     const bool mine = lane < N;
@@ -676,16 +703,41 @@ __device__ __forceinline__ int32_t wave_verdict(int32_t *verdict_word, const int
     }
     const int32_t s = mine ? s_at : -1;
     own_slot = __builtin_amdgcn_readlane(s, (int)req);   // the workgroup's own request (req < N)
+    if (cu_seqlens) {
+        bos = __builtin_amdgcn_readlane(c0, (int)req);
+        eos = __builtin_amdgcn_readlane(c1, (int)req);
+    } else {
+        bos = req * tokens;   // step calls: `tokens` is T
+        eos = bos + tokens;
+    }
     const bool cu_bad = cu_seqlens && mine &&
                         (c0 > c1 || (int64_t)c1 > tokens || (lane == 0 && (c0 < 0 || (int64_t)c0 > tokens)));
     const bool live = s != -1;
     const bool range_bad = live && (s < 0 || (int64_t)s >= num_slots);
     const bool checked = live && !range_bad;
+    // Every pair of the first N lanes meets: lanes of one 16-lane row
+    // through the row rotations of s (two lanes d apart meet at rotation d,
+    // so N <= 16 needs rotations 1 .. N - 1 only), lanes of rows i and j
+    // through the 16 row rotations of the copy whose rows are exchanged by
+    // i ^ j (one ds_bpermute each, only for the rows that hold requests).
+    // Only a live, in-range slot counts, so the -1 past N never matches.  No
+    // loop: a loop keeps the compiler from sinking the kernel-argument loads
+    // past it, and their wait then precedes the check (measured: about
+    // 0.5 us at 32 requests).
     bool dup = false;
-    for (int j = 0; j < N; ++j) {
-        const int32_t sj = __builtin_amdgcn_readlane(s, j);
-        dup |= checked && j != lane && sj == s;
+    if (N > 1)
+        dup = row_rotations_match<1, 3>(s, s);
+    if (N > 4)
+        dup |= row_rotations_match<4, 4>(s, s);
+    if (N > 8)
+        dup |= row_rotations_match<8, 8>(s, s);
+    if (N > 16)
+        dup |= row_rotations_match<0, 16>(__builtin_amdgcn_ds_bpermute((lane ^ 16) << 2, s), s);
+    if (N > 32) {
+        dup |= row_rotations_match<0, 16>(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, s), s);
+        dup |= row_rotations_match<0, 16>(__builtin_amdgcn_ds_bpermute((lane ^ 48) << 2, s), s);
     }
+    dup &= checked;
     int32_t code = KDA_DEVICE_OK;
     if (__builtin_amdgcn_ballot_w64(cu_bad))
         code = KDA_DEVICE_ERR_CU_SEQLENS;
@@ -712,11 +764,16 @@ __device__ __forceinline__ int32_t entry_verdict(const int32_t *status, const in
 // VCHECK instances (validated calls of at most CHECK_IN_WAVE requests) check
 // the metadata themselves, with `status` the verdict word to write, the
 // launch's request count and (packed calls) token rows in preloaded
-// arguments, and take their slot index from the lanes' loads; the others
-// read the word a kda_validate_kernel run wrote (or none) beside the slot.
+// arguments, and take the slot index and the request's token rows from the
+// lanes' loads; the others read the word a kda_validate_kernel run wrote (or
+// none) beside the slot, and fetch the token rows after the entry branch
+// (token_rows; fetching cu_seqlens beside the slot index measured 1-3% slower
+// on MI355X for the 32-column and 16-column kernels).  `tokens` is T for step
+// calls (cu_seqlens == nullptr).
 struct Entry {
     int32_t verdict;
     int64_t slot;
+    int64_t bos, eos;   // VCHECK only
 };
 
 template <bool VCHECK>
@@ -727,12 +784,30 @@ __device__ __forceinline__ Entry entry_check(const int32_t *status, const int32_
     Entry e;
     if constexpr (VCHECK) {
         e.verdict = wave_verdict(const_cast<int32_t *>(status), slot_idx, cu_seqlens, num_slots, requests, tokens,
-                                 req, e.slot);
+                                 req, e.slot, e.bos, e.eos);
     } else {
         e.verdict = entry_verdict(status, slot_idx);
         e.slot = slot_idx[req];
     }
     return e;
+}
+
+// The request's token rows [bos, eos): packed calls read cu_seqlens, step
+// calls have T rows each.
+template <bool VCHECK>
+__device__ __forceinline__ void token_rows(const Entry &e, const int32_t *cu_seqlens, int64_t req, int64_t T,
+                                           int64_t &bos, int64_t &eos)
+{
+    if constexpr (VCHECK) {
+        bos = e.bos;
+        eos = e.eos;
+    } else if (cu_seqlens) {
+        bos = cu_seqlens[req];
+        eos = cu_seqlens[req + 1];
+    } else {
+        bos = req * T;
+        eos = bos + T;
+    }
 }
 
 constexpr int BODY_LOOP = 0, BODY_PEELED = 1, BODY_STAGED = 2;
@@ -771,13 +846,7 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot
     if ((verdict != KDA_DEVICE_OK) | (slot < 0) | (slot >= num_slots))   // one branch: both loads first
         return;
     int64_t bos, eos;
-    if (cu_seqlens) {
-        bos = cu_seqlens[req];
-        eos = cu_seqlens[req + 1];
-    } else {
-        bos = req * T;
-        eos = bos + T;
-    }
+    token_rows<VCHECK>(entry, cu_seqlens, req, T, bos, eos);
     if (eos <= bos)
         return;
     const int h = qk_head(p, hv);
@@ -1220,13 +1289,7 @@ __global__ __launch_bounds__(64 * NQ) void kda_decode_q_kernel(const int32_t *sl
     if ((verdict != KDA_DEVICE_OK) | (slot < 0) | (slot >= num_slots))   // one branch: both loads first
         return;
     int64_t bos, eos;
-    if (cu_seqlens) {
-        bos = cu_seqlens[req];
-        eos = cu_seqlens[req + 1];
-    } else {
-        bos = req * T;
-        eos = bos + T;
-    }
+    token_rows<VCHECK>(entry, cu_seqlens, req, T, bos, eos);
     if (eos <= bos)
         return;
     const int64_t ntok = eos - bos;
@@ -1449,7 +1512,7 @@ __global__ __launch_bounds__(256) void kda_decode_split_kernel(const int32_t *sl
     }
 
     // (VCHECK: the launch's requests from its head count; step calls, no cu_seqlens)
-    const Entry entry = entry_check<VCHECK>(status, slot_idx, nullptr, num_slots, VCHECK ? units / HV : 0, 0, req);
+    const Entry entry = entry_check<VCHECK>(status, slot_idx, nullptr, num_slots, VCHECK ? units / HV : 0, T, req);
     const int32_t verdict = entry.verdict;
     const int64_t slot = entry.slot;
     if constexpr (EARLY)

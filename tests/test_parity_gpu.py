@@ -600,6 +600,35 @@ def test_validate_small_calls(shape, case):
         assert torch.equal(d.state, ref.state) and torch.equal(d.out.view(torch.int16), ref.out.view(torch.int16))
 
 
+@pytest.mark.parametrize("N,HV", [(2, 8), (33, 8), (64, 8)])
+def test_validate_small_duplicate_at_every_distance(N, HV):
+    """The in-wave duplicate check compares lanes through rotations: every
+    pair of requests on one slot, whatever their distance in the call
+    (1 to N - 1, across the wave's halves too), is rejected with code 2 and
+    leaves the pool untouched; the intact call passes."""
+    p = ki.make_problem("vdist", 130 + N, N=N, H=8, HV=HV, K=128, V=128, num_slots=N + 5, T=1)
+    d = upload(p)
+    before = d.state.clone()
+    slots = d.slot_idx.clone()
+    st = _status_word()
+    missed = []
+    for i in range(N):
+        for j in range(i + 1, N):
+            d.slot_idx.copy_(slots)
+            d.slot_idx[j] = slots[i]
+            st.fill_(-7)
+            run_gpu(d, device_status=st)
+            if st.item() != 2:
+                missed.append((i, j))
+    torch.cuda.synchronize()
+    assert not missed, missed[:10]
+    assert torch.equal(d.state, before)
+    d.slot_idx.copy_(slots)
+    run_gpu(d, device_status=st)
+    torch.cuda.synchronize()
+    assert st.item() == 0
+
+
 @pytest.mark.parametrize("N", [8, 64])
 def test_validate_small_packed_cu_seqlens_past_the_tokens(N):
     """A packed call of at most 64 requests whose cu_seqlens ends past the
