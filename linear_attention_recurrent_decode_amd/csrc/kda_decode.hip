@@ -241,6 +241,27 @@ __device__ __forceinline__ void add_swaps3(float &x, float &y, float &z)
     z = __builtin_bit_cast(float, z0) + __builtin_bit_cast(float, z1);
 }
 
+// The same two levels for the split-key waves, which need the three sums
+// only in LDS: u and w share their first swap, k.q joins them in the second,
+// and the sums end spread over the rows, u in row 0, w in row 1, k.q in rows
+// 2 and 3 (each addition has the operands, in the same order, that
+// add_swaps3 gives it, so the bits are the same; 8 VALU instructions in
+// place of 18).
+__device__ __forceinline__ float spread_swaps3(float u, float w, float kq)
+{
+    uint32_t a = __builtin_bit_cast(uint32_t, u), b = __builtin_bit_cast(uint32_t, w);
+    uint32_t k0 = __builtin_bit_cast(uint32_t, kq), k1 = k0;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_permlane16_swap_b32 %2, %3\n\ts_nop 1"
+                 : "+v"(a), "+v"(b), "+v"(k0), "+v"(k1));
+    // a = rows (u0, w0, u2, w2), b = (u1, w1, u3, w3): the pair sums of u in
+    // rows 0 and 2, of w in rows 1 and 3
+    uint32_t c = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b));
+    uint32_t d = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, k0) + __builtin_bit_cast(float, k1));
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(c), "+v"(d));
+    // c = rows (u01, w01, kq01, kq01), d = (u23, w23, kq23, kq23)
+    return __builtin_bit_cast(float, c) + __builtin_bit_cast(float, d);
+}
+
 // Sum over the 8 lanes that share a column group (lane bits 3..5: lanes l,
 // l+8, .., l+56), all on the VALU.  Each level adds the same two operands on
 // both lanes of a pair, so every lane of the group ends with the same bits,
@@ -1424,31 +1445,34 @@ constexpr int S_ROWS = 16;          // key rows per lane
 constexpr int S_COLS = 32;          // columns per workgroup
 constexpr int S_XCH = 3 * S_COLS;   // one row half's u, w and k.q per column
 
+// The exchange slots of a lane (xw: the one it writes, rows 0 .. 2 only;
+// xm, xo: its column's three sums of its own and of the other row half),
+// in the buffer of parity 0; `buf` picks the buffer.
+struct SplitXch {
+    float *xw;
+    const float *xm, *xo;
+};
+
 __device__ __forceinline__ void advance_split(float (&s)[S_ROWS], const PairPre &pre, const PairIn &in,
-                                              const DecodeParams &p, int64_t t, int hv, int rh, int rgl, int cl,
-                                              int col, float *xch)
+                                              const DecodeParams &p, int64_t t, int hv, int rh, int rgl, int col,
+                                              const SplitXch &xs, int buf)
 {
     const PairFactors &f = pre.f;
-    float u = 0.f, w = 0.f;
-    quarter_sums8<0>(s, pre.ak_lo, pre.ak_hi, pre.aq_lo, pre.aq_hi, u, w);
-    quarter_sums8<1>(s, pre.ak_lo, pre.ak_hi, pre.aq_lo, pre.aq_hi, u, w);
-    float kq = pre.kq;
-    add_swaps3(kq, u, w);
-    // the halves meet in LDS, double-buffered by token parity: a buffer is
-    // written again two tokens later, after every wave has passed the
-    // barrier of the token between, so after its reads of this one
-    float *x = xch + (int)(t & 1) * (2 * S_XCH);
-    if (rgl == 0) {
-        float *mine = x + rh * S_XCH + 3 * cl;
-        mine[0] = u;
-        mine[1] = w;
-        mine[2] = kq;
-    }
+    float uh = 0.f, wh = 0.f;
+    quarter_sums8<0>(s, pre.ak_lo, pre.ak_hi, pre.aq_lo, pre.aq_hi, uh, wh);
+    quarter_sums8<1>(s, pre.ak_lo, pre.ak_hi, pre.aq_lo, pre.aq_hi, uh, wh);
+    const float sum = spread_swaps3(uh, wh, pre.kq);   // u, w, k.q of the row half in rows 0, 1, 2
+    // the halves meet in LDS, double-buffered by the token's parity within
+    // the request (a compile-time offset where the tokens are unrolled): a
+    // buffer is written again two tokens later, after every wave has passed
+    // the barrier of the token between, so after its reads of this one
+    const int off = buf * (2 * S_XCH);
+    if (rgl < 3)
+        xs.xw[off] = sum;
     __syncthreads();
-    const float *other = x + (rh ^ 1) * S_XCH + 3 * cl;
-    u = u + other[0];
-    w = w + other[1];
-    kq = kq + other[2];
+    const float u = xs.xm[off] + xs.xo[off];
+    const float w = xs.xm[off + 1] + xs.xo[off + 1];
+    const float kq = xs.xm[off + 2] + xs.xo[off + 2];
     const float vp = f.b * (bf16_lo(in.v) - u);
     const float o = p.scale * fmaf(vp, kq, w);
     quarter_update8<0>(s, f.a_lo, f.a_hi, f.k_lo, f.k_hi, vp);
@@ -1535,6 +1559,7 @@ __global__ __launch_bounds__(256) void kda_decode_split_kernel(const int32_t *sl
     using Slab = SlabIO<S_COLS, BF16S, 256, 4>;
     extern __shared__ float stage[];    // the tile, then 2 x 2 exchange buffers
     float *xch = stage + Slab::LDS_FLOATS;
+    const SplitXch xs{xch + rh * S_XCH + 3 * cl + rgl, xch + rh * S_XCH + 3 * cl, xch + (rh ^ 1) * S_XCH + 3 * cl};
     const Slab slab(state, slot * slot_stride + (int64_t)hv * (KD * VD) + vt * S_COLS, (int)threadIdx.x);
     auto stage_columns = [&]() {
         __syncthreads();
@@ -1593,13 +1618,13 @@ __global__ __launch_bounds__(256) void kda_decode_split_kernel(const int32_t *sl
     for (int j = 0; j < PF; ++j) {
         if (j < T) {
             const PairPre pre = (EARLY && j == 0) ? pre0 : pair_pre<S_ROWS>(in[j], hg);
-            advance_split(s, pre, in[j], p, bos + j, hv, rh, rgl, cl, col, xch);
+            advance_split(s, pre, in[j], p, bos + j, hv, rh, rgl, col, xs, j & 1);
             keep_state(bos + j);
         }
     }
     for (int64_t t = bos + PF; t < eos; ++t) {
         load_pair<false, RAWG>(in[0], p, t, h, hv, row0, pair, col);
-        advance_split(s, pair_pre<S_ROWS>(in[0], hg), in[0], p, t, hv, rh, rgl, cl, col, xch);
+        advance_split(s, pair_pre<S_ROWS>(in[0], hg), in[0], p, t, hv, rh, rgl, col, xs, (int)((t - bos) & 1));
         keep_state(t);
     }
     if constexpr (!EARLY && !BF16S) {
