@@ -211,10 +211,11 @@ int32_t plan_body(const CallShape &c)
 //     N52 10.32 vs 12.20 on four, N64 11.91 vs 12.86); with the fused gate
 //     two 16-column waves up to 64 tiles (N8 3.80 vs 3.91 split-key, 4.06
 //     32-column; N9 4.24 on the 32-column kernel vs 4.36);
-//   fp32, two or more tokens: split-key waves up to 256 tiles (N32/T4 8.46
-//     vs 8.76 on four 16-column waves), and with two or three tokens up to
-//     320 (N40/T2 8.49 vs 8.59, N40/T3 8.81 vs 8.98; N36/T4 10.03 vs 9.81
-//     the other way); four 16-column waves to 576 tiles, 512 with two tokens
+//   fp32, two or more tokens: split-key waves up to 320 tiles (N32/T4 8.46
+//     vs 8.76 on four 16-column waves, N36/T4 9.21 vs 9.56, N40/T4 9.48 vs
+//     9.71, N40/T2 8.49 vs 8.59, N40/T3 8.81 vs 8.98; N44/T3 9.84 vs 9.08
+//     and N48/T4 10.75 vs 10.35 the other way); four 16-column waves to 576
+//     tiles, 512 with two tokens
 //     (N64/T2 12.30 vs 13.27 on the 32-column kernel, N72/T4 17.51 vs 19.70;
 //     but N72/T2 17.21 vs 14.90); the 32-column kernel to 768 (N80/T4 18.65
 //     vs 18.89, N96/T4 20.33 vs 22.33, N88/T3 16.93 vs 20.83, N96/T2 18.65
@@ -260,7 +261,7 @@ int32_t plan_quarter_waves(const CallShape &c)
             return c.units <= 64 ? 2 : 0;
         return c.units <= 128 ? PLAN_SPLIT : 0;
     }
-    if (c.units <= 256 || (c.T <= 3 && c.units <= 320))
+    if (c.units <= 320)
         return PLAN_SPLIT;
     if (c.units <= (c.T == 2 ? 512 : 576))
         return 4;

@@ -70,8 +70,8 @@ def test_status_strings_and_plan():
     # split-key 16-column waves (32 columns) up to 128 tiles, 32-column waves
     # (32 or 64 columns) to 256, four 16-column waves (64 columns) to 384,
     # eight (128 columns) beyond;
-    # with two or more tokens split-key waves up to 256 tiles (320 with two
-    # or three tokens), four 16-column waves (64 columns) to 576 (512 with
+    # with two or more tokens split-key waves up to 320 tiles, four
+    # 16-column waves (64 columns) to 576 (512 with
     # two tokens), 32-column waves to 768 (64 columns with two tokens, else
     # 128), four 16-column waves to 1536, eight beyond
     W, Q, S = kda.KDA_LAYOUT_WIDE, kda.KDA_LAYOUT_QUARTER, kda.KDA_LAYOUT_SPLIT
@@ -84,9 +84,9 @@ def test_status_strings_and_plan():
               (1537, 2): (128, Q), (4096, 2): (128, Q),
               (192, 3): (32, S), (320, 3): (32, S), (321, 3): (64, Q), (576, 3): (64, Q), (577, 3): (128, W),
               (768, 3): (128, W), (769, 3): (64, Q),
-              (8, 4): (32, S), (256, 4): (32, S), (257, 4): (64, Q), (512, 4): (64, Q), (576, 4): (64, Q),
+              (8, 4): (32, S), (256, 4): (32, S), (320, 4): (32, S), (321, 4): (64, Q), (512, 4): (64, Q), (576, 4): (64, Q),
               (577, 4): (128, W), (768, 4): (128, W), (769, 4): (64, Q), (1536, 4): (64, Q), (1537, 4): (128, Q),
-              (384, 9): (64, Q), (192, 9): (32, S), (256, 9): (32, S), (257, 9): (64, Q), (700, 9): (128, W)}
+              (384, 9): (64, Q), (192, 9): (32, S), (320, 9): (32, S), (321, 9): (64, Q), (700, 9): (128, W)}
     for (units, T), (width, layout) in expect.items():
         assert kda.kda_decode_plan(units, T, False) == width, (units, T)
         assert kda.kda_decode_plan(units, T, False, layout=True) == layout, (units, T)
@@ -95,7 +95,7 @@ def test_status_strings_and_plan():
     # the table is the same
     raw = {(1, 1): (32, Q), (64, 1): (32, Q), (65, 1): (32, W), (128, 1): (32, W), (256, 1): (64, W),
            (300, 1): (64, Q), (384, 1): (64, Q),
-           (385, 1): (128, Q), (512, 1): (128, Q), (8, 4): (32, S), (192, 2): (32, S), (300, 4): (64, Q)}
+           (385, 1): (128, Q), (512, 1): (128, Q), (8, 4): (32, S), (192, 2): (32, S), (300, 4): (32, S), (321, 4): (64, Q)}
     for (units, T), (width, layout) in raw.items():
         assert kda.kda_decode_plan(units, T, raw_gate=True) == width, (units, T)
         assert kda.kda_decode_plan(units, T, raw_gate=True, layout=True) == layout, (units, T)

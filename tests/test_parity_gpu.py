@@ -890,8 +890,9 @@ SPLIT, QUARTER = kda.KDA_LAYOUT_SPLIT, kda.KDA_LAYOUT_QUARTER
 QUARTER_CASES = [
     # (N, H, HV, T, raw gates, the 16-column-wave layout the library picks);
     # the library also picks the load order: the first token's inputs before
-    # the tile for calls of two or more tokens from 192 tiles to 256 (384
-    # with three or more tokens), the tile first otherwise
+    # the tile for calls of two or more tokens on the split-key waves from
+    # 192 tiles to 256 and on four 16-column waves with three or more
+    # tokens, the tile first otherwise
     (1, 8, 8, 4, False, SPLIT),       # 8 tiles
     (5, 1, 3, 2, False, SPLIT),       # three value heads per q/k head
     (9, 4, 8, 3, True, SPLIT),        # fused gate activation
@@ -900,12 +901,15 @@ QUARTER_CASES = [
     (8, 8, 8, 1, False, SPLIT),       # one token, 64 tiles
     (16, 2, 8, 1, False, SPLIT),      # one token, 128 tiles
     (8, 2, 8, 1, True, QUARTER),      # one token, 64 tiles, fused gate: two waves per workgroup
-    (32, 8, 8, 4, False, SPLIT),      # 256 tiles: the split-key layout's last size at four tokens
-    (40, 8, 8, 3, False, SPLIT),      # 320 tiles, three tokens, tile first: its last size at three
+    (32, 8, 8, 4, False, SPLIT),      # 256 tiles: the split-key layout's last inputs-first size
+    (40, 8, 8, 3, False, SPLIT),      # 320 tiles, three tokens, tile first: its last size
+    (40, 8, 8, 4, False, SPLIT),      # 320 tiles, four tokens, tile first
     (24, 2, 8, 2, True, SPLIT),       # 192 tiles, two tokens, fused gate, inputs first
-    (36, 4, 8, 4, False, QUARTER),    # 288 tiles: four waves per workgroup, inputs first
+    (36, 4, 8, 4, False, SPLIT),      # 288 tiles, four tokens, tile first
+    (42, 4, 8, 4, False, QUARTER),    # 336 tiles: four waves per workgroup, inputs first
     (41, 8, 8, 2, True, QUARTER),     # 328 tiles, two tokens, fused gate, tile first
-    (44, 2, 6, 5, False, QUARTER),    # 264 tiles, five tokens
+    (44, 2, 6, 5, False, SPLIT),      # 264 tiles, five tokens
+    (56, 2, 6, 5, False, QUARTER),    # 336 tiles, five tokens
     (60, 8, 8, 2, False, QUARTER),    # 480 tiles, two tokens
     (70, 8, 8, 4, False, QUARTER),    # 560 tiles, four tokens, inputs first
     (36, 8, 8, 1, False, QUARTER),    # one token, 288 tiles: four waves per workgroup
