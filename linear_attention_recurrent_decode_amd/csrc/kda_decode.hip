@@ -416,11 +416,22 @@ __device__ __forceinline__ void advance_token(f32x4 (&s)[ROWS_PER_LANE], TokenIn
             load_token<RAWG>(in, p, t + 1, h, hv, row0, col);
     }
 
-    // one pass over the old state: both key-axis partial sums
-    float u0 = 0.f, u1 = 0.f, u2 = 0.f, u3 = 0.f;
-    float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f;
+    // one pass over the old state: both key-axis partial sums, each chain
+    // opened by its first row's products
+    float u0, u1, u2, u3, w0, w1, w2, w3;
+    {
+        const float ak = a[0] * kk[0], aq = a[0] * qq[0];
+        u0 = s[0].x * ak;
+        u1 = s[0].y * ak;
+        u2 = s[0].z * ak;
+        u3 = s[0].w * ak;
+        w0 = s[0].x * aq;
+        w1 = s[0].y * aq;
+        w2 = s[0].z * aq;
+        w3 = s[0].w * aq;
+    }
 #pragma unroll
-    for (int i = 0; i < ROWS_PER_LANE; ++i) {
+    for (int i = 1; i < ROWS_PER_LANE; ++i) {
         const float ak = a[i] * kk[i], aq = a[i] * qq[i];
         u0 = fmaf(s[i].x, ak, u0);
         u1 = fmaf(s[i].y, ak, u1);
@@ -1063,20 +1074,39 @@ __device__ __forceinline__ void load_pair(PairIn &in, const DecodeParams &p, int
     "v_fmac_f32_dpp %0, %" AK ", %" S " row_newbcast:%c" IMM " row_mask:0xf bank_mask:0xf\n\t" \
     "v_fmac_f32_dpp %1, %" AQ ", %" S " row_newbcast:%c" IMM " row_mask:0xf bank_mask:0xf\n\t"
 
-template <int B, int R>
+// The first row of a 16-row chain: the sums start from its products, in
+// every lane layout (a product, not a multiply-add onto 0, so that the bits
+// agree even where a product is -0).
+#define Q_ROW_UW_FIRST(AK, AQ, S, IMM)                                                         \
+    "v_mul_f32_dpp %0, %" AK ", %" S " row_newbcast:%c" IMM " row_mask:0xf bank_mask:0xf\n\t" \
+    "v_mul_f32_dpp %1, %" AQ ", %" S " row_newbcast:%c" IMM " row_mask:0xf bank_mask:0xf\n\t"
+
+// FIRST: rows 8B .. 8B+7 open the chain (u and w are written, not read).
+template <int B, int R, bool FIRST = false>
 __device__ __forceinline__ void quarter_sums8(const float (&s)[R], float ak_lo, float ak_hi, float aq_lo,
                                               float aq_hi, float &u, float &w)
 {
-    asm volatile("s_nop 1\n\t"
-                 Q_ROW_UW("2", "4", "6", "14") Q_ROW_UW("3", "5", "7", "14")
-                 Q_ROW_UW("2", "4", "8", "15") Q_ROW_UW("3", "5", "9", "15")
-                 Q_ROW_UW("2", "4", "10", "16") Q_ROW_UW("3", "5", "11", "16")
-                 Q_ROW_UW("2", "4", "12", "17") Q_ROW_UW("3", "5", "13", "17")
-                 : "+v"(u), "+v"(w)
-                 : "v"(ak_lo), "v"(ak_hi), "v"(aq_lo), "v"(aq_hi),
-                   "v"(s[8 * B + 0]), "v"(s[8 * B + 1]), "v"(s[8 * B + 2]), "v"(s[8 * B + 3]),
-                   "v"(s[8 * B + 4]), "v"(s[8 * B + 5]), "v"(s[8 * B + 6]), "v"(s[8 * B + 7]),
-                   "i"(4 * B), "i"(4 * B + 1), "i"(4 * B + 2), "i"(4 * B + 3));
+#define Q_SUMS8_INPUTS                                                                                  \
+    "v"(ak_lo), "v"(ak_hi), "v"(aq_lo), "v"(aq_hi), "v"(s[8 * B + 0]), "v"(s[8 * B + 1]),               \
+        "v"(s[8 * B + 2]), "v"(s[8 * B + 3]), "v"(s[8 * B + 4]), "v"(s[8 * B + 5]), "v"(s[8 * B + 6]), \
+        "v"(s[8 * B + 7]), "i"(4 * B), "i"(4 * B + 1), "i"(4 * B + 2), "i"(4 * B + 3)
+    if constexpr (FIRST)
+        asm volatile("s_nop 1\n\t"
+                     Q_ROW_UW_FIRST("2", "4", "6", "14") Q_ROW_UW("3", "5", "7", "14")
+                     Q_ROW_UW("2", "4", "8", "15") Q_ROW_UW("3", "5", "9", "15")
+                     Q_ROW_UW("2", "4", "10", "16") Q_ROW_UW("3", "5", "11", "16")
+                     Q_ROW_UW("2", "4", "12", "17") Q_ROW_UW("3", "5", "13", "17")
+                     : "=&v"(u), "=&v"(w)
+                     : Q_SUMS8_INPUTS);
+    else
+        asm volatile("s_nop 1\n\t"
+                     Q_ROW_UW("2", "4", "6", "14") Q_ROW_UW("3", "5", "7", "14")
+                     Q_ROW_UW("2", "4", "8", "15") Q_ROW_UW("3", "5", "9", "15")
+                     Q_ROW_UW("2", "4", "10", "16") Q_ROW_UW("3", "5", "11", "16")
+                     Q_ROW_UW("2", "4", "12", "17") Q_ROW_UW("3", "5", "13", "17")
+                     : "+v"(u), "+v"(w)
+                     : Q_SUMS8_INPUTS);
+#undef Q_SUMS8_INPUTS
 }
 
 // The update of rows 8B .. 8B+7: s_i = k_i v' + (a_i s_i), one rounding for
@@ -1182,9 +1212,9 @@ __device__ __forceinline__ void advance_pair(float (&s)[Q_ROWS], const PairPre &
     const float ak_lo = pre.ak_lo, ak_hi = pre.ak_hi, aq_lo = pre.aq_lo, aq_hi = pre.aq_hi;
 
     // both key-axis partial sums, each 16-row half in row order
-    float u_lo = 0.f, w_lo = 0.f, u_hi = 0.f, w_hi = 0.f;
-    quarter_sums8<0>(s, ak_lo, ak_hi, aq_lo, aq_hi, u_lo, w_lo);
-    quarter_sums8<2>(s, ak_lo, ak_hi, aq_lo, aq_hi, u_hi, w_hi);
+    float u_lo, w_lo, u_hi, w_hi;
+    quarter_sums8<0, Q_ROWS, true>(s, ak_lo, ak_hi, aq_lo, aq_hi, u_lo, w_lo);
+    quarter_sums8<2, Q_ROWS, true>(s, ak_lo, ak_hi, aq_lo, aq_hi, u_hi, w_hi);
     quarter_sums8<1>(s, ak_lo, ak_hi, aq_lo, aq_hi, u_lo, w_lo);
     quarter_sums8<3>(s, ak_lo, ak_hi, aq_lo, aq_hi, u_hi, w_hi);
 
@@ -1458,8 +1488,8 @@ __device__ __forceinline__ void advance_split(float (&s)[S_ROWS], const PairPre 
                                               const SplitXch &xs, int buf)
 {
     const PairFactors &f = pre.f;
-    float uh = 0.f, wh = 0.f;
-    quarter_sums8<0>(s, pre.ak_lo, pre.ak_hi, pre.aq_lo, pre.aq_hi, uh, wh);
+    float uh, wh;
+    quarter_sums8<0, S_ROWS, true>(s, pre.ak_lo, pre.ak_hi, pre.aq_lo, pre.aq_hi, uh, wh);
     quarter_sums8<1>(s, pre.ak_lo, pre.ak_hi, pre.aq_lo, pre.aq_hi, uh, wh);
     const float sum = spread_swaps3(uh, wh, pre.kq);   // u, w, k.q of the row half in rows 0, 1, 2
     // the halves meet in LDS, double-buffered by the token's parity within
