@@ -273,6 +273,45 @@ __device__ __forceinline__ float sum_row_groups(float x)
     return add_permlane32_swap(x);
 }
 
+// Four values' sums over the row groups at once, for the 32-column waves:
+// the l^8 level as in sum_row_groups, then the two swap levels shared by the
+// four values, which end spread over the 16-lane rows (row r holds the sum
+// of x_r; each addition has the operands, in the same order, that
+// sum_row_groups gives it, so the bits are the same).
+__device__ __forceinline__ float spread_row_groups4(float x0, float x1, float x2, float x3)
+{
+    x0 += KDA_DPP(x0, DPP_ROW_ROR8);
+    x1 += KDA_DPP(x1, DPP_ROW_ROR8);
+    x2 += KDA_DPP(x2, DPP_ROW_ROR8);
+    x3 += KDA_DPP(x3, DPP_ROW_ROR8);
+    uint32_t a = __builtin_bit_cast(uint32_t, x0), b = __builtin_bit_cast(uint32_t, x1);
+    uint32_t c = __builtin_bit_cast(uint32_t, x2), d = __builtin_bit_cast(uint32_t, x3);
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_permlane16_swap_b32 %2, %3\n\ts_nop 1"
+                 : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+    // a = rows (x0 of row 0, x1 of row 0, x0 of row 2, x1 of row 2), b the
+    // same of rows 1 and 3; c, d for x2, x3
+    uint32_t e = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b));
+    uint32_t f = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, c) + __builtin_bit_cast(float, d));
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(e), "+v"(f));
+    // e = rows (x0, x1, x2, x3 over rows 0 + 1), f the same over rows 2 + 3
+    return __builtin_bit_cast(float, e) + __builtin_bit_cast(float, f);
+}
+
+// The four row values of a spread sum (row r holds x_r) in every lane.
+__device__ __forceinline__ void gather_rows4(float x, float &x0, float &x1, float &x2, float &x3)
+{
+    uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    // a = rows (x0, x0, x2, x2), b = (x1, x1, x3, x3)
+    uint32_t a2 = a, b2 = b;   // copies made by VALU moves: the leading s_nop covers them
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\tv_permlane32_swap_b32 %2, %3\n\ts_nop 1"
+                 : "+v"(a), "+v"(a2), "+v"(b), "+v"(b2));
+    x0 = __builtin_bit_cast(float, a);
+    x2 = __builtin_bit_cast(float, a2);
+    x1 = __builtin_bit_cast(float, b);
+    x3 = __builtin_bit_cast(float, b2);
+}
+
 // Sum over the 8 column groups of a wave (lane bits 0..2): pairs l <-> 7-l,
 // then l <-> l^1, then l <-> l^2, all symmetric, all on the VALU.
 __device__ __forceinline__ float sum_col_groups(float x)
@@ -363,7 +402,15 @@ __device__ __forceinline__ void load_token(TokenIn &in, const DecodeParams &p, i
 // contraction), so each inlined copy of this function rounds identically.
 // With PREFETCH the next token's inputs are loaded into `in` as soon as this
 // token's are unpacked, so they are in flight while this token computes.
-template <bool NORM, bool PREFETCH, bool RAWG>
+// SPREAD: the key-axis sums over the row groups by the shared swaps of
+// spread_row_groups4 (u then gathered into every lane, w left spread, so that
+// without the norm each 16-lane row forms one column's output): 25 fewer VALU
+// instructions per token, the same bits.  Measured on MI355X it pays on the
+// tokens after a request's first (N80/T4 17.59 vs 18.43 us, N96/T4 19.83 vs
+// 20.06, N72/T2 14.78 vs 14.92; N90/T3 17.25 vs 17.10 the other way) but
+// not on a one-token call (N24/T1 5.42 vs 5.38), so the first token keeps
+// the replicated sums.
+template <bool NORM, bool PREFETCH, bool RAWG, bool SPREAD = false>
 __device__ __forceinline__ void advance_token(f32x4 (&s)[ROWS_PER_LANE], TokenIn &in, const DecodeParams &p,
                                               const HeadGate<RAWG> &hg, int64_t t, int64_t eos, int h, int hv,
                                               int lane, int wave, int rg, int row0, int col,
@@ -442,25 +489,45 @@ __device__ __forceinline__ void advance_token(f32x4 (&s)[ROWS_PER_LANE], TokenIn
         w2 = fmaf(s[i].z, aq, w2);
         w3 = fmaf(s[i].w, aq, w3);
     }
-    u0 = sum_row_groups(u0);
-    u1 = sum_row_groups(u1);
-    u2 = sum_row_groups(u2);
-    u3 = sum_row_groups(u3);
-    w0 = sum_row_groups(w0);
-    w1 = sum_row_groups(w1);
-    w2 = sum_row_groups(w2);
-    w3 = sum_row_groups(w3);
     kq = sum_row_groups(kq);
+    // u in every lane (the update needs all four columns' v'); with SPREAD
+    // and without the norm w only where o is formed: each 16-lane row r
+    // forms o of column 4 cg + r
+    constexpr bool SPREAD_W = SPREAD && !NORM;
+    if constexpr (SPREAD) {
+        gather_rows4(spread_row_groups4(u0, u1, u2, u3), u0, u1, u2, u3);
+    } else {
+        u0 = sum_row_groups(u0);
+        u1 = sum_row_groups(u1);
+        u2 = sum_row_groups(u2);
+        u3 = sum_row_groups(u3);
+    }
+    float w_row = 0.f;
+    if constexpr (SPREAD_W) {
+        w_row = spread_row_groups4(w0, w1, w2, w3);
+    } else {
+        w0 = sum_row_groups(w0);
+        w1 = sum_row_groups(w1);
+        w2 = sum_row_groups(w2);
+        w3 = sum_row_groups(w3);
+    }
 
     // delta correction, readout, rank-1 update
     const float vp0 = b * (v0 - u0);
     const float vp1 = b * (v1 - u1);
     const float vp2 = b * (v2 - u2);
     const float vp3 = b * (v3 - u3);
-    float o0 = p.scale * fmaf(vp0, kq, w0);
-    float o1 = p.scale * fmaf(vp1, kq, w1);
-    float o2 = p.scale * fmaf(vp2, kq, w2);
-    float o3 = p.scale * fmaf(vp3, kq, w3);
+    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f, o_row = 0.f;
+    if constexpr (!SPREAD_W) {
+        o0 = p.scale * fmaf(vp0, kq, w0);
+        o1 = p.scale * fmaf(vp1, kq, w1);
+        o2 = p.scale * fmaf(vp2, kq, w2);
+        o3 = p.scale * fmaf(vp3, kq, w3);
+    } else {
+        const int r = lane >> 4;
+        const float vp_row = r == 0 ? vp0 : r == 1 ? vp1 : r == 2 ? vp2 : vp3;
+        o_row = p.scale * fmaf(vp_row, kq, w_row);
+    }
 #pragma unroll
     for (int i = 0; i < ROWS_PER_LANE; ++i) {
         s[i].x = fmaf(kk[i], vp0, a[i] * s[i].x);
@@ -488,11 +555,17 @@ __device__ __forceinline__ void advance_token(f32x4 (&s)[ROWS_PER_LANE], TokenIn
         o2 = o2 * r * bf16_lo(nw.y) * silu(bf16_lo(zz.y));
         o3 = o3 * r * bf16_hi(nw.y) * silu(bf16_hi(zz.y));
     }
-    if (rg == 0) {
-        uint2 packed;
-        packed.x = pack_bf16x2(o0, o1);
-        packed.y = pack_bf16x2(o2, o3);
-        *reinterpret_cast<uint2 *>(p.out + t * p.out_stride + (int64_t)hv * VD + col) = packed;
+    if constexpr (!SPREAD_W) {
+        if (rg == 0) {
+            uint2 packed;
+            packed.x = pack_bf16x2(o0, o1);
+            packed.y = pack_bf16x2(o2, o3);
+            *reinterpret_cast<uint2 *>(p.out + t * p.out_stride + (int64_t)hv * VD + col) = packed;
+        }
+    } else {
+        // lanes 16 r + cg (row group 2 r) store column 4 cg + r
+        if ((lane & 8) == 0)
+            p.out[t * p.out_stride + (int64_t)hv * VD + col + (lane >> 4)] = (uint16_t)pack_bf16x2(o_row, 0.0f);
     }
 }
 
@@ -935,7 +1008,8 @@ __global__ __launch_bounds__(64 * NW) void kda_decode_kernel(const int32_t *slot
         keep_state(bos);
         for (int64_t t = bos + 1; t < eos; ++t) {
             load_token<RAWG>(in, p, t, h, hv, row0, col);
-            advance_token<NORM, false, RAWG>(s, in, p, hg, t, eos, h, hv, lane, wave, rg, row0, col, norm_partial);
+            advance_token<NORM, false, RAWG, true>(s, in, p, hg, t, eos, h, hv, lane, wave, rg, row0, col,
+                                                   norm_partial);
             keep_state(t);
         }
     } else {
