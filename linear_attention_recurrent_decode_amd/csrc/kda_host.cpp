@@ -232,7 +232,11 @@ int32_t plan_body(const CallShape &c)
 //   bf16 pool, no norm: four 16-column waves (full 128-byte row pieces of
 //     bf16) at every size (N32/T1 5.15 vs 5.81 on the 32-column kernel and
 //     5.68 on eight waves, N128/T1 15.3 vs 16.3 on eight), the split-key
-//     waves with two or more tokens up to 32 tiles (N4/T4 4.85 vs 5.00);
+//     waves with two or more tokens up to 32 tiles (N4/T4 4.85 vs 5.00) and
+//     for one-token calls with activated gates up to 24 tiles (N1 3.03 vs
+//     3.23, N2 3.11 vs 3.29, N3 3.24 vs 3.31; N4 3.34 both, N6 3.61 vs 3.45
+//     the other way; with the fused gate equal at N1 and N2, N4 3.57 vs
+//     3.41 the other way);
 //   the norm epilogue (the head's 128 columns in one workgroup: eight
 //     16-column waves or the 32-column kernel at 128 columns): eight waves
 //     for every bf16-pool call, fp32 calls of two or more tokens up to 512
@@ -249,7 +253,7 @@ int32_t plan_quarter_waves(const CallShape &c)
         return (c.T >= 2 ? c.units <= 512 : c.T == 1 && c.units >= 512) ? 8 : 0;
     }
     if (c.bf16)
-        return (c.T >= 2 && c.units <= 32) ? PLAN_SPLIT : 4;
+        return ((c.T >= 2 && c.units <= 32) || (c.T == 1 && !c.raw && c.units <= 24)) ? PLAN_SPLIT : 4;
     if (c.T == 0)
         return c.units <= 1024 ? 4 : 8;
     if (c.T == 1) {

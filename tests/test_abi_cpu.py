@@ -105,13 +105,15 @@ def test_status_strings_and_plan():
             assert kda.kda_decode_plan(units, 4, packed=True, raw_gate=r) == width
             assert kda.kda_decode_plan(units, 4, packed=True, layout=True, raw_gate=r) == Q
     # bf16 pool without the norm: split-key waves for calls of two or more
-    # tokens up to 32 tiles, else four 16-column waves (64 columns); with
-    # the norm eight
-    for units in (1, 32, 33, 256, 511, 512, 3072):
+    # tokens up to 32 tiles and for one-token calls with activated gates up
+    # to 24 tiles, else four 16-column waves (64 columns); with the norm eight
+    for units in (1, 8, 24, 25, 32, 33, 256, 511, 512, 3072):
         for T in (1, 2, 4):
-            small = units <= 32 and T >= 2
+            small = units <= 32 and T >= 2 or units <= 24 and T == 1
             assert kda.kda_decode_plan(units, T, bf16_state=True) == (32 if small else 64)
             assert kda.kda_decode_plan(units, T, bf16_state=True, layout=True) == (S if small else Q)
+            small_raw = units <= 32 and T >= 2
+            assert kda.kda_decode_plan(units, T, bf16_state=True, raw_gate=True, layout=True) == (S if small_raw else Q)
             assert kda.kda_decode_plan(units, T, bf16_state=True, packed=True) == 64
             assert kda.kda_decode_plan(units, T, bf16_state=True, packed=True, layout=True) == Q
             assert kda.kda_decode_plan(units, T, True, bf16_state=True) == 128

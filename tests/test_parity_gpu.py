@@ -985,15 +985,17 @@ def test_quarter_waves_match_wide_waves_bitwise(case):
         assert torch.equal(o, results[0][0]) and torch.equal(st, results[0][1]) and torch.equal(it, results[0][2])
 
 
-@pytest.mark.parametrize("case", [(1, 8, 8, 1, False, QUARTER), (1, 8, 8, 2, False, SPLIT),
+@pytest.mark.parametrize("case", [(1, 8, 8, 1, False, SPLIT), (3, 8, 8, 1, False, SPLIT),
+                                  (4, 8, 8, 1, False, QUARTER), (1, 8, 8, 1, True, QUARTER), (1, 8, 8, 2, False, SPLIT),
                                   (4, 8, 8, 4, True, SPLIT), (7, 2, 4, 6, False, SPLIT),
                                   (9, 4, 8, 3, True, QUARTER), (20, 4, 8, 4, False, QUARTER),
                                   (32, 8, 8, 2, False, QUARTER), (64, 8, 8, 1, False, QUARTER),
                                   (40, 4, 4, None, False, QUARTER), (25, 2, 6, None, True, QUARTER)])
 def test_quarter_waves_bf16_pool_match_wide_waves_bitwise(case):
     """bf16 pool: the 16-column waves (widened exactly into LDS, rounded once
-    on the way out; split-key waves for several tokens up to 32 tiles, else
-    64-column workgroups), step and packed (T None: 1 to 6 tokens per
+    on the way out; split-key waves for several tokens up to 32 tiles and
+    for one token with activated gates up to 24, else 64-column
+    workgroups), step and packed (T None: 1 to 6 tokens per
     request), against the forced 32-column kernel, bit for bit with
     per-token states; and against the oracle."""
     N, H, HV, T, raw, layout = case
