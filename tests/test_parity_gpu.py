@@ -565,6 +565,8 @@ SMALL_VALIDATED = [
     (16, 2, 8, 2, False, False),     # split-key waves
     (64, 8, 8, 4, False, False),     # four 16-column waves, inputs first
     (32, 8, 8, 1, True, False),      # bf16 pool: four 16-column waves
+    (9, 1, 2, 1, True, False),       # bf16 pool, one token, 18 tiles: split-key waves
+    (9, 1, 3, 3, True, False),       # bf16 pool, three tokens, 27 tiles: split-key waves
     (40, 8, 8, None, False, False),  # packed: four 16-column waves
     (12, 2, 8, None, True, True),    # packed, bf16 pool, fused gate
     (65, 1, 2, None, False, False),  # one request more: the check kernel
