@@ -33,7 +33,9 @@ description: a duration-calibrated graph warmup):
      starting a replay, about 12 us on this ROCm, to the block: reported
      beside, as graph_replay_us_per_call.)
 Then, as extra keys: a plain device copy of the call's state bytes (read and
-write, the same rotation and protocol), the host cost of one enqueue through
+write, the same rotation and protocol), the tile-stream reference (the same
+calls' live tiles moved in place by a kernel that computes nothing,
+libkda_stream.so), the host cost of one enqueue through
 the C ABI, the cache-resident time (--warm), and the CPU oracle on all host
 cores and on one.  With --flags-b the blocks alternate A B B A ... between the
 library's choice (A) and a call with extra flag bits (B), and the line
@@ -519,6 +521,38 @@ def main():
                     "same per-launch cost"}
         del src, dst
         log(f"[bench] copy reference: {copy_us:.3f} us/call, {extras['copy_reference']['GBps']} GB/s")
+
+        # the tile-stream reference: each call's live tiles moved in place by
+        # a kernel that computes nothing (libkda_stream.so), the same calls of
+        # the same rotation, timed with the same protocol
+        slib = kda.stream_library()
+
+        def stream_launch(i):
+            a = combos[i % len(combos)]
+            st = slib.kda_stream_tiles(a.state, state_elem, a.num_slots, a.slot_stride, a.slot_idx, a.N, a.HV, sh)
+            if st != 0:
+                raise kda.KdaError(st, "stream reference")
+
+        stream_blocks = []
+        for _ in range(5):
+            first = pos
+            gap_graph = timer.capture(lambda: [stream_launch(first + i) for i in range(gap)])
+            t0_call = first + gap
+            pos = t0_call + args.steps
+            stream_blocks.append(timer.time_block(gap_graph, lambda: [stream_launch(t0_call + i)
+                                                                      for i in range(args.steps)], args.steps))
+            del gap_graph
+        stream_us = float(np.median(stream_blocks))
+        extras["stream_reference"] = {
+            "us_per_call": round(stream_us, 4), "state_GBps": round(nbytes["state"] / (stream_us * 1e-6) / 1e9, 1),
+            "decode_over_stream": round(us_per_call / stream_us, 4),
+            "blocks": [round(x, 4) for x in stream_blocks],
+            "what": "the call's live state tiles read and written back in place by a kernel that computes "
+                    "nothing (one 512-lane workgroup per tile, all loads before the stores), the same calls "
+                    "of the same cold rotation and timing protocol: the time of the call's state traffic "
+                    "alone at its launch shape, in one access pattern (the decode's own lane layouts can "
+                    "move the tiles faster)"}
+        log(f"[bench] stream reference: {stream_us:.3f} us/call, {extras['stream_reference']['state_GBps']} GB/s")
 
         # host cost of one enqueue through the C ABI (validation + launch), from Python via ctypes
         batch, batches = 1000, 10

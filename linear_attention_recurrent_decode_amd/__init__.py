@@ -32,6 +32,8 @@ __all__ = [
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libkda.so")
+# the benchmark's tile-stream reference (include/kda_stream.h); not the decode path
+stream_library_path = os.path.join(_PKG, "libkda_stream.so")
 
 KDA_STATUS = {
     0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_ALIGN",
@@ -133,6 +135,26 @@ def library() -> ctypes.CDLL:
         raise RuntimeError(f"{library_path} is not built: run linear_attention_recurrent_decode_amd.build.build()")
     _lib = _open(library_path)
     return _lib
+
+
+_stream_lib = None
+
+
+def stream_library() -> ctypes.CDLL:
+    """Load libkda_stream.so, the tile-stream reference the benchmark times
+    beside the decode (it moves a call's state bytes in place and computes
+    nothing); raise if it is missing."""
+    global _stream_lib
+    if _stream_lib is not None:
+        return _stream_lib
+    if not os.path.exists(stream_library_path):
+        raise RuntimeError(f"{stream_library_path} is not built: run linear_attention_recurrent_decode_amd.build.build()")
+    lib = ctypes.CDLL(stream_library_path)
+    lib.kda_stream_tiles.restype = ctypes.c_int
+    lib.kda_stream_tiles.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    _stream_lib = lib
+    return lib
 
 
 def kda_status_string(status: int) -> str:

@@ -24,6 +24,9 @@ SRC = os.path.join(CSRC, "kda_decode.hip")
 HOST_SRC = os.path.join(CSRC, "kda_host.cpp")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkda.so")
+# the benchmark's tile-stream reference (include/kda_stream.h), a library of its own
+STREAM_SRC = os.path.join(CSRC, "kda_stream.hip")
+STREAM_LIB = os.path.join(PKG, "libkda_stream.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -86,9 +89,13 @@ def build(verbose: bool = False, kernarg_preload: int = KERNARG_PRELOAD) -> str:
         msgs += _run([hipcc(), *flags, "-I", INCLUDE, "-I", CSRC, "-c", SRC, "-o", dev_o], "kernel layer")
         tmp_lib = LIB + ".tmp"
         msgs += _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp_lib, dev_o, host_o], "link")
+        tmp_stream = STREAM_LIB + ".tmp"
+        msgs += _run([hipcc(), *flags, "-shared", "-fPIC", "-I", INCLUDE, "-o", tmp_stream, STREAM_SRC],
+                     "stream reference")
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
     os.replace(tmp_lib, LIB)
+    os.replace(tmp_stream, STREAM_LIB)
     return LIB
 
 

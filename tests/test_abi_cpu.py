@@ -41,6 +41,31 @@ def test_library_exports_every_declared_symbol():
     assert set(names) <= exported
 
 
+def test_stream_reference_exports_and_host_checks():
+    """The benchmark's tile-stream reference (include/kda_stream.h): the
+    library exports what the header declares, and every argument check
+    answers before any launch (fake pointers, never dereferenced)."""
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "kda_stream.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+    assert names == ["kda_stream_tiles"]
+    out = subprocess.run(["nm", "-D", "--defined-only", kda.stream_library_path], capture_output=True,
+                         text=True).stdout
+    assert set(names) <= set(re.findall(r"\bT (kda_\w+)", out))
+    lib = kda.stream_library()
+    st, idx, tile = 0x10000, 0x20000, 128 * 128
+    assert lib.kda_stream_tiles(None, 4, 8, 8 * tile, idx, 2, 8, None) == 1          # KDA_ERR_NULL
+    assert lib.kda_stream_tiles(st, 4, 8, 8 * tile, None, 2, 8, None) == 1
+    assert lib.kda_stream_tiles(st, 3, 8, 8 * tile, idx, 2, 8, None) == 2            # KDA_ERR_SHAPE
+    assert lib.kda_stream_tiles(st, 4, 8, 8 * tile - 1, idx, 2, 8, None) == 2
+    assert lib.kda_stream_tiles(st, 4, 8, 8 * tile, idx, 65536, 8, None) == 2
+    assert lib.kda_stream_tiles(st, 4, 8, 8 * tile, idx, -1, 8, None) == 2
+    assert lib.kda_stream_tiles(st, 4, 8, 8 * tile, idx, 2, 0, None) == 2
+    assert lib.kda_stream_tiles(st + 8, 4, 8, 8 * tile, idx, 2, 8, None) == 3        # KDA_ERR_ALIGN
+    assert lib.kda_stream_tiles(st, 2, 8, 8 * tile + 1, idx, 2, 8, None) == 3
+    assert lib.kda_stream_tiles(st, 4, 8, 8 * tile, idx + 2, 2, 8, None) == 3
+    assert lib.kda_stream_tiles(st, 4, 8, 8 * tile, idx, 0, 8, None) == 0            # nothing to do
+
+
 def test_struct_layout_matches_c(tmp_path):
     fields = [f[0] for f in kda.KdaDecodeArgs._fields_]
     src = tmp_path / "layout.c"

@@ -1300,3 +1300,26 @@ def test_gated_rmsnorm(rows, V):
     kda.kda_gated_rmsnorm(xt, zt, wt, xt, 1e-6)
     torch.cuda.synchronize()
     assert torch.equal(xt.view(torch.int16), y.view(torch.int16))
+
+
+# ------------------------------------------------------- the benchmark's tile-stream reference
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_stream_reference_leaves_the_pool_unchanged(dtype):
+    """libkda_stream.so moves the live tiles in place and computes nothing:
+    the pool (and the guard bytes around it) are bitwise unchanged, slots
+    outside the pool and padding rows are skipped, N = 0 enqueues nothing."""
+    HV, slots = 4, 9
+    elem = 4 if dtype == torch.float32 else 2
+    g = torch.Generator(device="cpu").manual_seed(5)
+    raw = torch.randint(-2 ** 15, 2 ** 15, (slots + 2, HV, 128, 128), dtype=torch.int32, generator=g)
+    full = (raw.float() if dtype == torch.float32 else raw.to(torch.int16).view(torch.bfloat16)).to(DEV)
+    pool = full[1:slots + 1]
+    before = full.clone()
+    slot_idx = torch.tensor([3, -1, 0, 8, slots, 5, -7], dtype=torch.int32, device=DEV)
+    lib = kda.stream_library()
+    sh = torch.cuda.current_stream().cuda_stream
+    assert lib.kda_stream_tiles(pool.data_ptr(), elem, slots, HV * 128 * 128, slot_idx.data_ptr(), 7, HV, sh) == 0
+    assert lib.kda_stream_tiles(pool.data_ptr(), elem, slots, HV * 128 * 128, slot_idx.data_ptr(), 0, HV, sh) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(full.view(torch.int16 if elem == 2 else torch.int32),
+                       before.view(torch.int16 if elem == 2 else torch.int32))
