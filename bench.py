@@ -525,7 +525,11 @@ def main():
         # the tile-stream reference: each call's live tiles moved in place by
         # a kernel that computes nothing (libkda_stream.so), the same calls of
         # the same rotation, timed with the same protocol
-        slib = kda.stream_library()
+        try:
+            slib = kda.stream_library()
+        except RuntimeError as e:   # an extra: the decode's line does not depend on it
+            slib = None
+            log(f"[bench] no stream reference: {e}")
 
         def stream_launch(i):
             a = combos[i % len(combos)]
@@ -534,7 +538,7 @@ def main():
                 raise kda.KdaError(st, "stream reference")
 
         stream_blocks = []
-        for _ in range(5):
+        for _ in range(5 if slib is not None else 0):
             first = pos
             gap_graph = timer.capture(lambda: [stream_launch(first + i) for i in range(gap)])
             t0_call = first + gap
@@ -542,17 +546,19 @@ def main():
             stream_blocks.append(timer.time_block(gap_graph, lambda: [stream_launch(t0_call + i)
                                                                       for i in range(args.steps)], args.steps))
             del gap_graph
-        stream_us = float(np.median(stream_blocks))
-        extras["stream_reference"] = {
-            "us_per_call": round(stream_us, 4), "state_GBps": round(nbytes["state"] / (stream_us * 1e-6) / 1e9, 1),
-            "decode_over_stream": round(us_per_call / stream_us, 4),
-            "blocks": [round(x, 4) for x in stream_blocks],
-            "what": "the call's live state tiles read and written back in place by a kernel that computes "
-                    "nothing (one 512-lane workgroup per tile, all loads before the stores), the same calls "
-                    "of the same cold rotation and timing protocol: the time of the call's state traffic "
-                    "alone at its launch shape, in one access pattern (the decode's own lane layouts can "
-                    "move the tiles faster)"}
-        log(f"[bench] stream reference: {stream_us:.3f} us/call, {extras['stream_reference']['state_GBps']} GB/s")
+        if stream_blocks:
+            stream_us = float(np.median(stream_blocks))
+            extras["stream_reference"] = {
+                "us_per_call": round(stream_us, 4),
+                "state_GBps": round(nbytes["state"] / (stream_us * 1e-6) / 1e9, 1),
+                "decode_over_stream": round(us_per_call / stream_us, 4),
+                "blocks": [round(x, 4) for x in stream_blocks],
+                "what": "the call's live state tiles read and written back in place by a kernel that computes "
+                        "nothing (one 512-lane workgroup per tile, all loads before the stores), the same calls "
+                        "of the same cold rotation and timing protocol: the time of the call's state traffic "
+                        "alone at its launch shape, in one access pattern (the decode's own lane layouts can "
+                        "move the tiles faster)"}
+            log(f"[bench] stream reference: {stream_us:.3f} us/call, {extras['stream_reference']['state_GBps']} GB/s")
 
         # host cost of one enqueue through the C ABI (validation + launch), from Python via ctypes
         batch, batches = 1000, 10
